@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU tests and the bench.
+
+This module only draws random numbers and encodes them as the storage types the
+layer takes (bf16 bit patterns, float32).  It holds none of the layer's own
+arithmetic: no smoothing, no low-rank split, no quantization, no GEMM.
+
+Distributions follow the workloads described for the DiT linears that the SVDQuant
+W4A4 layer replaces (1024x1024 images, 4096 image + 512 text tokens):
+
+* activations  X ~ N(0, 1), with a seeded set of outlier input channels scaled by a
+  constant factor (x20 for the tiny case, x30 with 1 % of channels otherwise);
+* weights      W ~ N(0, 0.02), float32, logical shape [K, N] (Y = X @ W);
+* bias         b ~ N(0, 0.02), bf16;
+* calibration  a second, independent draw of X used to set the smoothing factors.
+
+Seeds are derived from a config id c as in ``seeds(c)``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Encode float32 values as bf16 bit patterns (uint16) with torch's cast.
+
+    torch rounds float32 -> bfloat16 to nearest-even; this is only the input
+    encoding of synthetic data, done by the library, not by this project.
+    """
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact: append 16 zero bits)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class Seeds:
+    x: int
+    x_cal: int
+    w: int
+    bias: int
+    outliers: int
+    sketch: int
+
+    def step(self, s: int) -> int:
+        """Seed of the activations of denoise step ``s`` in a chained workload."""
+        return self.x + 99 + s
+
+
+def seeds(config_id: int) -> Seeds:
+    c = 1000 * int(config_id)
+    return Seeds(x=c + 1, x_cal=c + 2, w=c + 3, bias=c + 4, outliers=c + 5, sketch=c + 6)
+
+
+def outlier_channels(K: int, count: int, seed: int) -> np.ndarray:
+    """Sorted indices of ``count`` distinct outlier input channels."""
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(K, size=count, replace=False)).astype(np.int64)
+
+
+def default_outlier_count(K: int) -> int:
+    """1 % of the input channels, rounded (31 at K=3072, 123 at K=12288)."""
+    return int(round(0.01 * K))
+
+
+def activations_f32(M: int, K: int, seed: int, outliers: np.ndarray, factor: float) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if len(outliers):
+        x[:, outliers] *= np.float32(factor)
+    return x
+
+
+def activations(M: int, K: int, seed: int, outliers: np.ndarray, factor: float) -> np.ndarray:
+    """bf16 bit patterns [M, K] of N(0,1) activations with scaled outlier channels."""
+    return to_bf16_bits(activations_f32(M, K, seed, outliers, factor))
+
+
+def weights(K: int, N: int, seed: int, std: float = 0.02) -> np.ndarray:
+    """float32 weights, logical [K, N] (Y = X @ W)."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((K, N), dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def bias(N: int, seed: int, std: float = 0.02) -> np.ndarray:
+    """bf16 bit patterns [N]."""
+    rng = np.random.default_rng(seed)
+    return to_bf16_bits(rng.standard_normal(N, dtype=np.float32) * np.float32(std))
+
+
+def sketch(N: int, width: int, seed: int) -> np.ndarray:
+    """Gaussian test matrix [N, width] (float32) for a randomized range finder."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((N, width), dtype=np.float32)
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """Raw (unprepared) inputs of one linear: activations, calibration data, W, bias."""
+
+    M: int
+    K: int
+    N: int
+    x: np.ndarray        # bf16 bits [M, K]
+    x_cal: np.ndarray    # bf16 bits [M_cal, K]
+    w: np.ndarray        # float32 [K, N]
+    bias: np.ndarray     # bf16 bits [N]
+    outliers: np.ndarray
+    factor: float
+
+
+def layer_inputs(config_id: int, M: int, K: int, N: int, *, outlier_count: int | None = None,
+                 factor: float = 30.0, cal_rows: int | None = None) -> LayerInputs:
+    """All raw inputs of one layer, drawn from the seeds of ``config_id``."""
+    sd = seeds(config_id)
+    n_out = default_outlier_count(K) if outlier_count is None else outlier_count
+    idx = outlier_channels(K, n_out, sd.outliers)
+    m_cal = M if cal_rows is None else cal_rows
+    return LayerInputs(
+        M=M, K=K, N=N,
+        x=activations(M, K, sd.x, idx, factor),
+        x_cal=activations(m_cal, K, sd.x_cal, idx, factor),
+        w=weights(K, N, sd.w),
+        bias=bias(N, sd.bias),
+        outliers=idx,
+        factor=factor,
+    )
+
+
+# The workloads: (config id, M, K, N, outlier count or None for 1 %, outlier factor).
+TINY = dict(config_id=1, M=256, K=512, N=512, outlier_count=4, factor=20.0)
+ATTN_PROJ = dict(config_id=2, M=4096, K=3072, N=3072, outlier_count=None, factor=30.0)
+QKV = dict(config_id=3, M=4608, K=3072, N=9216, outlier_count=None, factor=30.0)
+MLP_UP = dict(config_id=3, M=4608, K=3072, N=12288, outlier_count=None, factor=30.0)
+MLP_DOWN = dict(config_id=3, M=4608, K=12288, N=3072, outlier_count=None, factor=30.0)
+NVFP4_SQ = dict(config_id=4, M=4096, K=3072, N=3072, outlier_count=None, factor=30.0)
+NVFP4_UP = dict(config_id=4, M=4096, K=3072, N=12288, outlier_count=None, factor=30.0)
