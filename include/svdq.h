@@ -1,0 +1,152 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 linear layer.
+ *
+ * What the layer computes (Diffusers docs "Nunchaku Lite", "Supported quantization
+ * types" table and "NunchakuLiteQuantizationConfig" section; the infolabhq
+ * tutorial's section on why 4-bit inference matters):
+ *
+ *   svdq_w4a4 linear, precision int4 (group 64) or nvfp4 (group 16), with the SVDQ
+ *   low-rank correction of rank r (32 in the config example), compute_dtype bf16:
+ *
+ *     xhat = bf16(x * smooth)                      per-input-channel smoothing
+ *     U    = bf16(xhat @ lora_down^T)              rank-r down projection
+ *     codes, scales = quantize(xhat)               4-bit, one scale per group
+ *     Y    = bf16( sum_g s_x s_w (codes_x . codes_w)_g  [ * g_x g_w for nvfp4 ]
+ *                  + U @ lora_up^T + bias )
+ *
+ *   awq_w4a16 linear (INT4 weight-only, group 64), the comparison path:
+ *     Y = bf16( sum_g s[n,g] sum_{k in g} x[m,k] (q[n,k] - z[n,g]) + bias[n] )
+ *
+ * Conventions for every entry point
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Every pointer argument is a DEVICE pointer (hipMalloc / torch CUDA tensors)
+ *     unless stated otherwise.  All arrays are dense, row-major, 16-byte aligned.
+ *   - The caller owns every buffer.  The library allocates no device memory; it
+ *     keeps only a per-device architecture cache.
+ *   - Work is enqueued on `stream` and is asynchronous: outputs are valid once the
+ *     stream has been synchronized.  Nothing is launched when a call returns an
+ *     error.  Errors are detected on the host, before any device access, in the
+ *     order NULL -> config -> shape -> alignment -> workspace -> device; launch
+ *     failures return SVDQ_ERR_HIP.  svdq_last_error() describes the last failure
+ *     of the calling thread.
+ *   - Weights are logically W[K, N] (Y = X W) and are stored per output column
+ *     (N rows of length K), like nn.Linear.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_NULL = 1,      /* a required pointer is NULL                              */
+  SVDQ_ERR_CONFIG = 2,    /* (method, precision, group_size, rank, dtype) unsupported */
+  SVDQ_ERR_SHAPE = 3,     /* sizes violate the layer's shape rules                    */
+  SVDQ_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                         */
+  SVDQ_ERR_WORKSPACE = 5, /* workspace smaller than svdq_workspace_bytes()           */
+  SVDQ_ERR_DEVICE = 6,    /* no device, or the current device is not gfx950          */
+  SVDQ_ERR_HIP = 7,       /* a HIP runtime call or kernel launch failed               */
+  SVDQ_ERR_RANGE = 8      /* an input value is outside the supported range            */
+} svdq_status;
+
+typedef enum { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 } svdq_precision;
+typedef enum { SVDQ_BF16 = 0 } svdq_dtype;
+
+/* Mirrors the svdq_w4a4 / awq_w4a16 entries of NunchakuLiteQuantizationConfig.
+ * Supported: svdq_w4a4 {int4, 64} and {nvfp4, 16} with rank 0..32 in steps of 16
+ * (0, 16 or 32); awq_w4a16 {int4, 64} with rank 0.  compute_dtype: bf16 only. */
+typedef struct {
+  int32_t precision;     /* svdq_precision */
+  int32_t group_size;    /* 64 (int4) or 16 (nvfp4) */
+  int32_t rank;          /* low-rank correction rank r */
+  int32_t compute_dtype; /* svdq_dtype */
+} svdq_config;
+
+/* A prepared svdq_w4a4 layer in the kernel layout (see svdq_pack_weight). */
+typedef struct {
+  int64_t K, N;
+  const uint8_t* qweight;    /* packed codes, svdq_packed_weight_bytes() codes part      */
+  const void* wscales;       /* packed scales, svdq_packed_weight_bytes() scales part    */
+  float w_global;            /* NVFP4 per-tensor weight scale g_w; ignored for int4      */
+  const uint16_t* smooth;    /* [K] bf16 smoothing multiplier m                          */
+  const uint16_t* lora_down; /* [r][K] bf16, L1^T (NULL iff r == 0)                      */
+  const uint16_t* lora_up;   /* [N][r] bf16, L2^T (NULL iff r == 0)                      */
+  const uint16_t* bias;      /* [N] bf16 or NULL                                         */
+} svdq_w4a4_weight;
+
+/* An awq_w4a16 layer in the interchange layout. */
+typedef struct {
+  int64_t K, N;
+  const uint8_t* qweight;   /* [N][K/2] unsigned nibbles 0..15, element 2j in bits 3:0 */
+  const uint16_t* scales;   /* [N][K/64] bf16                                          */
+  const uint8_t* zeros;     /* [N][K/64] zero points 0..15                             */
+  const uint16_t* bias;     /* [N] bf16 or NULL                                        */
+} awq_w4a16_weight;
+
+/* Returns SVDQ_OK if `hip_device` exists and is a gfx950 (MI355X-class) GPU, else
+ * SVDQ_ERR_DEVICE with the reason in svdq_last_error().  This is the load-time
+ * capability check with a clear error (infolabhq tutorial, hardware caveats
+ * section: unsupported GPUs are rejected at load). */
+svdq_status svdq_check_device(int hip_device);
+
+/* Bytes of the packed weight buffers for a K x N svdq_w4a4 layer (0 on bad
+ * config or shape).  *codes_bytes and *scales_bytes receive the two parts. */
+size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
+                                size_t* codes_bytes, size_t* scales_bytes);
+
+/* Converts interchange-layout weight codes and scales into the kernel layout.
+ *   codes        [N][K/2]  int4: two's complement nibbles, element 2j in bits 3:0;
+ *                          nvfp4: E2M1 nibbles, same order
+ *   scales       [N][K/G]  int4: bf16; nvfp4: E4M3 bytes
+ *   packed_codes, packed_scales: buffers of svdq_packed_weight_bytes()
+ * int4 codes must lie in the symmetric range [-7, 7] (what the layer's
+ * quantizer produces); a -8 code makes the call return SVDQ_ERR_RANGE.  This
+ * is an offline step: it synchronizes `stream` before returning. */
+svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N,
+                             const uint8_t* codes, const void* scales,
+                             uint8_t* packed_codes, void* packed_scales, hipStream_t stream);
+
+/* Workspace bytes svdq_w4a4_linear needs for M tokens of K inputs. */
+size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);
+
+/* Activation side of the layer (smoothing, low-rank down projection, quantization)
+ * in the interchange layout:
+ *   x          [M][K] bf16 activations
+ *   smooth     [K] bf16 multiplier m;  lora_down [r][K] bf16 (NULL iff r == 0)
+ *   act_global NVFP4 static activation scale g_x (ignored for int4)
+ *   codes      [M][K/2] out: int4 two's complement / E2M1 nibbles, 2j in bits 3:0
+ *   scales     [M][K/G] out: bf16 (int4) or E4M3 bytes (nvfp4)
+ *   lora_act   [M][r] out: U = bf16(xhat @ lora_down^T)  (NULL iff r == 0)
+ * int4: s = bf16(amax/7) per 64-group, q = round-half-even(xhat/s) in [-7, 7].
+ * nvfp4: s = E4M3(amax / (6 g_x)) per 16-block, code = E2M1(xhat / (s g_x)). */
+svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
+                              const uint16_t* smooth, const uint16_t* lora_down, float act_global,
+                              uint8_t* codes, void* scales, uint16_t* lora_act, hipStream_t stream);
+
+/* The whole layer: Y[M][N] (bf16) = svdq_w4a4(X[M][K]).  `workspace` holds the
+ * quantized activations between the two kernels (svdq_workspace_bytes). */
+svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                             const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The AWQ W4A16 comparison layer: Y[M][N] (bf16) from bf16 X[M][K].  cfg must be
+ * {int4, 64, rank 0, bf16}. */
+svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
+                             const uint16_t* x, int64_t M, uint16_t* y, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* svdq_status_str(svdq_status s);
+
+/* Message describing the last error of the calling thread ("" if none). */
+const char* svdq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H */

@@ -1,0 +1,86 @@
+"""Test-side helpers: host <-> device transfer of bit patterns, the Y tolerance check,
+and a decoder of the library's kernel layouts (so tests can compare them with the
+oracle's interchange codes)."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import formats as F
+
+Z0 = 0x18618618
+Z2 = 0x61861861
+
+
+def dev_bf16(bits: np.ndarray):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_u8(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def host_bits(t) -> np.ndarray:
+    """bf16 / uint8 device tensor -> numpy bit patterns (uint16 / uint8)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def check_y(y_bits: np.ndarray, r: np.ndarray, max_ulp: int = 2, max_rel: float = 1e-2,
+            mean_rel: float = 2e-3, floor_frac: float = 1e-3):
+    """The output tolerance: within `max_ulp` bf16 steps of bf16(r) wherever
+    |r| >= floor (floor = 1e-3 rms(r)), and relative error e = |y - r| / max(|r|, floor)
+    with max(e) <= 1e-2 and mean(e) <= 2e-3."""
+    y = F.bf16_to_f64(y_bits)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    floor = floor_frac * rms if rms > 0 else 1e-30
+    big = np.abs(r) >= floor
+    ref_bits = F.bf16_rne(r.astype(np.float32))
+    ulp = F.bf16_ulp_distance(y_bits, ref_bits)
+    worst_ulp = int(ulp[big].max()) if big.any() else 0
+    e = np.abs(y - r) / np.maximum(np.abs(r), floor)
+    stats = dict(worst_ulp=worst_ulp, max_rel=float(e.max()) if e.size else 0.0,
+                 mean_rel=float(e.mean()) if e.size else 0.0)
+    assert worst_ulp <= max_ulp, stats
+    assert stats["max_rel"] <= max_rel, stats
+    assert stats["mean_rel"] <= mean_rel, stats
+    return stats
+
+
+def decode_compact_int4(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
+    """Kernel-layout int4 codes (compact E2M3 runs) -> signed codes [rows_pad, K].
+
+    Layout: ((row // 32) * G + g) * 1024 + h * 512 + (row % 32) * 16 + 8 p bytes hold
+    the run (x0, x1) of k = 64 g + 32 h + 16 p + j, j = 0..15.
+    """
+    G = K // 64
+    w = np.asarray(buf, dtype=np.uint8)[: rows_pad * K // 2].view(np.uint32)
+    w = w.reshape(rows_pad // 32, G, 2, 32, 2, 2).astype(np.uint64)   # rb, g, h, r, p, (x0,x1)
+    x0, x1 = w[..., 0], w[..., 1]
+    o0 = x0 & (~Z0 & 0xFFFFFFFF)
+    o2 = x1 & (~Z2 & 0xFFFFFFFF)
+    o1 = (x0 & Z0) | (x1 & Z2)
+    out = np.zeros(o0.shape + (16,), dtype=np.int64)
+    for j in range(16):
+        pos = 6 * j
+        f = np.zeros(o0.shape, dtype=np.uint64)
+        for b in range(6):
+            p = pos + b
+            src = o0 if p < 32 else (o1 if p < 64 else o2)
+            f |= ((src >> np.uint64(p % 32)) & np.uint64(1)) << np.uint64(b)
+        mag = (f & np.uint64(7)).astype(np.int64)
+        assert np.all((f & np.uint64(0x18)) == 0), "exponent bits set in an int4 field"
+        out[..., j] = np.where(f & np.uint64(0x20), -mag, mag)
+    # axes: rb, g, h, r, p, j -> row = rb*32 + r, k = 64 g + 32 h + 16 p + j
+    out = out.transpose(0, 3, 1, 2, 4, 5).reshape(rows_pad, K)
+    return out
+
+
+def int4_interchange(q: np.ndarray) -> np.ndarray:
+    return F.pack_nibbles(F.int4_encode(q))

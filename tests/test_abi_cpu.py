@@ -1,0 +1,125 @@
+"""The C ABI on a host without a GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import w4a4_rank_corrected_linear_amd._lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HAVE_GPU = torch.cuda.is_available()
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+FAKE_MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_functions()
+    assert {"svdq_w4a4_linear", "svdq_quantize_act", "awq_w4a16_linear"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_status_strings():
+    for s, name in enumerate(["SVDQ_OK", "SVDQ_ERR_NULL", "SVDQ_ERR_CONFIG", "SVDQ_ERR_SHAPE",
+                              "SVDQ_ERR_ALIGN", "SVDQ_ERR_WORKSPACE", "SVDQ_ERR_DEVICE",
+                              "SVDQ_ERR_HIP", "SVDQ_ERR_RANGE"]):
+        assert L.status_str(s) == name
+
+
+def cfg(precision=L.INT4, group=64, rank=32, dtype=L.BF16):
+    return L.SvdqConfig(precision, group, rank, dtype)
+
+
+def weight(K=512, N=512, rank=32, ptr=FAKE):
+    lora = ptr if rank else None
+    return L.SvdqW4A4Weight(K, N, ptr, ptr, 1.0, ptr, lora, lora, ptr)
+
+
+def linear(c, w, M=16, ws_bytes=1 << 30, x=FAKE, y=FAKE, ws=FAKE):
+    return L.lib().svdq_w4a4_linear(ctypes.byref(c), ctypes.byref(w), x, M, 1.0, y, ws, ws_bytes, None)
+
+
+def test_config_table():
+    """Supported (method, precision, group): svdq (int4, 64), svdq (nvfp4, 16),
+    awq (int4, 64); anything else is SVDQ_ERR_CONFIG."""
+    lib = L.lib()
+    assert lib.svdq_workspace_bytes(ctypes.byref(cfg()), 16, 512) > 0
+    for bad in [cfg(group=16), cfg(precision=L.NVFP4, group=64), cfg(group=32), cfg(rank=8),
+                cfg(rank=64), cfg(dtype=1), cfg(precision=7)]:
+        assert lib.svdq_workspace_bytes(ctypes.byref(bad), 16, 512) == 0
+        assert linear(bad, weight()) == L.ERR_CONFIG
+    awq = L.AwqW4A16Weight(512, 512, FAKE, FAKE, FAKE, None)
+    assert lib.awq_w4a16_linear(ctypes.byref(cfg(rank=32)), ctypes.byref(awq), FAKE, 4, FAKE, None) == L.ERR_CONFIG
+    assert lib.awq_w4a16_linear(ctypes.byref(cfg(group=16)), ctypes.byref(awq), FAKE, 4, FAKE, None) == L.ERR_CONFIG
+
+
+def test_null_arguments():
+    c = cfg()
+    assert linear(c, weight(), x=None) == L.ERR_NULL
+    assert linear(c, weight(), y=None) == L.ERR_NULL
+    w = weight()
+    w.lora_up = None
+    assert linear(c, w) == L.ERR_NULL            # rank 32 needs both factors
+    lib = L.lib()
+    assert lib.svdq_quantize_act(ctypes.byref(c), None, 4, 512, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None) == L.ERR_NULL
+    assert lib.svdq_pack_weight(ctypes.byref(c), 512, 512, FAKE, None, FAKE, FAKE, None) == L.ERR_NULL
+    assert "NULL" in L.last_error()
+
+
+@pytest.mark.parametrize("K,N,M", [(500, 512, 4), (512, 500, 4), (64, 512, 4), (512, 64, 4),
+                                   (512, 512, -1), (512, 200, 4)])
+def test_shape_rules(K, N, M):
+    assert linear(cfg(), weight(K, N), M=M) == L.ERR_SHAPE
+
+
+def test_alignment():
+    assert linear(cfg(), weight(), x=FAKE_MISALIGNED) == L.ERR_ALIGN
+    assert linear(cfg(), weight(ptr=FAKE_MISALIGNED)) == L.ERR_ALIGN
+
+
+def test_workspace_size_and_check():
+    lib = L.lib()
+    need = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 100, 512)
+    # M padded to 128 rows: codes 128*512/2, scales 8*128*2, U 128*32*2 (256-aligned)
+    assert need == 32768 + 2048 + 8192
+    assert linear(cfg(), weight(), M=100, ws_bytes=need - 1) == L.ERR_WORKSPACE
+    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 32768 + 2048
+
+
+def test_packed_weight_bytes():
+    lib = L.lib()
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    tot = lib.svdq_packed_weight_bytes(ctypes.byref(cfg()), 3072, 3072, ctypes.byref(cb), ctypes.byref(sb))
+    assert cb.value == 3072 * 3072 // 2
+    assert sb.value == 48 * 3072 * 2 + 256
+    assert tot == cb.value + sb.value
+
+
+def test_empty_batch_is_ok_without_launch():
+    assert linear(cfg(), weight(), M=0) == L.OK
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="a device is present: a valid call would launch")
+def test_no_device_is_a_clear_error():
+    assert L.lib().svdq_check_device(0) == L.ERR_DEVICE
+    assert "device" in L.last_error().lower()
+    assert linear(cfg(), weight(), M=16) == L.ERR_DEVICE
+
+
+def test_python_layer_rejects_host_tensors():
+    import w4a4_rank_corrected_linear_amd as svdq
+    x = torch.zeros(4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        svdq.quantize_act(x, torch.zeros(512, dtype=torch.bfloat16))

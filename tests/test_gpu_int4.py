@@ -1,0 +1,194 @@
+"""GPU parity of the int4 path against the oracle: svdq_quantize_act (codes and
+scales bit-exact, U within 1 bf16 step), svdq_pack_weight, and svdq_w4a4_linear
+(Y within the stated tolerance; bit-exact on grid-exact inputs)."""
+
+import numpy as np
+import pytest
+import torch
+
+import w4a4_rank_corrected_linear_amd as svdq
+from helpers import (check_y, decode_compact_int4, dev_bf16, dev_u8, host_bits,
+                     int4_interchange)
+from oracle import formats as F
+from oracle import linear as OL
+from oracle import prep as P
+from oracle import quant as Q
+from synth import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_dev(layer, bias=True):
+    return svdq.SvdqLinear.from_interchange(
+        dev_u8(layer.qweight), dev_bf16(layer.wscales), dev_bf16(layer.smooth),
+        dev_bf16(layer.lora_down) if layer.rank else None,
+        dev_bf16(layer.lora_up) if layer.rank else None,
+        dev_bf16(layer.bias) if (bias and layer.bias is not None) else None)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    li = I.layer_inputs(**I.TINY)
+    return li, P.prepare_svdq(li.w, li.x_cal, li.bias, rank=32)
+
+
+@pytest.mark.parametrize("M", [1, 17, 255, 256])
+def test_quantize_act_int4_bitexact(tiny, M):
+    li, layer = tiny
+    x = li.x[:M]
+    ref = Q.quantize_act_int4(x, layer.smooth, layer.lora_down)
+    codes, scales, u = svdq.quantize_act(dev_bf16(x), dev_bf16(layer.smooth), dev_bf16(layer.lora_down))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(codes), ref["codes"])
+    assert np.array_equal(host_bits(scales), ref["scales"])
+    assert F.bf16_ulp_distance(host_bits(u), ref["lora_act"]).max() <= 1
+
+
+def test_quantize_act_int4_wide_k_rank16_and_outliers():
+    rng = np.random.default_rng(77)
+    M, K = 40, 3072
+    idx = I.outlier_channels(K, 31, 5)
+    x = I.activations(M, K, 99, idx, 30.0)
+    m = F.bf16_rne(rng.uniform(0.05, 1.5, K).astype(np.float32))
+    ld = F.bf16_rne((rng.standard_normal((16, K)) * 0.05).astype(np.float32))
+    ref = Q.quantize_act_int4(x, m, ld)
+    codes, scales, u = svdq.quantize_act(dev_bf16(x), dev_bf16(m), dev_bf16(ld))
+    assert np.array_equal(host_bits(codes), ref["codes"])
+    assert np.array_equal(host_bits(scales), ref["scales"])
+    assert F.bf16_ulp_distance(host_bits(u), ref["lora_act"]).max() <= 1
+
+
+def test_quantize_act_ties_and_zero_groups():
+    """Exact half-way quotients round to even; all-zero groups give zero scale."""
+    rng = np.random.default_rng(78)
+    M, K = 32, 256
+    k = rng.integers(-7, 8, size=(M, K)).astype(np.float64)
+    k += np.where(rng.random((M, K)) < 0.3, 0.5, 0.0)           # plant ties
+    k = np.clip(k, -6.5, 6.5)
+    k[:, ::64] = 7.0
+    s = 2.0 ** rng.integers(-8, 4, size=(M, K // 64))
+    x = k * np.repeat(s, 64, axis=1)
+    x[3, 64:128] = 0.0
+    xb = F.bf16_rne(x.astype(np.float32))
+    assert np.array_equal(F.bf16_to_f64(xb), x)
+    one = F.bf16_rne(np.ones(K, np.float32))
+    ref = Q.quantize_act_int4(xb, one, None)
+    codes, scales, _ = svdq.quantize_act(dev_bf16(xb), dev_bf16(one), None)
+    assert np.array_equal(host_bits(codes), ref["codes"])
+    assert np.array_equal(host_bits(scales), ref["scales"])
+
+
+def test_pack_weight_layout(tiny):
+    _, layer = tiny
+    pc, ps = svdq.pack_weight(dev_u8(layer.qweight), dev_bf16(layer.wscales))
+    q = decode_compact_int4(host_bits(pc), layer.N, layer.K)
+    assert np.array_equal(q, F.int4_decode(F.unpack_nibbles(layer.qweight)))
+    G = layer.K // 64
+    st = host_bits(ps)[: G * layer.N * 2].view(np.uint16).reshape(G, layer.N)
+    assert np.array_equal(st, layer.wscales.T)
+
+
+def test_pack_weight_rejects_minus_eight(tiny):
+    _, layer = tiny
+    bad = layer.qweight.copy()
+    bad[5, 7] = (bad[5, 7] & 0x0F) | 0x80          # a -8 code
+    with pytest.raises(svdq.SvdqError) as ei:
+        svdq.pack_weight(dev_u8(bad), dev_bf16(layer.wscales))
+    assert ei.value.status == 8
+
+
+@pytest.mark.parametrize("M", [256, 1, 17, 129, 255])
+def test_linear_tiny(tiny, M):
+    li, layer = tiny
+    dl = _layer_dev(layer)
+    y = dl(dev_bf16(li.x[:M]))
+    ref = OL.w4a4_linear("int4", li.x[:M], layer)
+    check_y(host_bits(y), ref["r"])
+
+
+def test_linear_rank0_no_bias_and_rank16():
+    li = I.layer_inputs(config_id=9, M=96, K=1024, N=384, outlier_count=8, factor=20.0)
+    for rank, bias in [(0, None), (16, li.bias)]:
+        layer = P.prepare_svdq(li.w, li.x_cal, bias, rank=rank)
+        y = _layer_dev(layer)(dev_bf16(li.x))
+        check_y(host_bits(y), OL.w4a4_linear("int4", li.x, layer)["r"])
+
+
+def test_linear_grid_exact_is_bit_exact():
+    """Rank 0, no bias, X and W on the int4 grid with power-of-two scales in a narrow
+    range: every fp32 step on the GPU is exact, so Y equals bf16(r) bit for bit."""
+    rng = np.random.default_rng(79)
+    M, K, N = 200, 512, 256
+    kx = rng.integers(-7, 8, size=(M, K))
+    kx[:, ::64] = 7
+    sx = 2.0 ** rng.integers(-3, 0, size=(M, K // 64))
+    x = F.bf16_rne((kx * np.repeat(sx, 64, axis=1)).astype(np.float32))
+    kw = rng.integers(-7, 8, size=(N, K))
+    sw = 2.0 ** rng.integers(-7, -5, size=(N, K // 64))
+    one = F.bf16_rne(np.ones(K, np.float32))
+    layer = P.SvdqLayer(precision="int4", K=K, N=N, rank=0, qweight=int4_interchange(kw),
+                        wscales=F.bf16_rne(sw.astype(np.float32)), w_global=1.0, act_global=1.0,
+                        smooth=one, lora_down=np.zeros((0, K), np.uint16),
+                        lora_up=np.zeros((N, 0), np.uint16), bias=None)
+    ref = OL.w4a4_linear("int4", x, layer)
+    y = _layer_dev(layer)(dev_bf16(x))
+    assert np.array_equal(host_bits(y), ref["y"])
+
+
+def test_workspace_matches_standalone_quantize(tiny):
+    """The fused call's quantized activations equal svdq_quantize_act's outputs."""
+    li, layer = tiny
+    M = 200
+    dl = _layer_dev(layer)
+    ws = torch.zeros(dl.workspace(M, torch.device("cuda")).numel(), dtype=torch.uint8, device="cuda")
+    dl(dev_bf16(li.x[:M]), workspace=ws)
+    torch.cuda.synchronize()
+    ref = Q.quantize_act_int4(li.x[:M], layer.smooth, layer.lora_down)
+    w = host_bits(ws)
+    M_pad, K, G = 256, layer.K, layer.K // 64
+    q = decode_compact_int4(w, M_pad, K)
+    assert np.array_equal(q[:M], ref["q"])
+    assert np.all(q[M:] == 0)
+    off_s = M_pad * K // 2
+    s = w[off_s: off_s + G * M_pad * 2].view(np.uint16).reshape(G, M_pad)
+    assert np.array_equal(s[:, :M], ref["scales"].T)
+    off_u = off_s + G * M_pad * 2
+    u = w[off_u: off_u + M_pad * 32 * 2].view(np.uint16).reshape(M_pad, 32)
+    assert F.bf16_ulp_distance(u[:M], ref["lora_act"]).max() <= 1
+
+
+def test_linear_deterministic_and_writes_every_output(tiny):
+    li, layer = tiny
+    dl = _layer_dev(layer)
+    M = 255
+    x = dev_bf16(li.x[:M])
+    guard = torch.full((M + 8, layer.N), -1, dtype=torch.int16, device="cuda")
+    y1 = guard[:M].view(torch.bfloat16)
+    dl(x, out=y1)
+    g = host_bits(guard.view(torch.bfloat16))
+    assert not np.any(g[:M] == 0xFFFF), "an output element was not written"
+    assert np.all(g[M:] == 0xFFFF), "write past the end of Y"
+    y2 = dl(x)
+    assert np.array_equal(host_bits(y2), g[:M])
+
+
+@pytest.fixture(scope="module")
+def attn_proj():
+    cfg = dict(I.ATTN_PROJ)
+    li = I.layer_inputs(**cfg)
+    return li, P.prepare_svdq(li.w, li.x_cal, li.bias, rank=32)
+
+
+def test_linear_attention_projection_full_size(attn_proj):
+    """M = 4096, K = N = 3072 in the benchmarked launch; the oracle checks a sample
+    of rows (rows are independent)."""
+    li, layer = attn_proj
+    dl = _layer_dev(layer)
+    y = host_bits(dl(dev_bf16(li.x)))
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 61), [4094, 4095]]))
+    ref = OL.w4a4_linear_rows("int4", li.x, layer, rows)
+    check_y(y[rows], ref["r"])
+    codes, scales, u = svdq.quantize_act(dev_bf16(li.x[rows]), dev_bf16(layer.smooth),
+                                         dev_bf16(layer.lora_down))
+    assert np.array_equal(host_bits(codes), ref["act"]["codes"])
+    assert np.array_equal(host_bits(scales), ref["act"]["scales"])

@@ -1,0 +1,169 @@
+"""torch-facing wrappers of the C ABI: allocation of outputs and workspace with
+torch, the current HIP stream, and argument marshalling.  No arithmetic here."""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+
+def _p(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _want(t: torch.Tensor, dtype, name: str, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def check_device(device: int | None = None) -> None:
+    dev = torch.cuda.current_device() if device is None else device
+    L.check(L.lib().svdq_check_device(dev), "svdq_check_device")
+
+
+def workspace_bytes(precision: str, rank: int, M: int, K: int) -> int:
+    cfg = L.config(precision, rank)
+    return int(L.lib().svdq_workspace_bytes(ctypes.byref(cfg), M, K))
+
+
+def _scale_dtype(precision: str):
+    return torch.bfloat16 if precision == "int4" else torch.uint8
+
+
+def quantize_act(x: torch.Tensor, smooth: torch.Tensor, lora_down: torch.Tensor | None = None,
+                 precision: str = "int4", act_global: float = 1.0):
+    """svdq_quantize_act: returns (codes [M, K/2] u8, scales [M, K/G], lora_act [M, r] bf16)."""
+    _want(x, torch.bfloat16, "x")
+    M, K = x.shape
+    _want(smooth, torch.bfloat16, "smooth", (K,))
+    rank = 0 if lora_down is None else lora_down.shape[0]
+    if lora_down is not None:
+        _want(lora_down, torch.bfloat16, "lora_down", (rank, K))
+    cfg = L.config(precision, rank)
+    G = K // cfg.group_size
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M, G), dtype=_scale_dtype(precision), device=x.device)
+    lora_act = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device) if rank else None
+    st = L.lib().svdq_quantize_act(ctypes.byref(cfg), _p(x), M, K, _p(smooth), _p(lora_down),
+                                   float(act_global), _p(codes), _p(scales), _p(lora_act), _stream())
+    L.check(st, "svdq_quantize_act")
+    return codes, scales, lora_act
+
+
+def pack_weight(codes: torch.Tensor, scales: torch.Tensor, precision: str = "int4"):
+    """svdq_pack_weight: interchange [N, K/2] codes + [N, K/G] scales -> kernel layout.
+
+    Returns (packed_codes, packed_scales) as uint8 tensors.  Synchronizes the stream.
+    """
+    _want(codes, torch.uint8, "codes")
+    N, K2 = codes.shape
+    K = 2 * K2
+    cfg = L.config(precision, 0)
+    _want(scales, _scale_dtype(precision), "scales", (N, K // cfg.group_size))
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    total = L.lib().svdq_packed_weight_bytes(ctypes.byref(cfg), K, N, ctypes.byref(cb), ctypes.byref(sb))
+    if total == 0:
+        L.check(L.ERR_SHAPE, "svdq_packed_weight_bytes")
+    pc = torch.empty(cb.value, dtype=torch.uint8, device=codes.device)
+    ps = torch.empty(sb.value, dtype=torch.uint8, device=codes.device)
+    st = L.lib().svdq_pack_weight(ctypes.byref(cfg), K, N, _p(codes), _p(scales), _p(pc), _p(ps),
+                                  _stream())
+    L.check(st, "svdq_pack_weight")
+    return pc, ps
+
+
+class SvdqLinear:
+    """A prepared svdq_w4a4 layer resident in device memory.
+
+    smooth [K] bf16, lora_down [r, K] bf16, lora_up [N, r] bf16, bias [N] bf16 or None;
+    qweight/wscales in the kernel layout (see ``pack_weight``).
+    """
+
+    def __init__(self, K: int, N: int, qweight, wscales, smooth, lora_down, lora_up, bias,
+                 precision: str = "int4", w_global: float = 1.0, act_global: float = 1.0):
+        self.K, self.N = K, N
+        self.precision = precision
+        self.rank = 0 if lora_down is None else lora_down.shape[0]
+        self.qweight, self.wscales = qweight, wscales
+        self.smooth, self.lora_down, self.lora_up, self.bias = smooth, lora_down, lora_up, bias
+        self.w_global, self.act_global = float(w_global), float(act_global)
+        self.cfg = L.config(precision, self.rank)
+        self._w = L.SvdqW4A4Weight(K, N, qweight.data_ptr(), wscales.data_ptr(), self.w_global,
+                                   smooth.data_ptr(),
+                                   None if lora_down is None else lora_down.data_ptr(),
+                                   None if lora_up is None else lora_up.data_ptr(),
+                                   None if bias is None else bias.data_ptr())
+        self._ws = None
+
+    @classmethod
+    def from_interchange(cls, codes, scales, smooth, lora_down, lora_up, bias,
+                         precision: str = "int4", w_global: float = 1.0, act_global: float = 1.0):
+        N, K2 = codes.shape
+        pc, ps = pack_weight(codes, scales, precision)
+        return cls(2 * K2, N, pc, ps, smooth, lora_down, lora_up, bias, precision, w_global,
+                   act_global)
+
+    def workspace(self, M: int, device) -> torch.Tensor:
+        need = max(int(L.lib().svdq_workspace_bytes(ctypes.byref(self.cfg), M, self.K)), 256)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != device:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, act_global: float | None = None):
+        _want(x, torch.bfloat16, "x")
+        M, K = x.shape
+        if K != self.K:
+            raise ValueError(f"x has K = {K}, layer expects {self.K}")
+        y = torch.empty((M, self.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+        ws = self.workspace(M, x.device) if workspace is None else workspace
+        g = self.act_global if act_global is None else float(act_global)
+        st = L.lib().svdq_w4a4_linear(ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), M, g,
+                                      _p(y), _p(ws), ws.numel(), _stream())
+        L.check(st, "svdq_w4a4_linear")
+        return y
+
+    __call__ = forward
+
+
+class AwqLinear:
+    """An awq_w4a16 layer: qweight [N, K/2] u8, scales [N, K/64] bf16, zeros [N, K/64] u8."""
+
+    def __init__(self, qweight, scales, zeros, bias=None):
+        N, K2 = qweight.shape
+        self.K, self.N = 2 * K2, N
+        self.qweight, self.scales, self.zeros, self.bias = qweight, scales, zeros, bias
+        self.cfg = L.config("int4", 0)
+        self._w = L.AwqW4A16Weight(self.K, N, qweight.data_ptr(), scales.data_ptr(),
+                                   zeros.data_ptr(), None if bias is None else bias.data_ptr())
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None):
+        return awq_w4a16_linear(x, self, out)
+
+    __call__ = forward
+
+
+def awq_w4a16_linear(x: torch.Tensor, layer: AwqLinear, out: torch.Tensor | None = None):
+    _want(x, torch.bfloat16, "x")
+    M, K = x.shape
+    y = torch.empty((M, layer.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    st = L.lib().awq_w4a16_linear(ctypes.byref(layer.cfg), ctypes.byref(layer._w), _p(x), M, _p(y),
+                                  _stream())
+    L.check(st, "awq_w4a16_linear")
+    return y

@@ -1,0 +1,74 @@
+// Weight packing: interchange layout -> kernel layout (an offline step).
+//
+// int4: codes [N][K/2] two's complement nibbles -> compact E2M3 layout of common.h
+//       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N].
+//       A -8 code cannot be held by the sign-magnitude E2M3 field: it raises the
+//       range flag, which the host turns into SVDQ_ERR_RANGE.
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+// One thread per (row-block, group, half, row % 32): reads the 16 interchange bytes
+// of 32 codes and writes the 16 compact bytes of the same 32 codes.
+__global__ void __launch_bounds__(256)
+k_pack_int4_codes(const uint8_t* __restrict__ codes, uint4* __restrict__ out, int N, int K,
+                  int* __restrict__ flag) {
+  const int G = K >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)N * G * 2;
+  if (t >= total) return;
+  const int r = (int)(t & 31);
+  const int h = (int)((t >> 5) & 1);
+  const int64_t rest = t >> 6;         // (row-block, group)
+  const int g = (int)(rest % G);
+  const int64_t rb = rest / G;
+  const int64_t n = rb * 32 + r;
+  const uint4 v = *reinterpret_cast<const uint4*>(codes + n * (K >> 1) + 32 * g + 16 * h);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t outw[4];
+  bool bad = false;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    uint32_t t0 = 0, t1 = 0, t2 = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t nib = (w[2 * p + (j >> 3)] >> (4 * (j & 7))) & 0xFu;
+      const int q = (nib & 8u) ? (int)nib - 16 : (int)nib;
+      bad |= (q == -8);
+      const uint32_t f = e2m3_field(q < -7 ? -7 : q);
+      const int pos = 6 * j;
+      if (pos < 32) t0 |= f << pos;
+      if (pos + 6 > 32 && pos < 64) t1 |= (pos >= 32) ? (f << (pos - 32)) : (f >> (32 - pos));
+      if (pos + 6 > 64) t2 |= (pos >= 64) ? (f << (pos - 64)) : (f >> (64 - pos));
+    }
+    fp6_compact(t0, t1, t2, outw[2 * p], outw[2 * p + 1]);
+  }
+  out[t] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  if (bad) atomicOr(flag, 1);
+}
+
+__global__ void __launch_bounds__(256)
+k_transpose_scales_u16(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int N, int G) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)N * G) return;
+  const int64_t g = t / N, n = t % N;
+  out[t] = in[n * G + g];
+}
+
+__global__ void k_zero_flag(int* flag) { *flag = 0; }
+
+hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
+                            uint16_t* out_scales, int* flag, int N, int K, hipStream_t st) {
+  const int G = K >> 6;
+  hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
+  const int64_t total = (int64_t)N * G * 2;
+  hipLaunchKernelGGL(k_pack_int4_codes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     codes, reinterpret_cast<uint4*>(out_codes), N, K, flag);
+  const int64_t ts = (int64_t)N * G;
+  hipLaunchKernelGGL(k_transpose_scales_u16, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
+                     scales, out_scales, N, G);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -1,0 +1,291 @@
+// Host side of the C ABI declared in include/svdq.h: argument validation (all on
+// the host, before any device access), the per-device architecture check,
+// workspace layout and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "svdq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+svdq_status fail(svdq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+svdq_status ok() {
+  g_last_error.clear();
+  return SVDQ_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+svdq_status check_device_impl(int dev) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0)
+    return fail(SVDQ_ERR_DEVICE, "no HIP device available (%s)",
+                e != hipSuccess ? hipGetErrorString(e) : "device count is 0");
+  if (dev < 0 || dev >= count)
+    return fail(SVDQ_ERR_DEVICE, "device %d out of range (%d devices)", dev, count);
+  if (dev < kMaxDevices) {
+    const int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 1) return SVDQ_OK;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess)
+    return fail(SVDQ_ERR_DEVICE, "hipGetDeviceProperties(%d) failed: %s", dev, hipGetErrorString(e));
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_state[dev].store(good ? 1 : 2, std::memory_order_release);
+  if (!good)
+    return fail(SVDQ_ERR_DEVICE,
+                "device %d is %s; this library is built for gfx950 (MI355X-class) only", dev,
+                prop.gcnArchName);
+  return SVDQ_OK;
+}
+
+svdq_status check_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(SVDQ_ERR_DEVICE, "no current HIP device (%s)", hipGetErrorString(e));
+  return check_device_impl(dev);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+svdq_status check_svdq_config(const svdq_config* c) {
+  if (c->compute_dtype != SVDQ_BF16)
+    return fail(SVDQ_ERR_CONFIG, "compute_dtype %d unsupported (bf16 only)", c->compute_dtype);
+  const bool int4 = c->precision == SVDQ_INT4 && c->group_size == 64;
+  const bool nvfp4 = c->precision == SVDQ_NVFP4 && c->group_size == 16;
+  if (!int4 && !nvfp4)
+    return fail(SVDQ_ERR_CONFIG,
+                "svdq_w4a4 supports (int4, group 64) and (nvfp4, group 16); got (precision %d, "
+                "group %d)", c->precision, c->group_size);
+  if (c->rank != 0 && c->rank != 16 && c->rank != 32)
+    return fail(SVDQ_ERR_CONFIG, "rank %d unsupported (0, 16 or 32)", c->rank);
+  if (nvfp4)
+    return fail(SVDQ_ERR_CONFIG, "nvfp4 is not available in this build");
+  return SVDQ_OK;
+}
+
+svdq_status check_k(int64_t K) {
+  if (K < 128 || K % 128 != 0 || K > (int64_t(1) << 20))
+    return fail(SVDQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128 (<= 2^20)", (long long)K);
+  return SVDQ_OK;
+}
+
+svdq_status check_n(int64_t N) {
+  if (N < 128 || N % 128 != 0 || N > (int64_t(1) << 20))
+    return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 128 (<= 2^20)", (long long)N);
+  return SVDQ_OK;
+}
+
+svdq_status check_m(int64_t M, int64_t K) {
+  if (M < 0 || M > (int64_t(1) << 24) || M * K > (int64_t(1) << 36))
+    return fail(SVDQ_ERR_SHAPE, "M = %lld out of range (0 <= M <= 2^24, M*K <= 2^36)", (long long)M);
+  return SVDQ_OK;
+}
+
+struct WsLayout {
+  int64_t M_pad = 0;
+  size_t codes = 0, scales = 0, lora = 0, total = 0;
+};
+
+WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
+  WsLayout L;
+  L.M_pad = round_up(M, 128);
+  const int64_t G = K / c->group_size;
+  const size_t codes = (size_t)(L.M_pad * K / 2);
+  const size_t scales = (size_t)(G * L.M_pad * 2);
+  const size_t lora = (size_t)(L.M_pad * c->rank * 2);
+  L.codes = 0;
+  L.scales = (size_t)round_up((int64_t)codes, 256);
+  L.lora = L.scales + (size_t)round_up((int64_t)scales, 256);
+  L.total = L.lora + (size_t)round_up((int64_t)lora, 256);
+  return L;
+}
+
+svdq_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SVDQ_OK;
+}
+
+#define SVDQ_TRY(expr)                    \
+  do {                                    \
+    const svdq_status _s = (expr);        \
+    if (_s != SVDQ_OK) return _s;         \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_check_device(int hip_device) {
+  const svdq_status s = check_device_impl(hip_device);
+  return s == SVDQ_OK ? ok() : s;
+}
+
+size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N, size_t* codes_bytes,
+                                size_t* scales_bytes) {
+  if (!cfg || check_svdq_config(cfg) != SVDQ_OK || check_k(K) != SVDQ_OK || check_n(N) != SVDQ_OK) {
+    if (codes_bytes) *codes_bytes = 0;
+    if (scales_bytes) *scales_bytes = 0;
+    return 0;
+  }
+  const int64_t G = K / cfg->group_size;
+  const size_t cb = (size_t)(N * K / 2);
+  const size_t sb = (size_t)round_up(G * N * 2, 256) + 256;  // + range-flag trailer
+  if (codes_bytes) *codes_bytes = cb;
+  if (scales_bytes) *scales_bytes = sb;
+  return cb + sb;
+}
+
+svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const uint8_t* codes,
+                             const void* scales, uint8_t* packed_codes, void* packed_scales,
+                             hipStream_t stream) {
+  if (!cfg || !codes || !scales || !packed_codes || !packed_scales)
+    return fail(SVDQ_ERR_NULL, "svdq_pack_weight: NULL argument");
+  SVDQ_TRY(check_svdq_config(cfg));
+  SVDQ_TRY(check_k(K));
+  SVDQ_TRY(check_n(N));
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed_codes) || !aligned16(packed_scales))
+    return fail(SVDQ_ERR_ALIGN, "svdq_pack_weight: pointers must be 16-byte aligned");
+  SVDQ_TRY(check_current_device());
+  const int64_t G = K / cfg->group_size;
+  int* flag = reinterpret_cast<int*>(static_cast<uint8_t*>(packed_scales) + round_up(G * N * 2, 256));
+  SVDQ_TRY(hip_check(svdq::launch_pack_int4(codes, static_cast<const uint16_t*>(scales), packed_codes,
+                                             static_cast<uint16_t*>(packed_scales), flag, (int)N,
+                                             (int)K, stream),
+                     "pack kernel launch"));
+  int host_flag = 0;
+  SVDQ_TRY(hip_check(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream),
+                     "pack flag copy"));
+  SVDQ_TRY(hip_check(hipStreamSynchronize(stream), "pack synchronize"));
+  if (host_flag)
+    return fail(SVDQ_ERR_RANGE,
+                "int4 weight code -8 found: the packed layout holds the symmetric range [-7, 7]");
+  return ok();
+}
+
+size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K) {
+  if (!cfg || check_svdq_config(cfg) != SVDQ_OK || check_k(K) != SVDQ_OK || check_m(M, K) != SVDQ_OK)
+    return 0;
+  return ws_layout(cfg, M, K).total;
+}
+
+svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
+                              const uint16_t* smooth, const uint16_t* lora_down, float act_global,
+                              uint8_t* codes, void* scales, uint16_t* lora_act, hipStream_t stream) {
+  (void)act_global;
+  if (!cfg || !x || !smooth || !codes || !scales)
+    return fail(SVDQ_ERR_NULL, "svdq_quantize_act: NULL argument");
+  SVDQ_TRY(check_svdq_config(cfg));
+  if (cfg->rank > 0 && (!lora_down || !lora_act))
+    return fail(SVDQ_ERR_NULL, "svdq_quantize_act: rank %d needs lora_down and lora_act", cfg->rank);
+  SVDQ_TRY(check_k(K));
+  SVDQ_TRY(check_m(M, K));
+  if (!aligned16(x) || !aligned16(smooth) || !aligned16(codes) || !aligned16(scales) ||
+      (cfg->rank > 0 && (!aligned16(lora_down) || !aligned16(lora_act))))
+    return fail(SVDQ_ERR_ALIGN, "svdq_quantize_act: pointers must be 16-byte aligned");
+  if (M == 0) return ok();
+  SVDQ_TRY(check_current_device());
+  SVDQ_TRY(hip_check(svdq::launch_k1_int4(false, x, (int)M, (int)K, smooth,
+                                           cfg->rank ? lora_down : nullptr, cfg->rank, codes,
+                                           static_cast<uint16_t*>(scales),
+                                           cfg->rank ? lora_act : nullptr, (int)M, stream),
+                     "quantize kernel launch"));
+  return ok();
+}
+
+svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, const uint16_t* x,
+                             int64_t M, float act_global, uint16_t* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  (void)act_global;
+  if (!cfg || !w || !x || !y || !workspace || !w->qweight || !w->wscales || !w->smooth)
+    return fail(SVDQ_ERR_NULL, "svdq_w4a4_linear: NULL argument");
+  SVDQ_TRY(check_svdq_config(cfg));
+  if (cfg->rank > 0 && (!w->lora_down || !w->lora_up))
+    return fail(SVDQ_ERR_NULL, "svdq_w4a4_linear: rank %d needs lora_down and lora_up", cfg->rank);
+  SVDQ_TRY(check_k(w->K));
+  SVDQ_TRY(check_n(w->N));
+  SVDQ_TRY(check_m(M, w->K));
+  if (M * w->N > (int64_t(1) << 36))
+    return fail(SVDQ_ERR_SHAPE, "M * N too large");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || !aligned16(w->qweight) ||
+      !aligned16(w->wscales) || !aligned16(w->smooth) || (w->bias && !aligned16(w->bias)) ||
+      (cfg->rank > 0 && (!aligned16(w->lora_down) || !aligned16(w->lora_up))))
+    return fail(SVDQ_ERR_ALIGN, "svdq_w4a4_linear: pointers must be 16-byte aligned");
+  const WsLayout L = ws_layout(cfg, M, w->K);
+  if (workspace_bytes < L.total)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, L.total);
+  if (M == 0) return ok();
+  SVDQ_TRY(check_current_device());
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* a_codes = ws + L.codes;
+  uint16_t* a_scales = reinterpret_cast<uint16_t*>(ws + L.scales);
+  uint16_t* a_lora = reinterpret_cast<uint16_t*>(ws + L.lora);
+  SVDQ_TRY(hip_check(svdq::launch_k1_int4(true, x, (int)M, (int)w->K, w->smooth,
+                                           cfg->rank ? w->lora_down : nullptr, cfg->rank, a_codes,
+                                           a_scales, cfg->rank ? a_lora : nullptr, (int)L.M_pad,
+                                           stream),
+                     "quantize kernel launch"));
+  SVDQ_TRY(hip_check(svdq::launch_k2_int4(a_codes, a_scales, a_lora, w->qweight,
+                                           static_cast<const uint16_t*>(w->wscales), w->lora_up,
+                                           w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
+                                           cfg->rank, stream),
+                     "gemm kernel launch"));
+  return ok();
+}
+
+svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, const uint16_t* x,
+                             int64_t M, uint16_t* y, hipStream_t stream) {
+  (void)stream;
+  if (!cfg || !w || !x || !y || !w->qweight || !w->scales || !w->zeros)
+    return fail(SVDQ_ERR_NULL, "awq_w4a16_linear: NULL argument");
+  if (cfg->precision != SVDQ_INT4 || cfg->group_size != 64 || cfg->rank != 0 ||
+      cfg->compute_dtype != SVDQ_BF16)
+    return fail(SVDQ_ERR_CONFIG, "awq_w4a16 supports (int4, group 64, rank 0, bf16) only");
+  SVDQ_TRY(check_k(w->K));
+  SVDQ_TRY(check_n(w->N));
+  SVDQ_TRY(check_m(M, w->K));
+  return fail(SVDQ_ERR_CONFIG, "awq_w4a16 is not available in this build");
+}
+
+const char* svdq_status_str(svdq_status s) {
+  switch (s) {
+    case SVDQ_OK: return "SVDQ_OK";
+    case SVDQ_ERR_NULL: return "SVDQ_ERR_NULL";
+    case SVDQ_ERR_CONFIG: return "SVDQ_ERR_CONFIG";
+    case SVDQ_ERR_SHAPE: return "SVDQ_ERR_SHAPE";
+    case SVDQ_ERR_ALIGN: return "SVDQ_ERR_ALIGN";
+    case SVDQ_ERR_WORKSPACE: return "SVDQ_ERR_WORKSPACE";
+    case SVDQ_ERR_DEVICE: return "SVDQ_ERR_DEVICE";
+    case SVDQ_ERR_HIP: return "SVDQ_ERR_HIP";
+    case SVDQ_ERR_RANGE: return "SVDQ_ERR_RANGE";
+  }
+  return "SVDQ_ERR_UNKNOWN";
+}
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
