@@ -84,3 +84,30 @@ def decode_compact_int4(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
 
 def int4_interchange(q: np.ndarray) -> np.ndarray:
     return F.pack_nibbles(F.int4_encode(q))
+
+
+def decode_fp6_operand(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
+    """GEMM A-operand layout (E2M3 lane slots) -> signed int4 codes [rows_pad, K].
+
+    Chunk (row // 32, g) of 1536 B: lane slot h*32 + row%32 holds dwords 0-3 at
+    slot*16 and dwords 4-5 at 1024 + slot*8; field f (bits 6f..6f+5 of the six
+    dwords) is k = 64 g + 32 h + f, an E2M3 code with sign bit 5 and magnitude in
+    bits 2:0 (value q/8).
+    """
+    G = K // 64
+    b = np.asarray(buf, dtype=np.uint8)[: rows_pad // 32 * G * 1536].reshape(rows_pad // 32, G, 1536)
+    lo = b[:, :, :1024].reshape(rows_pad // 32, G, 64, 16).view(np.uint32)        # [rb, g, slot, 4]
+    hi = b[:, :, 1024:].reshape(rows_pad // 32, G, 64, 8).view(np.uint32)         # [rb, g, slot, 2]
+    dw = np.concatenate([lo, hi], axis=-1).astype(np.uint64)                       # [rb, g, slot, 6]
+    out = np.zeros(dw.shape[:-1] + (32,), dtype=np.int64)
+    for f in range(32):
+        code = np.zeros(dw.shape[:-1], dtype=np.uint64)
+        for bit in range(6):
+            p = 6 * f + bit
+            code |= ((dw[..., p // 32] >> np.uint64(p % 32)) & np.uint64(1)) << np.uint64(bit)
+        assert np.all((code & np.uint64(0x18)) == 0), "exponent bits set in an int4 field"
+        mag = (code & np.uint64(7)).astype(np.int64)
+        out[..., f] = np.where(code & np.uint64(0x20), -mag, mag)
+    # [rb, g, h*32 + r, f] -> row = 32 rb + r, k = 64 g + 32 h + f
+    out = out.reshape(rows_pad // 32, G, 2, 32, 32).transpose(0, 3, 1, 2, 4)
+    return out.reshape(rows_pad, K)

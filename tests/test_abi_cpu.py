@@ -92,10 +92,10 @@ def test_alignment():
 def test_workspace_size_and_check():
     lib = L.lib()
     need = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 100, 512)
-    # M padded to 128 rows: codes 128*512/2, scales 8*128*2, U 128*32*2 (256-aligned)
-    assert need == 32768 + 2048 + 8192
+    # M padded to 128 rows: operand 128*512*3/4, scales 8*128*2, U 128*32*2 (256-aligned)
+    assert need == 49152 + 2048 + 8192
     assert linear(cfg(), weight(), M=100, ws_bytes=need - 1) == L.ERR_WORKSPACE
-    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 32768 + 2048
+    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 49152 + 2048
 
 
 def test_packed_weight_bytes():

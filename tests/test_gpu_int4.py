@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import w4a4_rank_corrected_linear_amd as svdq
-from helpers import (check_y, decode_compact_int4, dev_bf16, dev_u8, host_bits,
-                     int4_interchange)
+from helpers import (check_y, decode_compact_int4, decode_fp6_operand, dev_bf16, dev_u8,
+                     host_bits, int4_interchange)
 from oracle import formats as F
 from oracle import linear as OL
 from oracle import prep as P
@@ -146,10 +146,10 @@ def test_workspace_matches_standalone_quantize(tiny):
     ref = Q.quantize_act_int4(li.x[:M], layer.smooth, layer.lora_down)
     w = host_bits(ws)
     M_pad, K, G = 256, layer.K, layer.K // 64
-    q = decode_compact_int4(w, M_pad, K)
+    q = decode_fp6_operand(w, M_pad, K)
     assert np.array_equal(q[:M], ref["q"])
     assert np.all(q[M:] == 0)
-    off_s = M_pad * K // 2
+    off_s = M_pad * K * 3 // 4
     s = w[off_s: off_s + G * M_pad * 2].view(np.uint16).reshape(G, M_pad)
     assert np.array_equal(s[:, :M], ref["scales"].T)
     off_u = off_s + G * M_pad * 2

@@ -114,7 +114,8 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   WsLayout L;
   L.M_pad = round_up(M, 128);
   const int64_t G = K / c->group_size;
-  const size_t codes = (size_t)(L.M_pad * K / 2);
+  // int4: GEMM A operand as E2M3 fields, 6 bits per value (3/4 byte)
+  const size_t codes = (size_t)(L.M_pad * K * 3 / 4);
   const size_t scales = (size_t)(G * L.M_pad * 2);
   const size_t lora = (size_t)(L.M_pad * c->rank * 2);
   L.codes = 0;
