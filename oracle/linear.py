@@ -24,10 +24,11 @@ from . import formats as F
 from . import quant as Q
 
 
-def _lowrank_bias(U_bits, lora_up_bits, bias_bits, M, N):
+def _lowrank_bias(U, lora_up_bits, bias_bits, M, N):
+    """U @ L2 + b in float64; U is the unrounded down projection [M, r]."""
     out = np.zeros((M, N), dtype=np.float64)
-    if lora_up_bits is not None and np.asarray(U_bits).shape[1] > 0:
-        out += F.bf16_to_f64(U_bits) @ F.bf16_to_f64(lora_up_bits).T
+    if lora_up_bits is not None and np.asarray(U).shape[1] > 0:
+        out += np.asarray(U, dtype=np.float64) @ F.bf16_to_f64(lora_up_bits).T
     if bias_bits is not None:
         out += F.bf16_to_f64(bias_bits)[None, :]
     return out

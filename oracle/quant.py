@@ -18,8 +18,13 @@ The pages leave the steps open; the readings used (all recorded in the design doc):
    in).  Block scale s = E4M3(fl32(amax / fl32(6 g))) (saturating).  Element code =
    E2M1(fl32(xhat / fl32(s g))), sign taken from the quotient's sign bit; with s = 0
    the block's codes are 0.
-4. Low-rank down projection on the smoothed activations:
-   U = bf16(xhat @ L1) with L1 = lora_down^T, summed exactly (float64) then rounded.
+4. Low-rank down projection on the smoothed activations: U = xhat @ L1 with
+   L1 = lora_down^T.  The branch's inputs and weights are bf16 and its sum is
+   accumulated in float32 on the device; U is not rounded to bf16 before the
+   up-projection.  (A bf16-rounded U would let a last-bit difference in the
+   accumulation move a whole output row by ulp(U) |L2|, far beyond a few bf16 steps
+   of Y for small outputs, so the intermediate is kept at accumulation precision.)
+   The oracle's U is the float64 sum, exact up to float64 rounding.
 """
 
 from __future__ import annotations
@@ -41,17 +46,16 @@ def smooth(x_bits, smooth_bits) -> np.ndarray:
 
 
 def lora_down(xhat_bits, lora_down_bits) -> np.ndarray:
-    """U = bf16(xhat @ lora_down^T), the exact sum rounded once via float32.
+    """U = xhat @ lora_down^T as float64 [M, r] (not rounded; step 4).
 
-    ``lora_down_bits`` is L1^T, shape [r, K].  Returns bf16 bits [M, r]
-    (an empty [M, 0] array for rank 0).
+    ``lora_down_bits`` is L1^T, shape [r, K], bf16 bits.  Rank 0 gives an empty
+    [M, 0] array.
     """
     xh = F.bf16_to_f64(xhat_bits)
     if lora_down_bits is None or np.asarray(lora_down_bits).shape[0] == 0:
-        return np.zeros((xh.shape[0], 0), dtype=np.uint16)
+        return np.zeros((xh.shape[0], 0), dtype=np.float64)
     l1t = F.bf16_to_f64(lora_down_bits)
-    u = xh @ l1t.T
-    return F.bf16_rne(u.astype(np.float32))
+    return xh @ l1t.T
 
 
 def int4_scales_codes(v_f32: np.ndarray, group: int = INT4_GROUP):
@@ -105,7 +109,7 @@ def quantize_act_int4(x_bits, smooth_bits, lora_down_bits=None):
     """svdq_quantize_act, int4 group 64.
 
     Returns dict(codes=[M, K/2] packed bytes, scales=[M, K/64] bf16 bits,
-    lora_act=[M, r] bf16 bits, q=[M, K] ints, xhat=[M, K] bf16 bits).
+    lora_act=[M, r] float64, q=[M, K] ints, xhat=[M, K] bf16 bits).
     """
     xhat = smooth(x_bits, smooth_bits)
     q, s_bits = int4_scales_codes(F.bf16_to_f32(xhat), INT4_GROUP)
@@ -117,7 +121,7 @@ def quantize_act_nvfp4(x_bits, smooth_bits, act_global: float, lora_down_bits=No
     """svdq_quantize_act, NVFP4 group 16 with E4M3 block scales.
 
     Returns dict(codes=[M, K/2] packed E2M1 bytes, scales=[M, K/16] E4M3 codes,
-    lora_act=[M, r] bf16 bits, e2m1=[M, K] codes, xhat=[M, K] bf16 bits).
+    lora_act=[M, r] float64, e2m1=[M, K] codes, xhat=[M, K] bf16 bits).
     """
     xhat = smooth(x_bits, smooth_bits)
     c, s_codes = nvfp4_scales_codes(F.bf16_to_f32(xhat), act_global, NVFP4_GROUP)

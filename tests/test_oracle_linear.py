@@ -102,7 +102,6 @@ def test_exact_low_rank_special_case():
     out = L.w4a4_linear("int4", x, layer)
     xhat = F.bf16_to_f64(x) * F.bf16_to_f64(m)[None, :]       # exact (powers of two)
     u = xhat @ F.bf16_to_f64(l1t).T                             # exact small dyadics
-    assert np.array_equal(F.bf16_to_f64(F.bf16_rne(u.astype(np.float32))), u), "u exact"
     expect = u @ F.bf16_to_f64(l2t).T + F.bf16_to_f64(b)[None, :]
     assert np.array_equal(out["r"], expect)
 

@@ -173,4 +173,15 @@ def test_lora_down_exact_sum(rank):
     assert u.shape == (8, rank)
     if rank:
         exact = F.bf16_to_f64(x) @ F.bf16_to_f64(l1t).T
-        assert np.array_equal(F.bf16_to_f64(u), exact)
+        assert np.array_equal(u, exact)
+
+
+def test_lora_down_is_not_rounded_to_bf16():
+    """U keeps the full sum: 1 + 2^-10 and 3 * 2^-12 + 2^-20 are not bf16 numbers."""
+    x = _bits(np.array([[1.0, 2.0 ** -10, 0.0, 0.0], [0.0, 0.0, 2.0 ** -12, 2.0 ** -20]]))
+    x = np.concatenate([x, np.zeros((2, 124), np.uint16)], axis=1)
+    l1t = np.zeros((1, 128), np.uint16)
+    l1t[0, :4] = _bits(np.array([1.0, 1.0, 3.0, 1.0]))
+    one = np.full(128, ONE, np.uint16)
+    u = Q.quantize_act_int4(x, one, l1t)["lora_act"]
+    assert u[0, 0] == 1.0 + 2.0 ** -10 and u[1, 0] == 3 * 2.0 ** -12 + 2.0 ** -20
