@@ -1,0 +1,328 @@
+"""Throughput of the svdq_w4a4 int4 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn_proj]
+                    [--no-cpu-baseline] [--copy-probe]
+
+One step is one svdq_w4a4_linear call (quantize kernel + GEMM kernel) on a resident
+batch: X bf16 [M, K] -> Y bf16 [M, N].  The default workload is the DiT attention
+projection of a 1024x1024 image: M = 4096 tokens, K = N = 3072, int4 group 64,
+rank 32.  Inputs are seeded synthetic data; the layer's weights are seeded bytes in
+the prepared int4 layout (codes in -7..7, bf16 scales, smoothing, low-rank factors,
+bias), since weight preparation is an offline step outside the timed call.
+
+Prints one JSON line:
+  value        effective TOPS = 2 M N K / (wall time per call), from W untimed and
+               K timed calls bracketed by device synchronizations
+  roofline     for the GEMM kernel: 2 M N K / its mean duration, from HIP events
+               recorded on the launch stream during the timed calls, against the
+               dense peak of the MFMA data type it issues (FP6, 10.1 PFLOP/s);
+               `traffic` is the HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE
+               counter runs recorded under profiles/, or null if the GEMM source has
+               changed since they were taken
+  cpu_baseline the CPU oracle on the same inputs (full call, repeated for about
+               10-30 s), on the host's cores
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 linear effective TOPS at M=4096,K=N=3072 (+% MFMA peak)"
+PEAK_FP6_TFLOPS = 10100.0   # MI355X dense FP6/FP4 MFMA
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (config id, M, K, N, rank)
+    "attn_proj": (2, 4096, 3072, 3072, 32),
+    "qkv": (3, 4608, 3072, 9216, 32),
+    "mlp_up": (3, 4608, 3072, 12288, 32),
+    "mlp_down": (3, 4608, 12288, 3072, 32),
+}
+
+GEMM_SOURCES = ["w4a4_rank_corrected_linear_amd/csrc/k2_gemm_int4.hip",
+                "w4a4_rank_corrected_linear_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k2_gemm_int4_attn_proj_traffic.txt")
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed counter summary, or None."""
+    if workload != "attn_proj" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(workload: str):
+    from synth import inputs as I
+    cid, M, K, N, rank = WORKLOADS[workload]
+    sd = I.seeds(cid)
+    idx = I.outlier_channels(K, I.default_outlier_count(K), sd.outliers)
+    x = I.activations(M, K, sd.x, idx, 30.0)
+    pb = I.prepared_int4_bytes(cid, K, N, rank)
+    return dict(M=M, K=K, N=N, rank=rank, x=x, pb=pb, seeds=dict(x=sd.x, w=sd.w + 500,
+                                                                 bias=sd.bias, outliers=sd.outliers))
+
+
+def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 8):
+    """The oracle on the same inputs, timed on the host (test infrastructure)."""
+    from oracle import linear as OL
+    from oracle import prep as P
+    pb = inp["pb"]
+    layer = P.SvdqLayer(precision="int4", K=pb.K, N=pb.N, rank=pb.rank, qweight=pb.qweight,
+                        wscales=pb.wscales, w_global=1.0, act_global=1.0, smooth=pb.smooth,
+                        lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < 2 or (time.perf_counter() - t_all < min_seconds and len(times) < max_reps):
+        t0 = time.perf_counter()
+        OL.w4a4_linear("int4", inp["x"], layer)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": round(2.0 * M * N * K / t / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"full {M}x{K}x{N} call on the same inputs, {len(times)} runs, median "
+                      f"{t:.3f} s (float64 numpy/BLAS)"}
+
+
+PROFILE_CMDS = {
+    "stats": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_stats "
+             "-o run --output-format csv -- python3 <repo>/bench.py --no-cpu-baseline",
+    "fetch": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_fetch -o run "
+             "--output-format csv -- python3 <repo>/bench.py --no-cpu-baseline --steps 20 "
+             "--warmup 5 --copy-probe",
+    "write": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_write -o run "
+             "--output-format csv -- python3 <repo>/bench.py --no-cpu-baseline --steps 20 "
+             "--warmup 5 --copy-probe",
+}
+
+
+def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
+    """Turn the CSV output of the three rocprofv3 runs in PROFILE_CMDS (under
+    out_dir) into the text summaries kept under profiles/ (host only, no GPU)."""
+    import csv
+    import glob
+
+    def one(pattern):
+        files = glob.glob(os.path.join(out_dir, pattern), recursive=True)
+        if not files:
+            raise FileNotFoundError(os.path.join(out_dir, pattern))
+        return files[0]
+
+    def short(name):
+        for key in ("k1_quant_int4", "k2_gemm_int4", "MulFunctor", "FillFunctor", "k_pack_int4",
+                    "k_transpose", "k_zero_flag", "copyBuffer"):
+            if key in name:
+                return key
+        return name[:40]
+
+    cid, M, K, N, rank = WORKLOADS[workload]
+    lines = [f"# rocprofv3 kernel statistics: bench.py, workload {workload} "
+             f"(M={M} K={K} N={N} rank {rank}, int4 g64), 500 timed + 50 warmup calls",
+             f"# command: {PROFILE_CMDS['stats']}",
+             "# kernel                      calls     avg_us     min_us     max_us   share_%"]
+    for r in csv.DictReader(open(one("prof_stats/**/*kernel_stats.csv"))):
+        lines.append(f"{short(r['Name']):28s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} "
+                     f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
+                     f"{float(r['Percentage']):8.2f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"svdq_w4a4_int4_{workload}_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    per = {}
+    for tag, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        acc = {}
+        for r in csv.DictReader(open(one(f"pmc_{tag}/**/*counter_collection.csv"))):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(short(r["Kernel_Name"]), {}).setdefault(r["Dispatch_Id"], 0.0)
+            acc[short(r["Kernel_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        per[tag] = {k: sum(v.values()) / len(v) for k, v in acc.items()}   # KiB per dispatch
+    copy_bytes = 256.0 * 1024 * 1024
+    f_fetch = per["fetch"]["MulFunctor"] * 1024 / copy_bytes
+    f_write = per["write"]["MulFunctor"] * 1024 / copy_bytes
+    k2_traffic = per["fetch"]["k2_gemm_int4"] * 1024 / f_fetch + per["write"]["k2_gemm_int4"] * 1024 / f_write
+    k1_traffic = per["fetch"]["k1_quant_int4"] * 1024 / f_fetch + per["write"]["k1_quant_int4"] * 1024 / f_write
+    t = [f"# HBM traffic per dispatch from rocprofv3 counters, workload {workload} "
+         f"(M={M} K={K} N={N} rank {rank}, int4 g64)",
+         f"# fetch command: {PROFILE_CMDS['fetch']}",
+         f"# write command: {PROFILE_CMDS['write']}",
+         "# scale: the copy probe (elementwise multiply, float32, 256 MiB read + 256 MiB write)",
+         "# reads FETCH_SIZE = copy_fetch_KiB and WRITE_SIZE = copy_write_KiB; bytes = counter KiB",
+         "# * 1024 / factor, factor = counter bytes of the probe / 256 MiB",
+         f"copy_fetch_KiB = {per['fetch']['MulFunctor']:.1f}",
+         f"copy_write_KiB = {per['write']['MulFunctor']:.1f}",
+         f"fetch_factor = {f_fetch:.4f}",
+         f"write_factor = {f_write:.4f}"]
+    for k in ("k1_quant_int4", "k2_gemm_int4"):
+        t.append(f"{k}_fetch_KiB = {per['fetch'][k]:.1f}")
+        t.append(f"{k}_write_KiB = {per['write'][k]:.1f}")
+    t += [f"k1_traffic_bytes_per_launch = {k1_traffic:.0f}",
+          f"traffic_bytes_per_launch = {k2_traffic:.0f}",
+          f"gemm_source_sha256_16 = {gemm_source_hash()}"]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(t) + "\n")
+    print("\n".join(lines + t))
+
+
+def main() -> int:
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2])
+        return 0
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (scale reference for HBM counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the layer shards by tokens with no exchange, run one process per GPU instead",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import w4a4_rank_corrected_linear_amd as svdq
+
+    if not torch.cuda.is_available():
+        print("no GPU visible: bench.py needs a gfx950 device", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    svdq.check_device(0)
+
+    inp = make_inputs(args.workload)
+    M, K, N, rank = inp["M"], inp["K"], inp["N"], inp["rank"]
+    pb = inp["pb"]
+
+    def bf16(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+        return t.view(torch.bfloat16).to(dev)
+
+    codes = torch.from_numpy(pb.qweight).to(dev)
+    layer = svdq.SvdqLinear.from_interchange(codes, bf16(pb.wscales), bf16(pb.smooth),
+                                             bf16(pb.lora_down), bf16(pb.lora_up), bf16(pb.bias))
+    x = bf16(inp["x"])
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = layer.workspace(M, dev)
+    print(f"[bench] workload {args.workload} M={M} K={K} N={N} rank={rank}; warmup {args.warmup}, "
+          f"steps {args.steps}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        layer(x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    svdq.timing_start(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer(x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    calls, kern_ms = svdq.timing_stop()
+    if calls != args.steps or len(kern_ms) != 2:
+        raise RuntimeError(f"kernel timing recorded {calls} calls / {len(kern_ms)} kernels")
+    print(f"[bench] timed {args.steps} calls in {wall:.4f} s", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        n = 64 << 20
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print("[bench] copy probe: 3 x elementwise 256 MiB read + 256 MiB write", file=sys.stderr,
+              flush=True)
+
+    ops = 2.0 * M * N * K
+    ms_per_step = wall * 1e3 / args.steps
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    k1_ms, k2_ms = kern_ms
+    achieved = ops / (k2_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(args.workload)
+    k1_bytes = M * K * 2 + M * K * 3 // 4 + (K // 64) * M * 2 + M * rank * 4
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: svdq_w4a4 int4 g64 rank {rank}, "
+                               f"M={M} K={K} N={N}",
+                   "M": M, "K": K, "N": N, "rank": rank, "precision": "int4", "group_size": 64,
+                   "compute_dtype": "bf16", "seeds": inp["seeds"]},
+        "pct_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
+        "kernels": {
+            "quantize_ms": round(k1_ms, 6),
+            "quantize_GBps_algorithmic": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
+            "gemm_ms": round(k2_ms, 6),
+            "gemm_TOPS": round(achieved, 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP6_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP6_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the same inputs", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

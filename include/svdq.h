@@ -9,7 +9,7 @@
  *   low-rank correction of rank r (32 in the config example), compute_dtype bf16:
  *
  *     xhat = bf16(x * smooth)                      per-input-channel smoothing
- *     U    = bf16(xhat @ lora_down^T)              rank-r down projection
+ *     U    = xhat @ lora_down^T (fp32 accumulation) rank-r down projection
  *     codes, scales = quantize(xhat)               4-bit, one scale per group
  *     Y    = bf16( sum_g s_x s_w (codes_x . codes_w)_g  [ * g_x g_w for nvfp4 ]
  *                  + U @ lora_up^T + bias )
@@ -122,12 +122,13 @@ size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);
  *   act_global NVFP4 static activation scale g_x (ignored for int4)
  *   codes      [M][K/2] out: int4 two's complement / E2M1 nibbles, 2j in bits 3:0
  *   scales     [M][K/G] out: bf16 (int4) or E4M3 bytes (nvfp4)
- *   lora_act   [M][r] out: U = bf16(xhat @ lora_down^T)  (NULL iff r == 0)
+ *   lora_act   [M][r] out: U = xhat @ lora_down^T, fp32 (NULL iff r == 0); U is
+ *              accumulated in fp32 and kept unrounded for the up projection
  * int4: s = bf16(amax/7) per 64-group, q = round-half-even(xhat/s) in [-7, 7].
  * nvfp4: s = E4M3(amax / (6 g_x)) per 16-block, code = E2M1(xhat / (s g_x)). */
 svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
                               const uint16_t* smooth, const uint16_t* lora_down, float act_global,
-                              uint8_t* codes, void* scales, uint16_t* lora_act, hipStream_t stream);
+                              uint8_t* codes, void* scales, float* lora_act, hipStream_t stream);
 
 /* The whole layer: Y[M][N] (bf16) = svdq_w4a4(X[M][K]).  `workspace` holds the
  * quantized activations between the two kernels (svdq_workspace_bytes). */
@@ -139,6 +140,20 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w,
  * {int4, 64, rank 0, bf16}. */
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
                              const uint16_t* x, int64_t M, uint16_t* y, hipStream_t stream);
+
+/* Per-kernel timing, for measurement tools.  After svdq_timing_start(max_calls) and
+ * until svdq_timing_stop, each svdq_w4a4_linear / awq_w4a16_linear call made on the
+ * calling thread launches its kernels with a pair of HIP events that receive each
+ * kernel's own start and end timestamps (hipExtLaunchKernelGGL; the first max_calls
+ * calls only, 1 <= max_calls <= 65536).  The events are created by
+ * svdq_timing_start and destroyed by svdq_timing_stop.  svdq_timing_stop waits for
+ * the recorded events and returns, through host pointers, the number of recorded
+ * calls, the number of kernels per call, and in mean_ms[i] (i < max_kernels) the
+ * mean duration of kernel i in milliseconds.  Every recorded call must have
+ * launched the same number of kernels, else SVDQ_ERR_CONFIG.  Calls made while
+ * timing is off launch with null events. */
+svdq_status svdq_timing_start(int max_calls);
+svdq_status svdq_timing_stop(int* calls, int* kernels, float* mean_ms, int max_kernels);
 
 /* Human-readable name of a status code (static string). */
 const char* svdq_status_str(svdq_status s);

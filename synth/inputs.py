@@ -141,3 +141,55 @@ MLP_UP = dict(config_id=3, M=4608, K=3072, N=12288, outlier_count=None, factor=3
 MLP_DOWN = dict(config_id=3, M=4608, K=12288, N=3072, outlier_count=None, factor=30.0)
 NVFP4_SQ = dict(config_id=4, M=4096, K=3072, N=3072, outlier_count=None, factor=30.0)
 NVFP4_UP = dict(config_id=4, M=4096, K=3072, N=12288, outlier_count=None, factor=30.0)
+
+
+def _nibble_bytes(rng: np.random.Generator, rows: int, half_k: int) -> np.ndarray:
+    """Bytes whose two 4-bit fields are drawn uniformly from the 15 two's complement
+    patterns of -7..7 (the pattern 0x8 of -8 is never drawn)."""
+    pats = np.array([0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15], dtype=np.uint8)
+    lo = pats[rng.integers(0, 15, size=(rows, half_k))]
+    hi = pats[rng.integers(0, 15, size=(rows, half_k))]
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+@dataclasses.dataclass
+class PreparedBytes:
+    """Seeded bytes in the layout of a prepared int4 svdq_w4a4 layer (stand-ins for
+    the output of the offline weight preparation, for timing the forward call).
+
+    qweight  uint8 [N, K/2]    codes uniform in -7..7
+    wscales  bf16  [N, K/64]   about 0.015 (log-normal spread)
+    smooth   bf16  [K]         0.4..0.6, outlier channels 0.08..0.12
+    lora_down bf16 [rank, K]   N(0, 0.05);  lora_up bf16 [N, rank]  N(0, 0.05)
+    bias     bf16  [N]         N(0, 0.02)
+    """
+
+    K: int
+    N: int
+    rank: int
+    qweight: np.ndarray
+    wscales: np.ndarray
+    smooth: np.ndarray
+    lora_down: np.ndarray
+    lora_up: np.ndarray
+    bias: np.ndarray
+
+
+def prepared_int4_bytes(config_id: int, K: int, N: int, rank: int = 32,
+                        outlier_count: int | None = None) -> PreparedBytes:
+    sd = seeds(config_id)
+    rng = np.random.default_rng(sd.w + 500)
+    n_out = default_outlier_count(K) if outlier_count is None else outlier_count
+    idx = outlier_channels(K, n_out, sd.outliers)
+    smooth = rng.uniform(0.4, 0.6, K).astype(np.float32)
+    smooth[idx] = rng.uniform(0.08, 0.12, len(idx)).astype(np.float32)
+    wscales = (0.015 * np.exp(0.1 * rng.standard_normal((N, K // 64)))).astype(np.float32)
+    return PreparedBytes(
+        K=K, N=N, rank=rank,
+        qweight=_nibble_bytes(rng, N, K // 2),
+        wscales=to_bf16_bits(wscales),
+        smooth=to_bf16_bits(smooth),
+        lora_down=to_bf16_bits(rng.standard_normal((rank, K), dtype=np.float32) * np.float32(0.05)),
+        lora_up=to_bf16_bits(rng.standard_normal((N, rank), dtype=np.float32) * np.float32(0.05)),
+        bias=bias(N, sd.bias),
+    )

@@ -53,6 +53,21 @@ def check_y(y_bits: np.ndarray, r: np.ndarray, max_ulp: int = 2, max_rel: float 
     return stats
 
 
+def check_u(u: np.ndarray, ref: dict, lora_down_bits: np.ndarray, chain: int | None = None):
+    """The low-rank down projection: fp32 device result u [M, r] against the oracle's
+    float64 U, within the rounding bound of an fp32 accumulation whose chain of
+    roundings is at most `chain` deep: |u - U| <= chain 2^-24 sum_k |xhat_k L1[k, j]|.
+    The kernel splits K over 8 waves, each summing at most K/8 products in one chain,
+    then adds the 8 partial sums: chain = K/8 + 16 covers fully sequential rounding."""
+    if chain is None:
+        chain = ref["xhat"].shape[1] // 8 + 16
+    xh = np.abs(F.bf16_to_f64(ref["xhat"]))
+    ld = np.abs(F.bf16_to_f64(lora_down_bits))
+    bound = chain * 2.0 ** -24 * (xh @ ld.T)
+    err = np.abs(np.asarray(u, dtype=np.float64) - ref["lora_act"])
+    assert np.all(err <= bound), float((err / np.maximum(bound, 1e-300)).max())
+
+
 def decode_compact_int4(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
     """Kernel-layout int4 codes (compact E2M3 runs) -> signed codes [rows_pad, K].
 

@@ -93,7 +93,7 @@ def test_workspace_size_and_check():
     lib = L.lib()
     need = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 100, 512)
     # M padded to 128 rows: operand 128*512*3/4, scales 8*128*2, U 128*32*2 (256-aligned)
-    assert need == 49152 + 2048 + 8192
+    assert need == 49152 + 2048 + 16384
     assert linear(cfg(), weight(), M=100, ws_bytes=need - 1) == L.ERR_WORKSPACE
     assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 49152 + 2048
 
@@ -123,3 +123,19 @@ def test_python_layer_rejects_host_tensors():
     x = torch.zeros(4, 512, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         svdq.quantize_act(x, torch.zeros(512, dtype=torch.bfloat16))
+
+
+def test_timing_hook_arguments():
+    lib = L.lib()
+    calls, kern = ctypes.c_int(-1), ctypes.c_int(-1)
+    buf = (ctypes.c_float * 4)()
+    assert lib.svdq_timing_start(0) == L.ERR_SHAPE
+    assert lib.svdq_timing_start(65537) == L.ERR_SHAPE
+    assert lib.svdq_timing_stop(None, ctypes.byref(kern), buf, 4) == L.ERR_NULL
+    assert lib.svdq_timing_stop(ctypes.byref(calls), ctypes.byref(kern), buf, 4) == L.ERR_CONFIG
+    assert calls.value == 0 and kern.value == 0
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="a device is present")
+def test_timing_start_without_device_is_a_clear_error():
+    assert L.lib().svdq_timing_start(8) == L.ERR_DEVICE

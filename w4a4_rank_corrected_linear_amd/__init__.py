@@ -17,5 +17,7 @@ from .api import (  # noqa: F401
     check_device,
     pack_weight,
     quantize_act,
+    timing_start,
+    timing_stop,
     workspace_bytes,
 )

@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
     L.svdq_w4a4_linear.restype = st
     L.awq_w4a16_linear.argtypes = [cfgp, ctypes.POINTER(AwqW4A16Weight), vp, i64, vp, vp]
     L.awq_w4a16_linear.restype = st
+    L.svdq_timing_start.argtypes = [ctypes.c_int]
+    L.svdq_timing_start.restype = st
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.svdq_timing_stop.argtypes = [ip, ip, ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+    L.svdq_timing_stop.restype = st
     L.svdq_status_str.argtypes = [st]
     L.svdq_status_str.restype = ctypes.c_char_p
     L.svdq_last_error.argtypes = []

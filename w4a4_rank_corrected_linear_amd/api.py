@@ -48,7 +48,7 @@ def _scale_dtype(precision: str):
 
 def quantize_act(x: torch.Tensor, smooth: torch.Tensor, lora_down: torch.Tensor | None = None,
                  precision: str = "int4", act_global: float = 1.0):
-    """svdq_quantize_act: returns (codes [M, K/2] u8, scales [M, K/G], lora_act [M, r] bf16)."""
+    """svdq_quantize_act: returns (codes [M, K/2] u8, scales [M, K/G], lora_act [M, r] fp32)."""
     _want(x, torch.bfloat16, "x")
     M, K = x.shape
     _want(smooth, torch.bfloat16, "smooth", (K,))
@@ -59,7 +59,7 @@ def quantize_act(x: torch.Tensor, smooth: torch.Tensor, lora_down: torch.Tensor 
     G = K // cfg.group_size
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((M, G), dtype=_scale_dtype(precision), device=x.device)
-    lora_act = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device) if rank else None
+    lora_act = torch.empty((M, rank), dtype=torch.float32, device=x.device) if rank else None
     st = L.lib().svdq_quantize_act(ctypes.byref(cfg), _p(x), M, K, _p(smooth), _p(lora_down),
                                    float(act_global), _p(codes), _p(scales), _p(lora_act), _stream())
     L.check(st, "svdq_quantize_act")
@@ -167,3 +167,18 @@ def awq_w4a16_linear(x: torch.Tensor, layer: AwqLinear, out: torch.Tensor | None
                                   _stream())
     L.check(st, "awq_w4a16_linear")
     return y
+
+
+def timing_start(max_calls: int) -> None:
+    """svdq_timing_start: record per-kernel HIP events in the next `max_calls` layer
+    calls made on this thread."""
+    L.check(L.lib().svdq_timing_start(int(max_calls)), "svdq_timing_start")
+
+
+def timing_stop(max_kernels: int = 4):
+    """svdq_timing_stop: returns (calls, [mean ms of kernel i])."""
+    calls, kernels = ctypes.c_int(0), ctypes.c_int(0)
+    buf = (ctypes.c_float * max_kernels)()
+    L.check(L.lib().svdq_timing_stop(ctypes.byref(calls), ctypes.byref(kernels), buf, max_kernels),
+            "svdq_timing_stop")
+    return calls.value, [float(buf[i]) for i in range(min(kernels.value, max_kernels))]

@@ -4,7 +4,7 @@
 // Layer definition: Diffusers docs "Nunchaku Lite", "Supported quantization types"
 // (svdq_w4a4, int4, group 64, SVDQ low-rank correction), with the readings stated
 // in svdq.h: xhat = bf16(x m), s = bf16(amax / 7), q = round-half-even(xhat / s)
-// clamped to [-7, 7], U = bf16(xhat @ lora_down^T).
+// clamped to [-7, 7], U = xhat @ lora_down^T (fp32 accumulation, not rounded).
 //
 // Work split: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide k-blocks
 // kb = w, w+8, ...  Lane l holds row l%16 and the 32 consecutive values
@@ -27,6 +27,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 struct K1Load {
   uint4 x[4];
   uint4 m[4];
+  uint4 l[2][4];  // lora_down B operands for the rank slices (0..15, 16..31)
 };
 
 template <int MODE>  // 0: interchange layout, 1: fused (GEMM operand) layout
@@ -34,7 +35,7 @@ __global__ void __launch_bounds__(512)
 k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
               const uint16_t* __restrict__ smooth, const uint16_t* __restrict__ ldown, int rank,
               uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-              uint16_t* __restrict__ uact, int M_out, int M_pad) {
+              float* __restrict__ uact, int M_out, int M_pad) {
   __shared__ float ured[8][16][33];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -57,6 +58,16 @@ k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
     for (int c = 0; c < 4; ++c) {
       L.x[c] = valid ? xp[c] : make_uint4(0, 0, 0, 0);
       L.m[c] = mp[c];
+    }
+    if (rank > 0) {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        if (sl * 16 < rank) {
+          const uint4* lp = reinterpret_cast<const uint4*>(ldown + (size_t)(16 * sl + r) * K + k0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) L.l[sl][c] = lp[c];
+        }
+      }
     }
   };
 
@@ -159,13 +170,11 @@ k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
       for (int c = 0; c < 4; ++c) {
         const v4i a4 = {(int)xb[4 * c], (int)xb[4 * c + 1], (int)xb[4 * c + 2], (int)xb[4 * c + 3]};
         const v8bf a = __builtin_bit_cast(v8bf, a4);
-        const int kk = 128 * kb + 32 * q + 8 * c;
-        const uint4 b0 = *reinterpret_cast<const uint4*>(ldown + (size_t)r * K + kk);
-        u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, b0), u0, 0, 0, 0);
-        if (rank > 16) {
-          const uint4 b1 = *reinterpret_cast<const uint4*>(ldown + (size_t)(16 + r) * K + kk);
-          u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, b1), u1, 0, 0, 0);
-        }
+        u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, cur.l[0][c]), u0, 0,
+                                                     0, 0);
+        if (rank > 16)
+          u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, cur.l[1][c]), u1,
+                                                       0, 0, 0);
       }
     }
     cur = nxt;
@@ -184,25 +193,26 @@ k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
       float v = ured[0][rr][cc];
 #pragma unroll
       for (int w = 1; w < 8; ++w) v += ured[w][rr][cc];
-      if (row0 + rr < M_out) uact[(size_t)(row0 + rr) * rank + cc] = (uint16_t)f32_to_bf16_rne(v);
+      if (row0 + rr < M_out) uact[(size_t)(row0 + rr) * rank + cc] = v;
     }
   }
 }
 
-// fused = false: interchange layout (codes [M][K/2], scales [M][K/64], U [M][r]).
+// fused = false: interchange layout (codes [M][K/2], scales [M][K/64], U [M][r] fp32).
 // fused = true : GEMM layout, M_pad rows (operand chunks of 1536 B per 32-row block
-//                and group, scales [K/64][M_pad], U [M_pad][r]); rows >= M are zero.
+//                and group, scales [K/64][M_pad], U [M_pad][r] fp32); rows >= M are zero.
 hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, uint16_t* scales,
-                          uint16_t* uact, int M_pad, hipStream_t st) {
+                          float* uact, int M_pad, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   const int M_out = fused ? M_pad : M;
   dim3 grid((M_out + 15) / 16);
   if (fused)
-    hipLaunchKernelGGL(k1_quant_int4<1>, grid, dim3(512), 0, st, x, M, K, smooth, ldown, rank,
-                       codes, scales, uact, M_out, M_pad);
+    hipExtLaunchKernelGGL(k1_quant_int4<1>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
+                          ldown, rank, codes, scales, uact, M_out, M_pad);
   else
-    hipLaunchKernelGGL(k1_quant_int4<0>, grid, dim3(512), 0, st, x, M, K, smooth, ldown, rank,
-                       codes, scales, uact, M_out, M_pad);
+    hipExtLaunchKernelGGL(k1_quant_int4<0>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
+                          ldown, rank, codes, scales, uact, M_out, M_pad);
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 template <int BN>
 __global__ void __launch_bounds__(256, 2)
 k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
-             const uint16_t* __restrict__ U, const uint8_t* __restrict__ B,
+             const float* __restrict__ U, const uint8_t* __restrict__ B,
              const uint16_t* __restrict__ sB, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
              int M, int N, int K, int M_pad, int rank) {
@@ -223,10 +223,21 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
       const int colb = col0 + (wn * WN + j) * 32;
       v16f c = acc[i][j];
       for (int kk = 0; kk < rank; kk += 16) {
-        const uint4 ua = *reinterpret_cast<const uint4*>(U + (size_t)(rowb + lr) * rank + kk + 8 * lh);
+        // U is fp32: split into bf16 hi + lo (u - hi is exact in fp32), two MFMAs;
+        // what is dropped is below 2^-17 |u|.
+        const float* up = U + (size_t)(rowb + lr) * rank + kk + 8 * lh;
+        const float4 u0 = *reinterpret_cast<const float4*>(up);
+        const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
+        const float uf[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        v8bf hi, lo;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          hi[t] = (__bf16)uf[t];
+          lo[t] = (__bf16)(uf[t] - (float)hi[t]);
+        }
         const uint4 lb = *reinterpret_cast<const uint4*>(L2t + (size_t)(colb + lr) * rank + kk + 8 * lh);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua),
-                                                    __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
       }
       const float bv = bias ? bf16_to_f32(bias[colb + lr]) : 0.f;
 #pragma unroll
@@ -246,19 +257,19 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   }
 }
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const uint16_t* U,
+hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U,
                           const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, hipStream_t st) {
+                          int rank, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const int BM = 128;
   if (N % 192 == 0) {
     dim3 grid(N / 192, M_pad / BM);
-    hipLaunchKernelGGL(k2_gemm_int4<192>, grid, dim3(256), 0, st, A, sA, U, B, sB, L2t, bias, Y, M,
-                       N, K, M_pad, rank);
+    hipExtLaunchKernelGGL(k2_gemm_int4<192>, grid, dim3(256), 0, st, ev0, ev1, 0, A, sA, U, B, sB,
+                          L2t, bias, Y, M, N, K, M_pad, rank);
   } else {
     dim3 grid(N / 128, M_pad / BM);
-    hipLaunchKernelGGL(k2_gemm_int4<128>, grid, dim3(256), 0, st, A, sA, U, B, sB, L2t, bias, Y, M,
-                       N, K, M_pad, rank);
+    hipExtLaunchKernelGGL(k2_gemm_int4<128>, grid, dim3(256), 0, st, ev0, ev1, 0, A, sA, U, B, sB,
+                          L2t, bias, Y, M, N, K, M_pad, rank);
   }
   return hipGetLastError();
 }

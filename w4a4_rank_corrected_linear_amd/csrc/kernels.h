@@ -1,20 +1,25 @@
 // Kernel launchers (host functions defined next to their kernels).  Every launcher
 // enqueues on `st` and returns hipGetLastError() of its launches.  Shapes were
-// validated by the C ABI before any of these is called.
+// validated by the C ABI before any of these is called.  `ev0` / `ev1` (may be
+// null) are HIP events that receive the kernel's start and end timestamps
+// (hipExtLaunchKernelGGL), used by the per-kernel timing hook.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace svdq {
 
 hipError_t launch_k1_int4(bool compact, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, uint16_t* scales,
-                          uint16_t* uact, int M_pad, hipStream_t st);
+                          float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr);
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const uint16_t* U,
+hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U,
                           const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, hipStream_t st);
+                          int rank, hipStream_t st, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr);
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
                             uint16_t* out_scales, int* flag, int N, int K, hipStream_t st);

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "svdq.h"
 #include "kernels.h"
@@ -117,7 +118,7 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   // int4: GEMM A operand as E2M3 fields, 6 bits per value (3/4 byte)
   const size_t codes = (size_t)(L.M_pad * K * 3 / 4);
   const size_t scales = (size_t)(G * L.M_pad * 2);
-  const size_t lora = (size_t)(L.M_pad * c->rank * 2);
+  const size_t lora = (size_t)(L.M_pad * c->rank * 4);  // fp32 U
   L.codes = 0;
   L.scales = (size_t)round_up((int64_t)codes, 256);
   L.lora = L.scales + (size_t)round_up((int64_t)scales, 256);
@@ -135,6 +136,49 @@ svdq_status hip_check(hipError_t e, const char* what) {
     const svdq_status _s = (expr);        \
     if (_s != SVDQ_OK) return _s;         \
   } while (0)
+
+// Per-kernel timing of the calling thread (svdq_timing_start / svdq_timing_stop):
+// each timed kernel gets a (start, end) event pair that hipExtLaunchKernelGGL fills
+// with the kernel's own begin and end timestamps.
+struct KernelTimer {
+  bool on = false;
+  std::vector<hipEvent_t> pool;           // created by svdq_timing_start
+  size_t used = 0;
+  std::vector<std::vector<int>> calls;    // per recorded call: event pairs (2i, 2i+1)
+  int max_calls = 0;
+  bool recording = false;                 // inside a call that is being recorded
+};
+thread_local KernelTimer g_timer;
+
+void timer_begin_call() {
+  KernelTimer& t = g_timer;
+  t.recording = t.on && (int)t.calls.size() < t.max_calls;
+  if (t.recording) t.calls.emplace_back();
+}
+
+struct EvPair {
+  hipEvent_t start = nullptr, end = nullptr;
+};
+
+// Event pair for the next kernel of the current call (null events when not timing).
+EvPair timer_kernel() {
+  KernelTimer& t = g_timer;
+  if (!t.recording) return {};
+  if (t.used + 2 > t.pool.size()) {
+    t.recording = false;
+    t.calls.pop_back();
+    return {};
+  }
+  const int idx = (int)t.used;
+  t.used += 2;
+  t.calls.back().push_back(idx);
+  return {t.pool[idx], t.pool[idx + 1]};
+}
+
+void timer_release() {
+  for (hipEvent_t e : g_timer.pool) (void)hipEventDestroy(e);
+  g_timer = KernelTimer();
+}
 
 }  // namespace
 
@@ -195,7 +239,7 @@ size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K) {
 
 svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
                               const uint16_t* smooth, const uint16_t* lora_down, float act_global,
-                              uint8_t* codes, void* scales, uint16_t* lora_act, hipStream_t stream) {
+                              uint8_t* codes, void* scales, float* lora_act, hipStream_t stream) {
   (void)act_global;
   if (!cfg || !x || !smooth || !codes || !scales)
     return fail(SVDQ_ERR_NULL, "svdq_quantize_act: NULL argument");
@@ -244,16 +288,19 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* a_codes = ws + L.codes;
   uint16_t* a_scales = reinterpret_cast<uint16_t*>(ws + L.scales);
-  uint16_t* a_lora = reinterpret_cast<uint16_t*>(ws + L.lora);
+  float* a_lora = reinterpret_cast<float*>(ws + L.lora);
+  timer_begin_call();
+  const EvPair e1 = timer_kernel();
   SVDQ_TRY(hip_check(svdq::launch_k1_int4(true, x, (int)M, (int)w->K, w->smooth,
                                            cfg->rank ? w->lora_down : nullptr, cfg->rank, a_codes,
                                            a_scales, cfg->rank ? a_lora : nullptr, (int)L.M_pad,
-                                           stream),
+                                           stream, e1.start, e1.end),
                      "quantize kernel launch"));
+  const EvPair e2 = timer_kernel();
   SVDQ_TRY(hip_check(svdq::launch_k2_int4(a_codes, a_scales, a_lora, w->qweight,
                                            static_cast<const uint16_t*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
-                                           cfg->rank, stream),
+                                           cfg->rank, stream, e2.start, e2.end),
                      "gemm kernel launch"));
   return ok();
 }
@@ -270,6 +317,66 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, 
   SVDQ_TRY(check_n(w->N));
   SVDQ_TRY(check_m(M, w->K));
   return fail(SVDQ_ERR_CONFIG, "awq_w4a16 is not available in this build");
+}
+
+svdq_status svdq_timing_start(int max_calls) {
+  if (max_calls < 1 || max_calls > 65536)
+    return fail(SVDQ_ERR_SHAPE, "svdq_timing_start: max_calls = %d out of [1, 65536]", max_calls);
+  timer_release();
+  SVDQ_TRY(check_current_device());
+  KernelTimer& t = g_timer;
+  const size_t n = (size_t)max_calls * 6;  // room for up to three kernels per call
+  t.pool.reserve(n);
+  for (size_t i = 0; i < n; ++i) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      timer_release();
+      return fail(SVDQ_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+    t.pool.push_back(e);
+  }
+  t.max_calls = max_calls;
+  t.on = true;
+  return ok();
+}
+
+svdq_status svdq_timing_stop(int* calls, int* kernels, float* mean_ms, int max_kernels) {
+  if (!calls || !kernels || (max_kernels > 0 && !mean_ms))
+    return fail(SVDQ_ERR_NULL, "svdq_timing_stop: NULL argument");
+  KernelTimer& t = g_timer;
+  *calls = 0;
+  *kernels = 0;
+  if (!t.on) return fail(SVDQ_ERR_CONFIG, "svdq_timing_stop: timing was not started");
+  const int nc = (int)t.calls.size();
+  const int nk = nc ? (int)t.calls[0].size() : 0;
+  for (const auto& c : t.calls)
+    if ((int)c.size() != nk) {
+      timer_release();
+      return fail(SVDQ_ERR_CONFIG, "svdq_timing_stop: calls launched different kernel counts");
+    }
+  std::vector<double> sum(nk > 0 ? nk : 0, 0.0);
+  for (const auto& c : t.calls) {
+    const hipError_t e = nk ? hipEventSynchronize(t.pool[c.back() + 1]) : hipSuccess;
+    if (e != hipSuccess) {
+      timer_release();
+      return fail(SVDQ_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    }
+    for (int i = 0; i < nk; ++i) {
+      float ms = 0.f;
+      const hipError_t e2 = hipEventElapsedTime(&ms, t.pool[c[i]], t.pool[c[i] + 1]);
+      if (e2 != hipSuccess) {
+        timer_release();
+        return fail(SVDQ_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e2));
+      }
+      sum[i] += ms;
+    }
+  }
+  for (int i = 0; i < nk && i < max_kernels; ++i) mean_ms[i] = (float)(sum[i] / nc);
+  *calls = nc;
+  *kernels = nk;
+  timer_release();
+  return ok();
 }
 
 const char* svdq_status_str(svdq_status s) {
