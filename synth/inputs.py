@@ -193,3 +193,25 @@ def prepared_int4_bytes(config_id: int, K: int, N: int, rank: int = 32,
         lora_up=to_bf16_bits(rng.standard_normal((N, rank), dtype=np.float32) * np.float32(0.05)),
         bias=bias(N, sd.bias),
     )
+
+
+@dataclasses.dataclass
+class PreparedNvfp4Bytes(PreparedBytes):
+    """Seeded bytes in the layout of a prepared nvfp4 svdq_w4a4 layer: E2M1 codes
+    uniform over all 16 patterns, E4M3 scale codes between 0.5 and 4 (codes 0x30..0x48),
+    per-tensor scales w_global (weights) and act_global (activations)."""
+
+    w_global: float = 1.0
+    act_global: float = 1.0
+
+
+def prepared_nvfp4_bytes(config_id: int, K: int, N: int, rank: int = 32,
+                         outlier_count: int | None = None) -> PreparedNvfp4Bytes:
+    base = prepared_int4_bytes(config_id, K, N, rank, outlier_count)
+    rng = np.random.default_rng(seeds(config_id).w + 700)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint16).astype(np.uint8)
+    scales = rng.integers(0x30, 0x49, size=(N, K // 16), dtype=np.uint16).astype(np.uint8)
+    return PreparedNvfp4Bytes(
+        K=K, N=N, rank=rank, qweight=codes, wscales=scales, smooth=base.smooth,
+        lora_down=base.lora_down, lora_up=base.lora_up, bias=base.bias,
+        w_global=float(np.float32(0.02 / 6.0)), act_global=float(np.float32(1.0 / 168.0)))

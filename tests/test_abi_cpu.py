@@ -139,3 +139,20 @@ def test_timing_hook_arguments():
 @pytest.mark.skipif(HAVE_GPU, reason="a device is present")
 def test_timing_start_without_device_is_a_clear_error():
     assert L.lib().svdq_timing_start(8) == L.ERR_DEVICE
+
+
+def test_nvfp4_sizes_and_global_scale_check():
+    lib = L.lib()
+    c = cfg(precision=L.NVFP4, group=16)
+    # bf16 operand 128 x 512 x 2, no scales, U 128 x 32 x 4
+    assert lib.svdq_workspace_bytes(ctypes.byref(c), 100, 512) == 131072 + 16384
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    tot = lib.svdq_packed_weight_bytes(ctypes.byref(c), 512, 256, ctypes.byref(cb), ctypes.byref(sb))
+    assert (cb.value, sb.value, tot) == (256 * 512 * 2, 256, 256 * 512 * 2 + 256)
+    w = weight()
+    for gx, gw in [(0.0, 1.0), (1.0, 0.0), (float("nan"), 1.0), (1.0, float("inf")), (-1.0, 1.0)]:
+        w.w_global = gw
+        st = lib.svdq_w4a4_linear(ctypes.byref(c), ctypes.byref(w), FAKE, 16, gx, FAKE, FAKE, 1 << 30, None)
+        assert st == L.ERR_RANGE, (gx, gw)
+    assert lib.svdq_quantize_act(ctypes.byref(c), FAKE, 4, 512, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE,
+                                 None) == L.ERR_RANGE

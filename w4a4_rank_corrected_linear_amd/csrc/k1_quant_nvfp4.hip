@@ -1,0 +1,231 @@
+// K1, nvfp4: smoothing + per-16-block amax + E4M3 block scale + E2M1 codes + rank-r
+// low-rank down projection, one pass over X.
+//
+// Layer definition: Diffusers docs "Nunchaku Lite", "Supported quantization types"
+// (svdq_w4a4, nvfp4, group 16, SVDQ low-rank correction).  Readings, as stated in
+// svdq.h: xhat = bf16(x m); per block of 16, s = E4M3(fl32(amax / fl32(6 g))) (round
+// to nearest even, saturating at 448); code = E2M1(fl32(xhat / fl32(s g))) (nearest,
+// ties to the even code, saturating at 6), sign from the quotient's sign bit; s = 0
+// gives zero codes; U = xhat @ lora_down^T in fp32.
+//
+// Work split as in the int4 quantizer: a 512-thread workgroup owns 16 rows; wave w
+// takes the 128-wide k-blocks kb = w, w+8, ...; lane l holds row l%16 and the 32
+// consecutive values k = 128 kb + 32 q + [0, 32), q = l/16, i.e. two whole NVFP4
+// blocks, so every amax is an in-lane max.
+//
+// Outputs: interchange layout (codes [M][K/2] with element 2j in bits 3:0, E4M3
+// scale bytes [M][K/16]), or, for the GEMM, the exact dequantized operand
+// A' = e2m1(code) * s as bf16 [M_pad][K] (|e2m1| has 2 and s 4 significant bits, so
+// the product is exact in bf16); the per-tensor scale g stays out of A' and is
+// applied to the GEMM's fp32 result.
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// E4M3 (FN) code of a non-negative float32, round to nearest even, saturating at 448
+// (code 0x7E).  Normal range: round the fp32 significand to 3 bits; below 2^-6 the
+// grid step is 2^-9, so the code is rne(v * 2^9) (8 lands on the smallest normal,
+// code 0x08).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;  // also +inf
+  if (v < 0x1p-6f) return (uint32_t)__builtin_rintf(v * 512.0f);
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t e = (u >> 23) - 127u + 7u;
+  const uint32_t code = (e << 3) | ((u >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Value of an E4M3 code (0..0x7E, non-negative).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude code of |v|: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the
+// even code, saturating at 6.  Each comparison adds one where v passes a midpoint;
+// the midpoints next to an even code are exclusive, the others inclusive.
+__device__ __forceinline__ uint32_t e2m1_mag(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t mag) {
+  // 0, .5, 1, 1.5, 2, 3, 4, 6
+  return mag < 4 ? 0.5f * (float)mag : (float)(2u << ((mag - 4u) >> 1)) * (1.0f + 0.5f * (float)(mag & 1u));
+}
+
+struct K1Load {
+  uint4 x[4];
+  uint4 m[4];
+  uint4 l[2][4];
+};
+
+template <int MODE>  // 0: interchange layout, 1: bf16 GEMM operand
+__global__ void __launch_bounds__(512)
+k1_quant_nvfp4(const uint16_t* __restrict__ x, int M, int K, const uint16_t* __restrict__ smooth,
+               const uint16_t* __restrict__ ldown, int rank, float g, uint8_t* __restrict__ out,
+               uint8_t* __restrict__ scales, float* __restrict__ uact, int M_out) {
+  __shared__ float ured[8][16][33];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int row = row0 + r;
+  const bool valid = row < M;
+  const int nkb = K >> 7;
+  const float denom = 6.0f * g;  // fl32(6 g)
+
+  v4f u0 = {0.f, 0.f, 0.f, 0.f};
+  v4f u1 = {0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](int kb, K1Load& L) {
+    const int k0 = 128 * kb + 32 * q;
+    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)row * K + k0);
+    const uint4* mp = reinterpret_cast<const uint4*>(smooth + k0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      L.x[c] = valid ? xp[c] : make_uint4(0, 0, 0, 0);
+      L.m[c] = mp[c];
+    }
+    if (rank > 0) {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        if (sl * 16 < rank) {
+          const uint4* lp = reinterpret_cast<const uint4*>(ldown + (size_t)(16 * sl + r) * K + k0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) L.l[sl][c] = lp[c];
+        }
+      }
+    }
+  };
+
+  K1Load cur, nxt;
+  int kb = wave;
+  if (kb < nkb) load(kb, cur);
+  for (; kb < nkb; kb += 8) {
+    if (kb + 8 < nkb) load(kb + 8, nxt);
+    const int k0 = 128 * kb + 32 * q;
+
+    float xh[32];
+    uint32_t xb[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t* xw = reinterpret_cast<const uint32_t*>(&cur.x[c]);
+      const uint32_t* mw = reinterpret_cast<const uint32_t*>(&cur.m[c]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float p0 = __uint_as_float(xw[p] << 16) * __uint_as_float(mw[p] << 16);
+        const float p1 = __uint_as_float(xw[p] & 0xFFFF0000u) * __uint_as_float(mw[p] & 0xFFFF0000u);
+        const v2bf pk = {(__bf16)p0, (__bf16)p1};
+        const uint32_t w = __builtin_bit_cast(uint32_t, pk);
+        xb[4 * c + p] = w;
+        xh[8 * c + 2 * p] = __uint_as_float(w << 16);
+        xh[8 * c + 2 * p + 1] = __uint_as_float(w & 0xFFFF0000u);
+      }
+    }
+
+    uint32_t codes[32];
+    float deq[32];
+    uint32_t sc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[16 * b + i]));
+      const uint32_t scode = e4m3_code(amax / denom);
+      sc[b] = scode;
+      const float s = e4m3_value(scode);
+      const float d = s * g;  // fl32(s g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float quot = xh[16 * b + i] / d;  // correctly rounded
+        const uint32_t mag = e2m1_mag(fabsf(quot));
+        const uint32_t sign = __float_as_uint(quot) >> 31;
+        const uint32_t c = s > 0.f ? (mag | (sign << 3)) : 0u;
+        codes[16 * b + i] = c;
+        const float v = e2m1_value(c & 7u) * s;  // exact
+        deq[16 * b + i] = (c & 8u) ? -v : v;
+      }
+    }
+
+    if constexpr (MODE == 1) {
+      if (row < M_out) {
+        uint32_t w[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          w[i] = (__float_as_uint(deq[2 * i]) >> 16) | (__float_as_uint(deq[2 * i + 1]) & 0xFFFF0000u);
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (size_t)row * K + k0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+      }
+    } else {
+      if (valid) {
+        uint32_t w[4];
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int i = 7; i >= 0; --i) acc = (acc << 4) | codes[8 * d4 + i];
+          w[d4] = acc;
+        }
+        *reinterpret_cast<uint4*>(out + ((size_t)row * K + k0) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint16_t*>(scales + (size_t)row * (K / 16) + k0 / 16) =
+            (uint16_t)(sc[0] | (sc[1] << 8));
+      }
+    }
+
+    if (rank > 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const v4i a4 = {(int)xb[4 * c], (int)xb[4 * c + 1], (int)xb[4 * c + 2], (int)xb[4 * c + 3]};
+        const v8bf a = __builtin_bit_cast(v8bf, a4);
+        u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, cur.l[0][c]), u0, 0,
+                                                     0, 0);
+        if (rank > 16)
+          u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, cur.l[1][c]), u1,
+                                                       0, 0, 0);
+      }
+    }
+    cur = nxt;
+  }
+
+  if (rank > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ured[wave][4 * q + i][r] = u0[i];
+      ured[wave][4 * q + i][16 + r] = u1[i];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < 16 * rank; t += 512) {
+      const int rr = t / rank, cc = t % rank;
+      float v = ured[0][rr][cc];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) v += ured[w][rr][cc];
+      if (row0 + rr < M_out) uact[(size_t)(row0 + rr) * rank + cc] = v;
+    }
+  }
+}
+
+// fused = false: codes [M][K/2], scales [M][K/16] (E4M3 bytes), U [M][r] fp32.
+// fused = true : A' bf16 [M_pad][K] (rows >= M are zero), U [M_pad][r] fp32.
+hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
+                           const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
+                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const int M_out = fused ? M_pad : M;
+  dim3 grid((M_out + 15) / 16);
+  if (fused)
+    hipExtLaunchKernelGGL(k1_quant_nvfp4<1>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
+                          ldown, rank, g, out, scales, uact, M_out);
+  else
+    hipExtLaunchKernelGGL(k1_quant_nvfp4<0>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
+                          ldown, rank, g, out, scales, uact, M_out);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

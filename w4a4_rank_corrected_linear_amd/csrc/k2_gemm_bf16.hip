@@ -1,0 +1,163 @@
+// K2, nvfp4: the 4-bit x 4-bit GEMM of the NVFP4 layer on exactly dequantized bf16
+// operands, fused with the per-tensor scale, the rank-r up projection, the bias and
+// the bf16 store.
+//
+//   Y[m,n] = bf16( g * sum_k A'[m,k] B'[n,k] + sum_j U[m,j] L2t[n,j] + b[n] ),
+//   A' = e2m1(x code) * s_x,  B' = e2m1(w code) * s_w   (exact in bf16), g = g_x g_w
+//
+// (Diffusers docs "Nunchaku Lite", "Supported quantization types": svdq_w4a4 nvfp4,
+// group 16 with E4M3 block scales, SVDQ low-rank correction.)  CDNA4's scaled MFMAs
+// take power-of-two scales per 32 values, not E4M3 scales per 16, so the block
+// scales are folded into the operands instead: every product A' B' is exact and the
+// sum over k accumulates in the fp32 MFMA accumulator, with no per-block rescale.
+//
+// Tiling: 256 threads (2 x 2 waves), tile 128 x 128, wave tile 64 x 64 (2 x 2 blocks
+// of v_mfma_f32_32x32x16_bf16), two workgroups per CU.  A stage is 64 values of k:
+// both 128 x 64 operand tiles (16 KiB each) are copied into LDS by global_load_lds
+// (16 B per lane) into one of two buffers while the other is consumed.  LDS holds a
+// tile as 16-byte units u = row * 8 + (c ^ (row & 7)), c = k / 8 within the stage: the
+// XOR swizzle puts the eight rows that one MFMA operand read touches at once in
+// distinct bank groups; it is applied by choosing each lane's source address.
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+__global__ void __launch_bounds__(256, 2)
+k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U,
+             const uint16_t* __restrict__ B, const uint16_t* __restrict__ L2t,
+             const uint16_t* __restrict__ bias, float g, uint16_t* __restrict__ Y, int M, int N,
+             int K, int M_pad, int rank) {
+  constexpr int BM = 128, BN = 128;
+  constexpr int TILE = 128 * 64;  // bf16 elements of one operand tile per stage
+  __shared__ __attribute__((aligned(16))) uint16_t A0[TILE], A1[TILE], B0[TILE], B1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = N / BN;
+  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  const int row0 = tm * BM, col0 = tn * BN;
+  const int S = K >> 6;
+
+  // Each wave copies 4 KiB of each operand tile per stage: 4 DMA instructions, lane i
+  // of instruction t filling unit u = 64 (4 wave + t) + i.
+  auto dma = [&](int s, uint16_t* Ab, uint16_t* Bb) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int u = 64 * (4 * wave + t) + lane;
+      const int r = u >> 3, c = (u & 7) ^ (r & 7);
+      const size_t off = (size_t)r * K + 64 * s + 8 * c;
+      __builtin_amdgcn_global_load_lds(A + (size_t)row0 * K + off, Ab + 8 * 64 * (4 * wave + t), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(B + (size_t)col0 * K + off, Bb + 8 * 64 * (4 * wave + t), 16, 0, 0);
+    }
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Operand fragment of MFMA k-step kk: lane l reads row (l % 32) of the 32-row
+  // block, values k = 16 kk + 8 (l / 32) + [0, 8).
+  auto frag = [&](const uint16_t* T, int row, int kk) {
+    const int c = 2 * kk + (lane >> 5);
+    const int u = row * 8 + (c ^ (row & 7));
+    return *reinterpret_cast<const v8bf*>(T + 8 * u);
+  };
+
+  auto compute = [&](const uint16_t* Ab, const uint16_t* Bb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      v8bf a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = frag(Ab, wm * 64 + 32 * i + (lane & 31), kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = frag(Bb, wn * 64 + 32 * j + (lane & 31), kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  auto sync_all = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  dma(0, A0, B0);
+  for (int s = 0; s < S; s += 2) {
+    sync_all();
+    if (s + 1 < S) dma(s + 1, A1, B1);
+    compute(A0, B0);
+    if (s + 1 < S) {
+      sync_all();
+      if (s + 2 < S) dma(s + 2, A0, B0);
+      compute(A1, B1);
+    }
+  }
+  sync_all();
+
+  // Epilogue: acc * g, + U @ L2t^T (U split into bf16 hi + lo), + bias, bf16 stores
+  // through a per-wave LDS tile (rows of 80 B).
+  const int lr = lane & 31, lh = lane >> 5;
+  uint16_t* tile = A0 + wave * (32 * 40);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rowb = row0 + wm * 64 + 32 * i;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int colb = col0 + wn * 64 + 32 * j;
+      v16f c = acc[i][j];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c[e] *= g;
+      for (int kk = 0; kk < rank; kk += 16) {
+        const float* up = U + (size_t)(rowb + lr) * rank + kk + 8 * lh;
+        const float4 u0 = *reinterpret_cast<const float4*>(up);
+        const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
+        const float uf[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        v8bf hi, lo;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          hi[t] = (__bf16)uf[t];
+          lo[t] = (__bf16)(uf[t] - (float)hi[t]);
+        }
+        const uint4 lb = *reinterpret_cast<const uint4*>(L2t + (size_t)(colb + lr) * rank + kk + 8 * lh);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
+      }
+      const float bv = bias ? bf16_to_f32(bias[colb + lr]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
+        tile[rin * 40 + lr] = (uint16_t)f32_to_bf16_rne(c[e] + bv);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int qd = lane + 64 * t;
+        const int rin = qd >> 2, ch = qd & 3;
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + rin * 40 + ch * 8);
+        const int row = rowb + rin;
+        if (row < M) *reinterpret_cast<uint4*>(Y + (size_t)row * N + colb + ch * 8) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_k2_bf16(const uint16_t* A, const float* U, const uint16_t* B,
+                          const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
+                          int N, int K, int M_pad, int rank, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
+  dim3 grid((N / 128) * (M_pad / 128));
+  hipExtLaunchKernelGGL(k2_gemm_bf16, grid, dim3(256), 0, st, ev0, ev1, 0, A, U, B, L2t, bias, g,
+                        Y, M, N, K, M_pad, rank);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -4,6 +4,9 @@
 //       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N].
 //       A -8 code cannot be held by the sign-magnitude E2M3 field: it raises the
 //       range flag, which the host turns into SVDQ_ERR_RANGE.
+// nvfp4: codes [N][K/2] E2M1 nibbles and scales [N][K/16] E4M3 bytes -> the exact
+//       dequantized weights e2m1 * s as bf16 [N][K] (2 and 4 significant bits: the
+//       product is a bf16 number).  An E4M3 NaN scale raises the range flag.
 #include "common.h"
 #include "kernels.h"
 
@@ -56,6 +59,38 @@ k_transpose_scales_u16(const uint16_t* __restrict__ in, uint16_t* __restrict__ o
   out[t] = in[n * G + g];
 }
 
+// One thread per 8 weights (4 code bytes, one E4M3 scale).
+__global__ void __launch_bounds__(256)
+k_pack_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+             uint4* __restrict__ out, int N, int K, int* __restrict__ flag) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)N * K / 8;
+  if (t >= total) return;
+  const int64_t n = t / (K / 8), k8 = t % (K / 8);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + 4 * k8);
+  const uint32_t sc = scales[n * (K / 16) + k8 / 2];
+  if ((sc & 0x7Fu) == 0x7Fu) atomicOr(flag, 1);
+  const uint32_t e = (sc >> 3) & 15u, m = sc & 7u;
+  float s = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if (sc & 0x80u) s = -s;
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t half[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (w >> (4 * (2 * p + h))) & 15u;
+      const uint32_t mag = c & 7u;
+      const float a = mag < 4 ? 0.5f * (float)mag
+                              : (float)(2u << ((mag - 4u) >> 1)) * (1.0f + 0.5f * (float)(mag & 1u));
+      const float v = (c & 8u) ? -(a * s) : a * s;
+      half[h] = __float_as_uint(v) >> 16;
+    }
+    o[p] = half[0] | (half[1] << 16);
+  }
+  out[t] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ void k_zero_flag(int* flag) { *flag = 0; }
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
@@ -68,6 +103,17 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
   const int64_t ts = (int64_t)N * G;
   hipLaunchKernelGGL(k_transpose_scales_u16, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
                      scales, out_scales, N, G);
+  return hipGetLastError();
+}
+
+
+
+hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
+                             int N, int K, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
+  const int64_t total = (int64_t)N * K / 8;
+  hipLaunchKernelGGL(k_pack_nvfp4, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, codes,
+                     scales, reinterpret_cast<uint4*>(out), N, K, flag);
   return hipGetLastError();
 }
 

@@ -21,6 +21,19 @@ hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U,
                           int rank, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
 
+hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
+                           const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
+                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
+                           hipEvent_t ev1 = nullptr);
+
+hipError_t launch_k2_bf16(const uint16_t* A, const float* U, const uint16_t* B,
+                          const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
+                          int N, int K, int M_pad, int rank, hipStream_t st,
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
+hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
+                             int N, int K, hipStream_t st);
+
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
                             uint16_t* out_scales, int* flag, int N, int K, hipStream_t st);
 

@@ -83,8 +83,6 @@ svdq_status check_svdq_config(const svdq_config* c) {
                 "group %d)", c->precision, c->group_size);
   if (c->rank != 0 && c->rank != 16 && c->rank != 32)
     return fail(SVDQ_ERR_CONFIG, "rank %d unsupported (0, 16 or 32)", c->rank);
-  if (nvfp4)
-    return fail(SVDQ_ERR_CONFIG, "nvfp4 is not available in this build");
   return SVDQ_OK;
 }
 
@@ -106,6 +104,12 @@ svdq_status check_m(int64_t M, int64_t K) {
   return SVDQ_OK;
 }
 
+svdq_status check_global(float g, const char* what) {
+  if (!(g > 0.f) || !(g < 3.0e38f))
+    return fail(SVDQ_ERR_RANGE, "nvfp4 %s scale %g must be finite and positive", what, (double)g);
+  return SVDQ_OK;
+}
+
 struct WsLayout {
   int64_t M_pad = 0;
   size_t codes = 0, scales = 0, lora = 0, total = 0;
@@ -115,9 +119,11 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   WsLayout L;
   L.M_pad = round_up(M, 128);
   const int64_t G = K / c->group_size;
-  // int4: GEMM A operand as E2M3 fields, 6 bits per value (3/4 byte)
-  const size_t codes = (size_t)(L.M_pad * K * 3 / 4);
-  const size_t scales = (size_t)(G * L.M_pad * 2);
+  // int4: GEMM A operand as E2M3 fields, 6 bits per value (3/4 byte), bf16 scales
+  // [G][M_pad]; nvfp4: the exact dequantized operand in bf16 [M_pad][K], no scales
+  const bool nv = c->precision == SVDQ_NVFP4;
+  const size_t codes = nv ? (size_t)(L.M_pad * K * 2) : (size_t)(L.M_pad * K * 3 / 4);
+  const size_t scales = nv ? 0 : (size_t)(G * L.M_pad * 2);
   const size_t lora = (size_t)(L.M_pad * c->rank * 4);  // fp32 U
   L.codes = 0;
   L.scales = (size_t)round_up((int64_t)codes, 256);
@@ -197,8 +203,11 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N, si
     return 0;
   }
   const int64_t G = K / cfg->group_size;
-  const size_t cb = (size_t)(N * K / 2);
-  const size_t sb = (size_t)round_up(G * N * 2, 256) + 256;  // + range-flag trailer
+  // int4: compact codes (1/2 byte per weight) and [G][N] bf16 scales; nvfp4: exact
+  // dequantized bf16 weights [N][K]; both with a 256-byte range-flag trailer
+  const bool nv = cfg->precision == SVDQ_NVFP4;
+  const size_t cb = nv ? (size_t)(N * K * 2) : (size_t)(N * K / 2);
+  const size_t sb = nv ? 256 : (size_t)round_up(G * N * 2, 256) + 256;
   if (codes_bytes) *codes_bytes = cb;
   if (scales_bytes) *scales_bytes = sb;
   return cb + sb;
@@ -216,18 +225,27 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
     return fail(SVDQ_ERR_ALIGN, "svdq_pack_weight: pointers must be 16-byte aligned");
   SVDQ_TRY(check_current_device());
   const int64_t G = K / cfg->group_size;
-  int* flag = reinterpret_cast<int*>(static_cast<uint8_t*>(packed_scales) + round_up(G * N * 2, 256));
-  SVDQ_TRY(hip_check(svdq::launch_pack_int4(codes, static_cast<const uint16_t*>(scales), packed_codes,
-                                             static_cast<uint16_t*>(packed_scales), flag, (int)N,
-                                             (int)K, stream),
-                     "pack kernel launch"));
+  const bool nv = cfg->precision == SVDQ_NVFP4;
+  int* flag = reinterpret_cast<int*>(static_cast<uint8_t*>(packed_scales) +
+                                     (nv ? 0 : round_up(G * N * 2, 256)));
+  if (nv)
+    SVDQ_TRY(hip_check(svdq::launch_pack_nvfp4(codes, static_cast<const uint8_t*>(scales),
+                                                reinterpret_cast<uint16_t*>(packed_codes), flag,
+                                                (int)N, (int)K, stream),
+                       "pack kernel launch"));
+  else
+    SVDQ_TRY(hip_check(svdq::launch_pack_int4(codes, static_cast<const uint16_t*>(scales),
+                                               packed_codes, static_cast<uint16_t*>(packed_scales),
+                                               flag, (int)N, (int)K, stream),
+                       "pack kernel launch"));
   int host_flag = 0;
   SVDQ_TRY(hip_check(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream),
                      "pack flag copy"));
   SVDQ_TRY(hip_check(hipStreamSynchronize(stream), "pack synchronize"));
   if (host_flag)
-    return fail(SVDQ_ERR_RANGE,
-                "int4 weight code -8 found: the packed layout holds the symmetric range [-7, 7]");
+    return fail(SVDQ_ERR_RANGE, nv ? "nvfp4 weight scale is an E4M3 NaN code"
+                                   : "int4 weight code -8 found: the packed layout holds the "
+                                     "symmetric range [-7, 7]");
   return ok();
 }
 
@@ -240,10 +258,11 @@ size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K) {
 svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
                               const uint16_t* smooth, const uint16_t* lora_down, float act_global,
                               uint8_t* codes, void* scales, float* lora_act, hipStream_t stream) {
-  (void)act_global;
   if (!cfg || !x || !smooth || !codes || !scales)
     return fail(SVDQ_ERR_NULL, "svdq_quantize_act: NULL argument");
   SVDQ_TRY(check_svdq_config(cfg));
+  const bool nv = cfg->precision == SVDQ_NVFP4;
+  if (nv) SVDQ_TRY(check_global(act_global, "activation"));
   if (cfg->rank > 0 && (!lora_down || !lora_act))
     return fail(SVDQ_ERR_NULL, "svdq_quantize_act: rank %d needs lora_down and lora_act", cfg->rank);
   SVDQ_TRY(check_k(K));
@@ -253,21 +272,32 @@ svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t
     return fail(SVDQ_ERR_ALIGN, "svdq_quantize_act: pointers must be 16-byte aligned");
   if (M == 0) return ok();
   SVDQ_TRY(check_current_device());
-  SVDQ_TRY(hip_check(svdq::launch_k1_int4(false, x, (int)M, (int)K, smooth,
-                                           cfg->rank ? lora_down : nullptr, cfg->rank, codes,
-                                           static_cast<uint16_t*>(scales),
-                                           cfg->rank ? lora_act : nullptr, (int)M, stream),
-                     "quantize kernel launch"));
+  if (nv)
+    SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(false, x, (int)M, (int)K, smooth,
+                                              cfg->rank ? lora_down : nullptr, cfg->rank,
+                                              act_global, codes, static_cast<uint8_t*>(scales),
+                                              cfg->rank ? lora_act : nullptr, (int)M, stream),
+                       "quantize kernel launch"));
+  else
+    SVDQ_TRY(hip_check(svdq::launch_k1_int4(false, x, (int)M, (int)K, smooth,
+                                             cfg->rank ? lora_down : nullptr, cfg->rank, codes,
+                                             static_cast<uint16_t*>(scales),
+                                             cfg->rank ? lora_act : nullptr, (int)M, stream),
+                       "quantize kernel launch"));
   return ok();
 }
 
 svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, const uint16_t* x,
                              int64_t M, float act_global, uint16_t* y, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  (void)act_global;
   if (!cfg || !w || !x || !y || !workspace || !w->qweight || !w->wscales || !w->smooth)
     return fail(SVDQ_ERR_NULL, "svdq_w4a4_linear: NULL argument");
   SVDQ_TRY(check_svdq_config(cfg));
+  const bool nv = cfg->precision == SVDQ_NVFP4;
+  if (nv) {
+    SVDQ_TRY(check_global(act_global, "activation"));
+    SVDQ_TRY(check_global(w->w_global, "weight"));
+  }
   if (cfg->rank > 0 && (!w->lora_down || !w->lora_up))
     return fail(SVDQ_ERR_NULL, "svdq_w4a4_linear: rank %d needs lora_down and lora_up", cfg->rank);
   SVDQ_TRY(check_k(w->K));
@@ -291,6 +321,23 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
   float* a_lora = reinterpret_cast<float*>(ws + L.lora);
   timer_begin_call();
   const EvPair e1 = timer_kernel();
+  if (nv) {
+    SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(true, x, (int)M, (int)w->K, w->smooth,
+                                              cfg->rank ? w->lora_down : nullptr, cfg->rank,
+                                              act_global, a_codes, nullptr,
+                                              cfg->rank ? a_lora : nullptr, (int)L.M_pad, stream,
+                                              e1.start, e1.end),
+                       "quantize kernel launch"));
+    const EvPair e2 = timer_kernel();
+    const float g = act_global * w->w_global;
+    SVDQ_TRY(hip_check(svdq::launch_k2_bf16(reinterpret_cast<const uint16_t*>(a_codes), a_lora,
+                                             reinterpret_cast<const uint16_t*>(w->qweight),
+                                             w->lora_up, w->bias, g, y, (int)M, (int)w->N,
+                                             (int)w->K, (int)L.M_pad, cfg->rank, stream, e2.start,
+                                             e2.end),
+                       "gemm kernel launch"));
+    return ok();
+  }
   SVDQ_TRY(hip_check(svdq::launch_k1_int4(true, x, (int)M, (int)w->K, w->smooth,
                                            cfg->rank ? w->lora_down : nullptr, cfg->rank, a_codes,
                                            a_scales, cfg->rank ? a_lora : nullptr, (int)L.M_pad,
