@@ -156,3 +156,15 @@ def test_nvfp4_sizes_and_global_scale_check():
         assert st == L.ERR_RANGE, (gx, gw)
     assert lib.svdq_quantize_act(ctypes.byref(c), FAKE, 4, 512, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE,
                                  None) == L.ERR_RANGE
+
+
+def test_awq_argument_rules():
+    lib = L.lib()
+    c = cfg(rank=0)
+    awq = L.AwqW4A16Weight(512, 512, FAKE, FAKE, FAKE, None)
+    assert lib.awq_w4a16_linear(ctypes.byref(c), ctypes.byref(awq), FAKE, 0, FAKE, None) == L.OK
+    assert lib.awq_w4a16_linear(ctypes.byref(c), ctypes.byref(awq), FAKE_MISALIGNED, 4, FAKE, None) == L.ERR_ALIGN
+    bad = L.AwqW4A16Weight(500, 512, FAKE, FAKE, FAKE, None)
+    assert lib.awq_w4a16_linear(ctypes.byref(c), ctypes.byref(bad), FAKE, 4, FAKE, None) == L.ERR_SHAPE
+    nul = L.AwqW4A16Weight(512, 512, FAKE, None, FAKE, None)
+    assert lib.awq_w4a16_linear(ctypes.byref(c), ctypes.byref(nul), FAKE, 4, FAKE, None) == L.ERR_NULL

@@ -31,6 +31,10 @@ hipError_t launch_k2_bf16(const uint16_t* A, const float* U, const uint16_t* B,
                           int N, int K, int M_pad, int rank, hipStream_t st,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
+hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc, const uint8_t* Z,
+                         const uint16_t* bias, uint16_t* Y, int M, int N, int K, hipStream_t st,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
 hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
                              int N, int K, hipStream_t st);
 

@@ -354,7 +354,6 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
 
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, const uint16_t* x,
                              int64_t M, uint16_t* y, hipStream_t stream) {
-  (void)stream;
   if (!cfg || !w || !x || !y || !w->qweight || !w->scales || !w->zeros)
     return fail(SVDQ_ERR_NULL, "awq_w4a16_linear: NULL argument");
   if (cfg->precision != SVDQ_INT4 || cfg->group_size != 64 || cfg->rank != 0 ||
@@ -363,7 +362,18 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, 
   SVDQ_TRY(check_k(w->K));
   SVDQ_TRY(check_n(w->N));
   SVDQ_TRY(check_m(M, w->K));
-  return fail(SVDQ_ERR_CONFIG, "awq_w4a16 is not available in this build");
+  if (M * w->N > (int64_t(1) << 36)) return fail(SVDQ_ERR_SHAPE, "M * N too large");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w->qweight) || !aligned16(w->scales) ||
+      !aligned16(w->zeros) || (w->bias && !aligned16(w->bias)))
+    return fail(SVDQ_ERR_ALIGN, "awq_w4a16_linear: pointers must be 16-byte aligned");
+  if (M == 0) return ok();
+  SVDQ_TRY(check_current_device());
+  timer_begin_call();
+  const EvPair e1 = timer_kernel();
+  SVDQ_TRY(hip_check(svdq::launch_k4_awq(x, w->qweight, w->scales, w->zeros, w->bias, y, (int)M,
+                                          (int)w->N, (int)w->K, stream, e1.start, e1.end),
+                     "awq kernel launch"));
+  return ok();
 }
 
 svdq_status svdq_timing_start(int max_calls) {
