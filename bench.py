@@ -42,12 +42,17 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {
-    # name: (config id, M, K, N, rank)
-    "attn_proj": (2, 4096, 3072, 3072, 32),
-    "qkv": (3, 4608, 3072, 9216, 32),
-    "mlp_up": (3, 4608, 3072, 12288, 32),
-    "mlp_down": (3, 4608, 12288, 3072, 32),
+    # name: (method, config id, M, K, N, rank)
+    "attn_proj": ("int4", 2, 4096, 3072, 3072, 32),
+    "qkv": ("int4", 3, 4608, 3072, 9216, 32),
+    "mlp_up": ("int4", 3, 4608, 3072, 12288, 32),
+    "mlp_down": ("int4", 3, 4608, 12288, 3072, 32),
+    "nvfp4_sq": ("nvfp4", 4, 4096, 3072, 3072, 32),
+    "nvfp4_up": ("nvfp4", 4, 4096, 3072, 12288, 32),
+    "awq_sq": ("awq", 4, 4096, 3072, 3072, 0),
+    "awq_up": ("awq", 4, 4096, 3072, 12288, 0),
 }
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 GEMM_SOURCES = ["w4a4_rank_corrected_linear_amd/csrc/k2_gemm_int4.hip",
                 "w4a4_rank_corrected_linear_amd/csrc/common.h"]
@@ -82,29 +87,42 @@ def recorded_traffic(workload: str):
 
 def make_inputs(workload: str):
     from synth import inputs as I
-    cid, M, K, N, rank = WORKLOADS[workload]
+    method, cid, M, K, N, rank = WORKLOADS[workload]
     sd = I.seeds(cid)
     idx = I.outlier_channels(K, I.default_outlier_count(K), sd.outliers)
     x = I.activations(M, K, sd.x, idx, 30.0)
-    pb = I.prepared_int4_bytes(cid, K, N, rank)
-    return dict(M=M, K=K, N=N, rank=rank, x=x, pb=pb, seeds=dict(x=sd.x, w=sd.w + 500,
-                                                                 bias=sd.bias, outliers=sd.outliers))
+    if method == "int4":
+        pb = I.prepared_int4_bytes(cid, K, N, rank)
+    elif method == "nvfp4":
+        pb = I.prepared_nvfp4_bytes(cid, K, N, rank)
+    else:
+        pb = I.prepared_awq_bytes(cid, K, N)
+    return dict(method=method, M=M, K=K, N=N, rank=rank, x=x, pb=pb,
+                seeds=dict(x=sd.x, w=sd.w, bias=sd.bias, outliers=sd.outliers))
 
 
 def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 8):
     """The oracle on the same inputs, timed on the host (test infrastructure)."""
     from oracle import linear as OL
     from oracle import prep as P
-    pb = inp["pb"]
-    layer = P.SvdqLayer(precision="int4", K=pb.K, N=pb.N, rank=pb.rank, qweight=pb.qweight,
-                        wscales=pb.wscales, w_global=1.0, act_global=1.0, smooth=pb.smooth,
-                        lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+    pb, method = inp["pb"], inp["method"]
+    if method == "awq":
+        layer = P.AwqLayer(K=pb.K, N=pb.N, group=64, qweight=pb.qweight, scales=pb.scales,
+                           zeros=pb.zeros, bias=pb.bias)
+        run = lambda: OL.awq_w4a16_linear(inp["x"], layer)  # noqa: E731
+    else:
+        wg = getattr(pb, "w_global", 1.0)
+        ag = getattr(pb, "act_global", 1.0)
+        layer = P.SvdqLayer(precision=method, K=pb.K, N=pb.N, rank=pb.rank, qweight=pb.qweight,
+                            wscales=pb.wscales, w_global=wg, act_global=ag, smooth=pb.smooth,
+                            lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+        run = lambda: OL.w4a4_linear(method, inp["x"], layer)  # noqa: E731
     M, K, N = inp["M"], inp["K"], inp["N"]
     times = []
     t_all = time.perf_counter()
     while len(times) < 2 or (time.perf_counter() - t_all < min_seconds and len(times) < max_reps):
         t0 = time.perf_counter()
-        OL.w4a4_linear("int4", inp["x"], layer)
+        run()
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     try:
@@ -149,7 +167,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
                 return key
         return name[:40]
 
-    cid, M, K, N, rank = WORKLOADS[workload]
+    _, cid, M, K, N, rank = WORKLOADS[workload]
     lines = [f"# rocprofv3 kernel statistics: bench.py, workload {workload} "
              f"(M={M} K={K} N={N} rank {rank}, int4 g64), 500 timed + 50 warmup calls",
              f"# command: {PROFILE_CMDS['stats']}",
@@ -233,6 +251,7 @@ def main() -> int:
     svdq.check_device(0)
 
     inp = make_inputs(args.workload)
+    method = inp["method"]
     M, K, N, rank = inp["M"], inp["K"], inp["N"], inp["rank"]
     pb = inp["pb"]
 
@@ -240,28 +259,40 @@ def main() -> int:
         t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
         return t.view(torch.bfloat16).to(dev)
 
-    codes = torch.from_numpy(pb.qweight).to(dev)
-    layer = svdq.SvdqLinear.from_interchange(codes, bf16(pb.wscales), bf16(pb.smooth),
-                                             bf16(pb.lora_down), bf16(pb.lora_up), bf16(pb.bias))
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
+
     x = bf16(inp["x"])
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ws = layer.workspace(M, dev)
-    print(f"[bench] workload {args.workload} M={M} K={K} N={N} rank={rank}; warmup {args.warmup}, "
-          f"steps {args.steps}", file=sys.stderr, flush=True)
+    if method == "awq":
+        layer = svdq.AwqLinear(u8(pb.qweight), bf16(pb.scales), u8(pb.zeros), bf16(pb.bias))
+        call = lambda: layer(x, out=y)  # noqa: E731
+        n_kernels = 1
+    else:
+        scales = bf16(pb.wscales) if method == "int4" else u8(pb.wscales)
+        layer = svdq.SvdqLinear.from_interchange(
+            u8(pb.qweight), scales, bf16(pb.smooth), bf16(pb.lora_down), bf16(pb.lora_up),
+            bf16(pb.bias), precision=method, w_global=getattr(pb, "w_global", 1.0),
+            act_global=getattr(pb, "act_global", 1.0))
+        ws = layer.workspace(M, dev)
+        call = lambda: layer(x, out=y, workspace=ws)  # noqa: E731
+        n_kernels = 2
+    print(f"[bench] workload {args.workload} ({method}) M={M} K={K} N={N} rank={rank}; warmup "
+          f"{args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
-        layer(x, out=y, workspace=ws)
+        call()
     torch.cuda.synchronize()
 
     svdq.timing_start(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        layer(x, out=y, workspace=ws)
+        call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     calls, kern_ms = svdq.timing_stop()
-    if calls != args.steps or len(kern_ms) != 2:
+    if calls != args.steps or len(kern_ms) != n_kernels:
         raise RuntimeError(f"kernel timing recorded {calls} calls / {len(kern_ms)} kernels")
     print(f"[bench] timed {args.steps} calls in {wall:.4f} s", file=sys.stderr, flush=True)
 
@@ -278,13 +309,23 @@ def main() -> int:
     ops = 2.0 * M * N * K
     ms_per_step = wall * 1e3 / args.steps
     value = ops / (ms_per_step * 1e-3) / 1e12
-    k1_ms, k2_ms = kern_ms
-    achieved = ops / (k2_ms * 1e-3) / 1e12
-    traffic = recorded_traffic(args.workload)
-    k1_bytes = M * K * 2 + M * K * 3 // 4 + (K // 64) * M * 2 + M * rank * 4
+    gemm_ms = kern_ms[-1]
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_FP6_TFLOPS if method == "int4" else PEAK_BF16_TFLOPS
+    kernels = {"gemm_ms": round(gemm_ms, 6), "gemm_TOPS": round(achieved, 3)}
+    if n_kernels == 2:
+        act_bytes = M * K * 3 // 4 + (K // 64) * M * 2 if method == "int4" else M * K * 2
+        k1_bytes = M * K * 2 + act_bytes + M * rank * 4
+        kernels = {"quantize_ms": round(kern_ms[0], 6),
+                   "quantize_GBps_algorithmic": round(k1_bytes / (kern_ms[0] * 1e-3) / 1e9, 1),
+                   **kernels}
+    desc = {"int4": "svdq_w4a4 int4 g64", "nvfp4": "svdq_w4a4 nvfp4 g16",
+            "awq": "awq_w4a16 int4 g64"}[method]
+    metric = METRIC if args.workload == "attn_proj" else (
+        f"{desc} linear effective TOPS at M={M},K={K},N={N}")
 
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -294,26 +335,22 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4",
+        "dtype": {"int4": "int4", "nvfp4": "nvfp4", "awq": "int4-weight/bf16-act"}[method],
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: svdq_w4a4 int4 g64 rank {rank}, "
-                               f"M={M} K={K} N={N}",
-                   "M": M, "K": K, "N": N, "rank": rank, "precision": "int4", "group_size": 64,
+        "config": {"workload": f"{args.workload}: {desc}" + (f" rank {rank}" if rank else "") +
+                               f", M={M} K={K} N={N}",
+                   "M": M, "K": K, "N": N, "rank": rank, "method": method,
                    "compute_dtype": "bf16", "seeds": inp["seeds"]},
         "pct_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
-        "kernels": {
-            "quantize_ms": round(k1_ms, 6),
-            "quantize_GBps_algorithmic": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
-            "gemm_ms": round(k2_ms, 6),
-            "gemm_TOPS": round(achieved, 3),
-        },
+        "pct_fp4_peak": round(100.0 * value / PEAK_FP6_TFLOPS, 2),
+        "kernels": kernels,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
-            "peak": PEAK_FP6_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP6_TFLOPS, 4),
-            "traffic": traffic,
+            "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(args.workload),
         },
         "cpu_baseline": None,
     }

@@ -215,3 +215,26 @@ def prepared_nvfp4_bytes(config_id: int, K: int, N: int, rank: int = 32,
         K=K, N=N, rank=rank, qweight=codes, wscales=scales, smooth=base.smooth,
         lora_down=base.lora_down, lora_up=base.lora_up, bias=base.bias,
         w_global=float(np.float32(0.02 / 6.0)), act_global=float(np.float32(1.0 / 168.0)))
+
+
+@dataclasses.dataclass
+class PreparedAwqBytes:
+    """Seeded bytes of an awq_w4a16 layer: unsigned 4-bit codes uniform over 0..15,
+    bf16 group scales about 0.003, zero points uniform over 0..15, bf16 bias."""
+
+    K: int
+    N: int
+    qweight: np.ndarray   # uint8 [N, K/2]
+    scales: np.ndarray    # bf16 bits [N, K/64]
+    zeros: np.ndarray     # uint8 [N, K/64]
+    bias: np.ndarray      # bf16 bits [N]
+
+
+def prepared_awq_bytes(config_id: int, K: int, N: int) -> PreparedAwqBytes:
+    rng = np.random.default_rng(seeds(config_id).w + 900)
+    return PreparedAwqBytes(
+        K=K, N=N,
+        qweight=rng.integers(0, 256, size=(N, K // 2), dtype=np.uint16).astype(np.uint8),
+        scales=to_bf16_bits((0.003 * np.exp(0.1 * rng.standard_normal((N, K // 64)))).astype(np.float32)),
+        zeros=rng.integers(0, 16, size=(N, K // 64), dtype=np.uint16).astype(np.uint8),
+        bias=bias(N, seeds(config_id).bias))
