@@ -75,7 +75,8 @@ typedef struct {
   const void* wscales;       /* packed scales, svdq_packed_weight_bytes() scales part    */
   float w_global;            /* NVFP4 per-tensor weight scale g_w; ignored for int4      */
   const uint16_t* smooth;    /* [K] bf16 smoothing multiplier m                          */
-  const uint16_t* lora_down; /* [r][K] bf16, L1^T (NULL iff r == 0)                      */
+  const uint16_t* lora_down; /* L1^T in the packed order of svdq_pack_lora_down (r*K bf16;
+                                NULL iff r == 0)                                          */
   const uint16_t* lora_up;   /* [N][r] bf16, L2^T (NULL iff r == 0)                      */
   const uint16_t* bias;      /* [N] bf16 or NULL                                         */
 } svdq_w4a4_weight;
@@ -111,6 +112,15 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
 svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N,
                              const uint8_t* codes, const void* scales,
                              uint8_t* packed_codes, void* packed_scales, hipStream_t stream);
+
+/* Reorders lora_down [r][K] bf16 (L1^T, interchange layout) into the order the layer's
+ * quantizer reads it: for each 128-wide k-block, 16-rank slice and 8-value chunk c of
+ * a 32-value lane slot, 64 entries of 16 bytes (entry 16 q + i holds ranks 16 sl + i,
+ * k = 128 kb + 32 q + 8 c .. + 8), each group 1 KiB contiguous.  `packed` has r*K bf16
+ * (same size); rank 16 or 32, K a multiple of 128.  The result is what
+ * svdq_w4a4_weight.lora_down points to.  Offline step; enqueued on `stream`. */
+svdq_status svdq_pack_lora_down(const svdq_config* cfg, int64_t K, const uint16_t* lora_down,
+                                uint16_t* packed, hipStream_t stream);
 
 /* Workspace bytes svdq_w4a4_linear needs for M tokens of K inputs. */
 size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);

@@ -168,3 +168,11 @@ def test_awq_argument_rules():
     assert lib.awq_w4a16_linear(ctypes.byref(c), ctypes.byref(bad), FAKE, 4, FAKE, None) == L.ERR_SHAPE
     nul = L.AwqW4A16Weight(512, 512, FAKE, None, FAKE, None)
     assert lib.awq_w4a16_linear(ctypes.byref(c), ctypes.byref(nul), FAKE, 4, FAKE, None) == L.ERR_NULL
+
+
+def test_pack_lora_down_argument_rules():
+    lib = L.lib()
+    assert lib.svdq_pack_lora_down(ctypes.byref(cfg()), 512, None, FAKE, None) == L.ERR_NULL
+    assert lib.svdq_pack_lora_down(ctypes.byref(cfg(rank=0)), 512, FAKE, FAKE, None) == L.ERR_CONFIG
+    assert lib.svdq_pack_lora_down(ctypes.byref(cfg()), 500, FAKE, FAKE, None) == L.ERR_SHAPE
+    assert lib.svdq_pack_lora_down(ctypes.byref(cfg()), 512, FAKE_MISALIGNED, FAKE, None) == L.ERR_ALIGN

@@ -219,3 +219,44 @@ def test_timing_hook_counts_two_kernels(tiny):
         dl(x)
     calls, ms = svdq.timing_stop()
     assert calls == 3 and len(ms) == 2 and all(t > 0 for t in ms)
+
+
+def test_workspace_with_three_k_splits():
+    """K = 3200 is quantized in k-splits of 1536, 1536 and 128 values: codes and scales
+    in the workspace are bit-exact, and the partial U sums add up to U."""
+    rng = np.random.default_rng(81)
+    M, K, N, r = 40, 3200, 128, 32
+    idx = I.outlier_channels(K, 31, 7)
+    x = I.activations(M, K, 101, idx, 30.0)
+    m = F.bf16_rne(rng.uniform(0.05, 1.5, K).astype(np.float32))
+    ld = F.bf16_rne((rng.standard_normal((r, K)) * 0.05).astype(np.float32))
+    lu = F.bf16_rne((rng.standard_normal((N, r)) * 0.05).astype(np.float32))
+    qw = F.pack_nibbles(F.int4_encode(rng.integers(-7, 8, size=(N, K))))
+    sw = F.bf16_rne((0.01 + 0.01 * rng.random((N, K // 64))).astype(np.float32))
+    layer = P.SvdqLayer(precision="int4", K=K, N=N, rank=r, qweight=qw, wscales=sw, w_global=1.0,
+                        act_global=1.0, smooth=m, lora_down=ld, lora_up=lu, bias=None)
+    dl = _layer_dev(layer)
+    ws = torch.zeros(dl.workspace(M, torch.device("cuda")).numel(), dtype=torch.uint8, device="cuda")
+    y = dl(dev_bf16(x), workspace=ws)
+    torch.cuda.synchronize()
+    ref = Q.quantize_act_int4(x, m, ld)
+    w = host_bits(ws)
+    M_pad, G, nsplit = 128, K // 64, 3
+    assert np.array_equal(decode_fp6_operand(w, M_pad, K)[:M], ref["q"])
+    off_s = M_pad * K * 3 // 4
+    s = w[off_s: off_s + G * M_pad * 2].view(np.uint16).reshape(G, M_pad)
+    assert np.array_equal(s[:, :M], ref["scales"].T)
+    off_u = off_s + -(-G * M_pad * 2 // 256) * 256
+    u = w[off_u: off_u + nsplit * M_pad * r * 4].view(np.float32).reshape(nsplit, M_pad, r)
+    check_u(u.astype(np.float64).sum(axis=0)[:M], ref, ld)
+    check_y(host_bits(y), OL.w4a4_linear("int4", x, layer)["r"])
+
+
+def test_pack_lora_down_fragment_order():
+    rng = np.random.default_rng(82)
+    for rank, K in [(32, 512), (16, 384)]:
+        ld = F.bf16_rne(rng.standard_normal((rank, K)).astype(np.float32))
+        packed = host_bits(svdq.pack_lora_down(dev_bf16(ld)))
+        units = packed.reshape(K // 128, rank // 16, 4, 4, 16, 8)       # kb, sl, c, q, i, 8
+        expect = ld.reshape(rank // 16, 16, K // 128, 4, 4, 8)          # sl, i, kb, q, c, 8
+        assert np.array_equal(units, expect.transpose(2, 0, 4, 3, 1, 5))

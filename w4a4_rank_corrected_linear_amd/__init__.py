@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     SvdqLinear,
     awq_w4a16_linear,
     check_device,
+    pack_lora_down,
     pack_weight,
     quantize_act,
     timing_start,

@@ -88,11 +88,22 @@ def pack_weight(codes: torch.Tensor, scales: torch.Tensor, precision: str = "int
     return pc, ps
 
 
+def pack_lora_down(lora_down: torch.Tensor, precision: str = "int4") -> torch.Tensor:
+    """svdq_pack_lora_down: [r, K] bf16 -> the quantizer's fragment order (same size)."""
+    _want(lora_down, torch.bfloat16, "lora_down")
+    rank, K = lora_down.shape
+    cfg = L.config(precision, rank)
+    out = torch.empty_like(lora_down)
+    L.check(L.lib().svdq_pack_lora_down(ctypes.byref(cfg), K, _p(lora_down), _p(out), _stream()),
+            "svdq_pack_lora_down")
+    return out
+
+
 class SvdqLinear:
     """A prepared svdq_w4a4 layer resident in device memory.
 
-    smooth [K] bf16, lora_down [r, K] bf16, lora_up [N, r] bf16, bias [N] bf16 or None;
-    qweight/wscales in the kernel layout (see ``pack_weight``).
+    smooth [K] bf16, lora_up [N, r] bf16, bias [N] bf16 or None; qweight/wscales and
+    lora_down in the kernel layouts (see ``pack_weight`` and ``pack_lora_down``).
     """
 
     def __init__(self, K: int, N: int, qweight, wscales, smooth, lora_down, lora_up, bias,
@@ -116,8 +127,8 @@ class SvdqLinear:
                          precision: str = "int4", w_global: float = 1.0, act_global: float = 1.0):
         N, K2 = codes.shape
         pc, ps = pack_weight(codes, scales, precision)
-        return cls(2 * K2, N, pc, ps, smooth, lora_down, lora_up, bias, precision, w_global,
-                   act_global)
+        ld = None if lora_down is None else pack_lora_down(lora_down, precision)
+        return cls(2 * K2, N, pc, ps, smooth, ld, lora_up, bias, precision, w_global, act_global)
 
     def workspace(self, M: int, device) -> torch.Tensor:
         need = max(int(L.lib().svdq_workspace_bytes(ctypes.byref(self.cfg), M, self.K)), 256)

@@ -6,36 +6,105 @@
 // in svdq.h: xhat = bf16(x m), s = bf16(amax / 7), q = round-half-even(xhat / s)
 // clamped to [-7, 7], U = xhat @ lora_down^T (fp32 accumulation, not rounded).
 //
-// Work split: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide k-blocks
-// kb = w, w+8, ...  Lane l holds row l%16 and the 32 consecutive values
-// k = 128 kb + 32 q + [0, 32), q = l/16, i.e. one half (h = q%2) of the 64-group
-// g = 2 kb + q/2: the amax is an in-lane max over 32 values and one cross-lane step
-// (lane l^16).  The same 32 values are one MFMA lane-slot of the GEMM's A operand,
-// so the fused layout is produced in registers by v_cvt_scalef32_2xpk16_fp6_f32.
-// For the rank-r down projection, MFMA call c (0..3) of v_mfma_f32_16x16x32_bf16
-// takes the lane's chunk c (k = ... + 8c + [0, 8)) at MFMA k-position 8q + [0, 8);
-// the B operand is read from lora_down at the same k.  Per-wave partial U tiles are
-// summed in LDS in a fixed order (deterministic).
+// Two kernels share the quantizer below:
+//  * k1_int4_fused (the layer's own path) uses the batch skeleton of k1_batch.h and
+//    writes the GEMM operand layout, scales [K/64][M_pad] and partial U per k-split;
+//  * k1_int4_interchange (svdq_quantize_act) streams whole rows with register
+//    prefetch and writes codes [M][K/2], scales [M][K/64] and U [M][r].
+// In both, lane l holds half h = q % 2 of the 64-group g = k0 / 64 (q = l / 16): the
+// amax is an in-lane max over 32 values and one cross-lane step (lane l ^ 16).  The
+// same 32 values are one MFMA lane slot of the GEMM's A operand, so the fused layout
+// is produced in registers by v_cvt_scalef32_2xpk16_fp6_f32.
 #include "common.h"
+#include "k1_batch.h"
 #include "kernels.h"
 
 namespace svdq {
 
 typedef int v6i __attribute__((ext_vector_type(6)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+// Scale and clamped quotients of the lane's 32 values (all lanes must call it).
+__device__ __forceinline__ uint32_t int4_quant32(const float (&xh)[32], float (&cq)[32]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  const uint32_t s_bits = f32_to_bf16_rne(amax / 7.0f);
+  const float s = bf16_to_f32(s_bits);
+  const bool tiny = (s > 0.f) && (s < 0x1p-125f);
+  // q = round-half-even(xhat / s), decided exactly.  r = v_rcp_f32(s) is within one ulp
+  // of 1/s; y1 = xhat r is then within a few ulp of the quotient, the remainder
+  // e = xhat - y1 s is exact (fma), and y = y1 + e r differs from the quotient by a
+  // few ulp times 2^-23 relative: it rounds exactly onto k + 1/2 at a tie, while a
+  // non-tie quotient of two bf16 numbers lies at least 2^-9 from any half-integer.
+  // With s = 0 every value is 0 and r = 0 gives y = 0.  A normal bf16 scale is within
+  // 2^-9 relative of amax / 7, so |y| <= 7.014 and rounding to the nearest integer
+  // already lands in [-7, 7]: the common path needs no clamp.  Scales below 2^-125
+  // (subnormal bf16 scales lose precision, and 1/s may overflow) take the exact
+  // division and the clamp; that case is tested once per wave so the common path
+  // stays straight-line.
+  const float rcp = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
+  if (!__any(tiny)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float y1 = xh[i] * rcp;
+      const float e = __builtin_fmaf(-y1, s, xh[i]);
+      cq[i] = __builtin_fmaf(e, rcp, y1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float y1 = xh[i] * rcp;
+      const float e = __builtin_fmaf(-y1, s, xh[i]);
+      const float y = tiny ? __fdiv_rn(xh[i], s) : __builtin_fmaf(e, rcp, y1);
+      cq[i] = __builtin_amdgcn_fmed3f(y, -7.0f, 7.0f);
+    }
+  }
+  return s_bits;
+}
+
+struct QuantInt4Fused {
+  __device__ static void block(const K1Args& a, const float (&xh)[32], int row, int k0, int q) {
+    float cq[32];
+    const uint32_t s_bits = int4_quant32(xh, cq);
+    const int g = k0 >> 6, h = q & 1;
+    // E2M3 fields of value q/8: the converter divides by the scale 8 and rounds to
+    // nearest even on the subnormal grid (step 1/8), i.e. to q/8.  Output field 2j
+    // comes from src0[j] and field 2j+1 from src1[j]: even k go to src0 and odd k
+    // to src1, so field f holds k = f.
+    v16f ev, od;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      ev[j] = cq[2 * j];
+      od[j] = cq[2 * j + 1];
+    }
+    const v6i f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+    // GEMM A-operand layout: chunk (row-block, group) of 1536 B; lane slot
+    // h*32 + row%32 holds dwords 0-3 at slot*16 and dwords 4-5 at 1024 + slot*8.
+    uint8_t* chunk = a.out + ((size_t)(row >> 5) * (a.K >> 6) + g) * 1536;
+    const int slot = h * 32 + (row & 31);
+    *reinterpret_cast<uint4*>(chunk + slot * 16) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+    *reinterpret_cast<uint2*>(chunk + 1024 + slot * 8) = make_uint2(f6[4], f6[5]);
+    if (h == 0) static_cast<uint16_t*>(a.scales)[(size_t)g * a.M_pad + row] = (uint16_t)s_bits;
+  }
+};
+
+__global__ void __launch_bounds__(256, 2) k1_int4_fused(K1Args a) { k1_batch<QuantInt4Fused>(a); }
+
+// Interchange kernel: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide
+// k-blocks kb = w, w+8, ... and prefetches the next block's X, smoothing and
+// lora_down operands into registers.  U is summed over the 8 waves in LDS.
 struct K1Load {
   uint4 x[4];
   uint4 m[4];
   uint4 l[2][4];  // lora_down B operands for the rank slices (0..15, 16..31)
 };
 
-template <int MODE>  // 0: interchange layout, 1: fused (GEMM operand) layout
 __global__ void __launch_bounds__(512)
-k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
-              const uint16_t* __restrict__ smooth, const uint16_t* __restrict__ ldown, int rank,
-              uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-              float* __restrict__ uact, int M_out, int M_pad) {
+k1_int4_interchange(const uint16_t* __restrict__ x, int M, int K,
+                    const uint16_t* __restrict__ smooth, const uint16_t* __restrict__ ldown,
+                    int rank, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                    float* __restrict__ uact) {
   __shared__ float ured[8][16][33];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -98,54 +167,10 @@ k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
         xh[8 * c + 2 * p + 1] = __uint_as_float(w & 0xFFFF0000u);
       }
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    const uint32_t s_bits = f32_to_bf16_rne(amax / 7.0f);
-    const float s = bf16_to_f32(s_bits);
-    const bool tiny = (s > 0.f) && (s < 0x1p-125f);
-    const float rcp = (s > 0.f && !tiny) ? __frcp_rn(s) : 0.f;
-
-    // q = round-half-even(xhat / s), decided exactly: y1 = xhat * (1/s) is a few ulp
-    // from the quotient; the remainder step e = xhat - y1 s (exact by fma) and
-    // y2 = y1 + e/s land on the correctly rounded quotient, in particular exactly on
-    // k + 1/2 at a tie, while a non-tie quotient of two bf16 numbers is at least 2^-9
-    // from any half-integer.  Scales below 2^-125 (1/s may overflow) divide exactly.
     float cq[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float y;
-      if (tiny) {
-        y = __fdiv_rn(xh[i], s);
-      } else {
-        const float y1 = xh[i] * rcp;
-        const float e = __builtin_fmaf(-y1, s, xh[i]);
-        y = __builtin_fmaf(e, rcp, y1);
-      }
-      cq[i] = __builtin_amdgcn_fmed3f(y, -7.0f, 7.0f);
-    }
+    const uint32_t s_bits = int4_quant32(xh, cq);
 
-    if constexpr (MODE == 1) {
-      // E2M3 fields of value q/8: the converter divides by the scale 8 and rounds to
-      // nearest even on the subnormal grid (step 1/8), i.e. to q/8.  Output field 2j
-      // comes from src0[j] and field 2j+1 from src1[j]: even k go to src0 and odd k
-      // to src1, so field f holds k = f.
-      v16f ev, od;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        ev[j] = cq[2 * j];
-        od[j] = cq[2 * j + 1];
-      }
-      const v6i f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
-      // GEMM A-operand layout: chunk (row-block, group) of 1536 B; lane slot
-      // h*32 + row%32 holds dwords 0-3 at slot*16 and dwords 4-5 at 1024 + slot*8.
-      uint8_t* chunk = codes + ((size_t)(row >> 5) * G + g) * 1536;
-      const int slot = h * 32 + (row & 31);
-      *reinterpret_cast<uint4*>(chunk + slot * 16) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint2*>(chunk + 1024 + slot * 8) = make_uint2(f6[4], f6[5]);
-      if (h == 0) scales[(size_t)g * M_pad + row] = (uint16_t)s_bits;
-    } else {
+    {
       // Round to integer by adding 1.5 * 2^23: the low bits of the sum are the two's
       // complement code (|q| <= 7); the add itself rounds half to even.
       uint32_t w[4];
@@ -193,26 +218,28 @@ k1_quant_int4(const uint16_t* __restrict__ x, int M, int K,
       float v = ured[0][rr][cc];
 #pragma unroll
       for (int w = 1; w < 8; ++w) v += ured[w][rr][cc];
-      if (row0 + rr < M_out) uact[(size_t)(row0 + rr) * rank + cc] = v;
+      if (row0 + rr < M) uact[(size_t)(row0 + rr) * rank + cc] = v;
     }
   }
 }
 
 // fused = false: interchange layout (codes [M][K/2], scales [M][K/64], U [M][r] fp32).
 // fused = true : GEMM layout, M_pad rows (operand chunks of 1536 B per 32-row block
-//                and group, scales [K/64][M_pad], U [M_pad][r] fp32); rows >= M are zero.
+//                and group, scales [K/64][M_pad], partial U [split][M_pad][r] fp32);
+//                rows >= M are zero.
 hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, uint16_t* scales,
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
-  const int M_out = fused ? M_pad : M;
-  dim3 grid((M_out + 15) / 16);
-  if (fused)
-    hipExtLaunchKernelGGL(k1_quant_int4<1>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
-                          ldown, rank, codes, scales, uact, M_out, M_pad);
-  else
-    hipExtLaunchKernelGGL(k1_quant_int4<0>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
-                          ldown, rank, codes, scales, uact, M_out, M_pad);
+  if (fused) {
+    K1Args a{x, M, K, smooth, ldown, rank, codes, scales, uact, M_pad, 1.0f};
+    dim3 grid(M_pad / 16, k1_splits(K));
+    hipExtLaunchKernelGGL(k1_int4_fused, grid, dim3(256), 0, st, ev0, ev1, 0, a);
+  } else {
+    dim3 grid((M + 15) / 16);
+    hipExtLaunchKernelGGL(k1_int4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,
+                          smooth, ldown, rank, codes, scales, uact);
+  }
   return hipGetLastError();
 }
 

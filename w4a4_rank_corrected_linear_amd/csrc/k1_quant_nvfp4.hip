@@ -8,22 +8,22 @@
 // ties to the even code, saturating at 6), sign from the quotient's sign bit; s = 0
 // gives zero codes; U = xhat @ lora_down^T in fp32.
 //
-// Work split as in the int4 quantizer: a 512-thread workgroup owns 16 rows; wave w
-// takes the 128-wide k-blocks kb = w, w+8, ...; lane l holds row l%16 and the 32
-// consecutive values k = 128 kb + 32 q + [0, 32), q = l/16, i.e. two whole NVFP4
-// blocks, so every amax is an in-lane max.
+// As in the int4 quantizer, lane l holds row l%16 and the 32 consecutive values
+// k0 .. k0 + 31 of a 128-wide k-block (k0 = 128 kb + 32 q, q = l/16), i.e. two whole
+// NVFP4 blocks, so every amax is an in-lane max.
 //
-// Outputs: interchange layout (codes [M][K/2] with element 2j in bits 3:0, E4M3
-// scale bytes [M][K/16]), or, for the GEMM, the exact dequantized operand
-// A' = e2m1(code) * s as bf16 [M_pad][K] (|e2m1| has 2 and s 4 significant bits, so
-// the product is exact in bf16); the per-tensor scale g stays out of A' and is
-// applied to the GEMM's fp32 result.
+// Two kernels share the quantizer below: k1_nvfp4_fused (the layer's own path, batch
+// skeleton of k1_batch.h) writes the exact dequantized GEMM operand
+// A' = e2m1(code) * s as bf16 [M_pad][K] (|e2m1| has 2 and s 4 significant bits, so the
+// product is exact in bf16) and partial U per k-split; the per-tensor scale g stays
+// out of A' and is applied to the GEMM's fp32 result.  k1_nvfp4_interchange
+// (svdq_quantize_act) writes codes [M][K/2] (element 2j in bits 3:0), E4M3 scale
+// bytes [M][K/16] and U [M][r].
 #include "common.h"
+#include "k1_batch.h"
 #include "kernels.h"
 
 namespace svdq {
-
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // E4M3 (FN) code of a non-negative float32, round to nearest even, saturating at 448
 // (code 0x7E).  Normal range: round the fp32 significand to 3 bits; below 2^-6 the
@@ -59,17 +59,64 @@ __device__ __forceinline__ float e2m1_value(uint32_t mag) {
   return mag < 4 ? 0.5f * (float)mag : (float)(2u << ((mag - 4u) >> 1)) * (1.0f + 0.5f * (float)(mag & 1u));
 }
 
+// Codes, dequantized values and the two block scales of the lane's 32 values.
+__device__ __forceinline__ void nvfp4_quant32(const float (&xh)[32], float g, uint32_t (&codes)[32],
+                                              float (&deq)[32], uint32_t (&sc)[2]) {
+  const float denom = 6.0f * g;  // fl32(6 g)
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[16 * b + i]));
+    const uint32_t scode = e4m3_code(amax / denom);
+    sc[b] = scode;
+    const float s = e4m3_value(scode);
+    const float d = s * g;  // fl32(s g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float quot = xh[16 * b + i] / d;  // correctly rounded
+      const uint32_t mag = e2m1_mag(fabsf(quot));
+      const uint32_t sign = __float_as_uint(quot) >> 31;
+      const uint32_t c = s > 0.f ? (mag | (sign << 3)) : 0u;
+      codes[16 * b + i] = c;
+      const float v = e2m1_value(c & 7u) * s;  // exact
+      deq[16 * b + i] = (c & 8u) ? -v : v;
+    }
+  }
+}
+
+struct QuantNvfp4Fused {
+  __device__ static void block(const K1Args& a, const float (&xh)[32], int row, int k0, int q) {
+    (void)q;
+    uint32_t codes[32], sc[2];
+    float deq[32];
+    nvfp4_quant32(xh, a.g, codes, deq, sc);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      w[i] = (__float_as_uint(deq[2 * i]) >> 16) | (__float_as_uint(deq[2 * i + 1]) & 0xFFFF0000u);
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)row * a.K + k0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+  }
+};
+
+__global__ void __launch_bounds__(256, 2) k1_nvfp4_fused(K1Args a) { k1_batch<QuantNvfp4Fused>(a); }
+
 struct K1Load {
   uint4 x[4];
   uint4 m[4];
   uint4 l[2][4];
 };
 
-template <int MODE>  // 0: interchange layout, 1: bf16 GEMM operand
+// Interchange kernel: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide
+// k-blocks kb = w, w+8, ... and prefetches the next block's X, smoothing and
+// lora_down operands into registers.  U is summed over the 8 waves in LDS.
 __global__ void __launch_bounds__(512)
-k1_quant_nvfp4(const uint16_t* __restrict__ x, int M, int K, const uint16_t* __restrict__ smooth,
-               const uint16_t* __restrict__ ldown, int rank, float g, uint8_t* __restrict__ out,
-               uint8_t* __restrict__ scales, float* __restrict__ uact, int M_out) {
+k1_nvfp4_interchange(const uint16_t* __restrict__ x, int M, int K,
+                     const uint16_t* __restrict__ smooth, const uint16_t* __restrict__ ldown,
+                     int rank, float g, uint8_t* __restrict__ out, uint8_t* __restrict__ scales,
+                     float* __restrict__ uact) {
   __shared__ float ured[8][16][33];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -79,7 +126,6 @@ k1_quant_nvfp4(const uint16_t* __restrict__ x, int M, int K, const uint16_t* __r
   const int row = row0 + r;
   const bool valid = row < M;
   const int nkb = K >> 7;
-  const float denom = 6.0f * g;  // fl32(6 g)
 
   v4f u0 = {0.f, 0.f, 0.f, 0.f};
   v4f u1 = {0.f, 0.f, 0.f, 0.f};
@@ -130,41 +176,11 @@ k1_quant_nvfp4(const uint16_t* __restrict__ x, int M, int K, const uint16_t* __r
       }
     }
 
-    uint32_t codes[32];
+    uint32_t codes[32], sc[2];
     float deq[32];
-    uint32_t sc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[16 * b + i]));
-      const uint32_t scode = e4m3_code(amax / denom);
-      sc[b] = scode;
-      const float s = e4m3_value(scode);
-      const float d = s * g;  // fl32(s g)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float quot = xh[16 * b + i] / d;  // correctly rounded
-        const uint32_t mag = e2m1_mag(fabsf(quot));
-        const uint32_t sign = __float_as_uint(quot) >> 31;
-        const uint32_t c = s > 0.f ? (mag | (sign << 3)) : 0u;
-        codes[16 * b + i] = c;
-        const float v = e2m1_value(c & 7u) * s;  // exact
-        deq[16 * b + i] = (c & 8u) ? -v : v;
-      }
-    }
+    nvfp4_quant32(xh, g, codes, deq, sc);
 
-    if constexpr (MODE == 1) {
-      if (row < M_out) {
-        uint32_t w[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          w[i] = (__float_as_uint(deq[2 * i]) >> 16) | (__float_as_uint(deq[2 * i + 1]) & 0xFFFF0000u);
-        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (size_t)row * K + k0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dst[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
-      }
-    } else {
+    {
       if (valid) {
         uint32_t w[4];
 #pragma unroll
@@ -207,24 +223,25 @@ k1_quant_nvfp4(const uint16_t* __restrict__ x, int M, int K, const uint16_t* __r
       float v = ured[0][rr][cc];
 #pragma unroll
       for (int w = 1; w < 8; ++w) v += ured[w][rr][cc];
-      if (row0 + rr < M_out) uact[(size_t)(row0 + rr) * rank + cc] = v;
+      if (row0 + rr < M) uact[(size_t)(row0 + rr) * rank + cc] = v;
     }
   }
 }
 
 // fused = false: codes [M][K/2], scales [M][K/16] (E4M3 bytes), U [M][r] fp32.
-// fused = true : A' bf16 [M_pad][K] (rows >= M are zero), U [M_pad][r] fp32.
+// fused = true : A' bf16 [M_pad][K] (rows >= M are zero), partial U [split][M_pad][r].
 hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  const int M_out = fused ? M_pad : M;
-  dim3 grid((M_out + 15) / 16);
-  if (fused)
-    hipExtLaunchKernelGGL(k1_quant_nvfp4<1>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
-                          ldown, rank, g, out, scales, uact, M_out);
-  else
-    hipExtLaunchKernelGGL(k1_quant_nvfp4<0>, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K, smooth,
-                          ldown, rank, g, out, scales, uact, M_out);
+  if (fused) {
+    K1Args a{x, M, K, smooth, ldown, rank, out, scales, uact, M_pad, g};
+    dim3 grid(M_pad / 16, k1_splits(K));
+    hipExtLaunchKernelGGL(k1_nvfp4_fused, grid, dim3(256), 0, st, ev0, ev1, 0, a);
+  } else {
+    dim3 grid((M + 15) / 16);
+    hipExtLaunchKernelGGL(k1_nvfp4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,
+                          smooth, ldown, rank, g, out, scales, uact);
+  }
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@
 namespace svdq {
 
 __global__ void __launch_bounds__(256, 2)
-k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U,
+k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int nsplit,
              const uint16_t* __restrict__ B, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, float g, uint16_t* __restrict__ Y, int M, int N,
              int K, int M_pad, int rank) {
@@ -118,10 +118,15 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U,
 #pragma unroll
       for (int e = 0; e < 16; ++e) c[e] *= g;
       for (int kk = 0; kk < rank; kk += 16) {
-        const float* up = U + (size_t)(rowb + lr) * rank + kk + 8 * lh;
-        const float4 u0 = *reinterpret_cast<const float4*>(up);
-        const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
-        const float uf[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        // U = sum of the quantizer's k-split partials, added in order
+        float uf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < nsplit; ++sp) {
+          const float* up = U + ((size_t)sp * M_pad + rowb + lr) * rank + kk + 8 * lh;
+          const float4 u0 = *reinterpret_cast<const float4*>(up);
+          const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
+          uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w;
+          uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z; uf[7] += u1.w;
+        }
         v8bf hi, lo;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -150,12 +155,12 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U,
   }
 }
 
-hipError_t launch_k2_bf16(const uint16_t* A, const float* U, const uint16_t* B,
+hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
                           const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
                           int N, int K, int M_pad, int rank, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
   dim3 grid((N / 128) * (M_pad / 128));
-  hipExtLaunchKernelGGL(k2_gemm_bf16, grid, dim3(256), 0, st, ev0, ev1, 0, A, U, B, L2t, bias, g,
+  hipExtLaunchKernelGGL(k2_gemm_bf16, grid, dim3(256), 0, st, ev0, ev1, 0, A, U, nsplit, B, L2t, bias, g,
                         Y, M, N, K, M_pad, rank);
   return hipGetLastError();
 }

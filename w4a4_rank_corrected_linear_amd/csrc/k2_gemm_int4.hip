@@ -37,7 +37,7 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 template <int BN>
 __global__ void __launch_bounds__(256, 2)
 k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
-             const float* __restrict__ U, const uint8_t* __restrict__ B,
+             const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
              const uint16_t* __restrict__ sB, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
              int M, int N, int K, int M_pad, int rank) {
@@ -225,10 +225,15 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
       for (int kk = 0; kk < rank; kk += 16) {
         // U is fp32: split into bf16 hi + lo (u - hi is exact in fp32), two MFMAs;
         // what is dropped is below 2^-17 |u|.
-        const float* up = U + (size_t)(rowb + lr) * rank + kk + 8 * lh;
-        const float4 u0 = *reinterpret_cast<const float4*>(up);
-        const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
-        const float uf[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        // U = sum of the quantizer's k-split partials, added in order
+        float uf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < nsplit; ++sp) {
+          const float* up = U + ((size_t)sp * M_pad + rowb + lr) * rank + kk + 8 * lh;
+          const float4 u0 = *reinterpret_cast<const float4*>(up);
+          const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
+          uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w;
+          uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z; uf[7] += u1.w;
+        }
         v8bf hi, lo;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -257,18 +262,18 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   }
 }
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U,
+hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U, int nsplit,
                           const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
                           int rank, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const int BM = 128;
   if (N % 192 == 0) {
     dim3 grid(N / 192, M_pad / BM);
-    hipExtLaunchKernelGGL(k2_gemm_int4<192>, grid, dim3(256), 0, st, ev0, ev1, 0, A, sA, U, B, sB,
+    hipExtLaunchKernelGGL(k2_gemm_int4<192>, grid, dim3(256), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB,
                           L2t, bias, Y, M, N, K, M_pad, rank);
   } else {
     dim3 grid(N / 128, M_pad / BM);
-    hipExtLaunchKernelGGL(k2_gemm_int4<128>, grid, dim3(256), 0, st, ev0, ev1, 0, A, sA, U, B, sB,
+    hipExtLaunchKernelGGL(k2_gemm_int4<128>, grid, dim3(256), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB,
                           L2t, bias, Y, M, N, K, M_pad, rank);
   }
   return hipGetLastError();

@@ -4,6 +4,10 @@
 //       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N].
 //       A -8 code cannot be held by the sign-magnitude E2M3 field: it raises the
 //       range flag, which the host turns into SVDQ_ERR_RANGE.
+// lora_down: [r][K] bf16 -> fragment order of the quantizer's low-rank MFMAs: for
+//       k-block kb (128 values), rank slice sl (16 ranks) and call c (0..3), lane
+//       l = 16 q + i holds lora_down[16 sl + i][128 kb + 32 q + 8 c .. + 8] (16 B), and
+//       the 64 lanes of one (kb, sl, c) are 1 KiB contiguous.
 // nvfp4: codes [N][K/2] E2M1 nibbles and scales [N][K/16] E4M3 bytes -> the exact
 //       dequantized weights e2m1 * s as bf16 [N][K] (2 and 4 significant bits: the
 //       product is a bf16 number).  An E4M3 NaN scale raises the range flag.
@@ -91,6 +95,21 @@ k_pack_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scal
   out[t] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// One thread per 16-byte unit of the packed lora_down.
+__global__ void __launch_bounds__(256)
+k_pack_lora_down(const uint16_t* __restrict__ in, uint4* __restrict__ out, int rank, int K) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nsl = rank / 16;
+  const int64_t total = (int64_t)(K / 128) * nsl * 4 * 64;
+  if (t >= total) return;
+  const int lane = (int)(t & 63), c = (int)((t >> 6) & 3);
+  const int64_t rest = t >> 8;
+  const int sl = (int)(rest % nsl);
+  const int64_t kb = rest / nsl;
+  const int i = lane & 15, q = lane >> 4;
+  out[t] = *reinterpret_cast<const uint4*>(in + (int64_t)(16 * sl + i) * K + 128 * kb + 32 * q + 8 * c);
+}
+
 __global__ void k_zero_flag(int* flag) { *flag = 0; }
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
@@ -107,6 +126,13 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
 }
 
 
+
+hipError_t launch_pack_lora_down(const uint16_t* in, uint16_t* out, int rank, int K, hipStream_t st) {
+  const int64_t total = (int64_t)(K / 128) * (rank / 16) * 4 * 64;
+  hipLaunchKernelGGL(k_pack_lora_down, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, in,
+                     reinterpret_cast<uint4*>(out), rank, K);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
                              int N, int K, hipStream_t st) {

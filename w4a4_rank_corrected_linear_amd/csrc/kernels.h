@@ -10,12 +10,18 @@
 
 namespace svdq {
 
+// The fused quantizers split K into pieces of at most kK1SplitK values, one
+// workgroup column each; each piece writes its own partial U [M_pad][r] and the GEMM
+// epilogue adds the pieces in order.
+constexpr int kK1SplitK = 1536;
+inline int k1_splits(int K) { return (K + kK1SplitK - 1) / kK1SplitK; }
+
 hipError_t launch_k1_int4(bool compact, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, uint16_t* scales,
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U,
+hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U, int nsplit,
                           const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
                           int rank, hipStream_t st, hipEvent_t ev0 = nullptr,
@@ -26,7 +32,7 @@ hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const ui
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                            hipEvent_t ev1 = nullptr);
 
-hipError_t launch_k2_bf16(const uint16_t* A, const float* U, const uint16_t* B,
+hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
                           const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
                           int N, int K, int M_pad, int rank, hipStream_t st,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
@@ -34,6 +40,8 @@ hipError_t launch_k2_bf16(const uint16_t* A, const float* U, const uint16_t* B,
 hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc, const uint8_t* Z,
                          const uint16_t* bias, uint16_t* Y, int M, int N, int K, hipStream_t st,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
+hipError_t launch_pack_lora_down(const uint16_t* in, uint16_t* out, int rank, int K, hipStream_t st);
 
 hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
                              int N, int K, hipStream_t st);

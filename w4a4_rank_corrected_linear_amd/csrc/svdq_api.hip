@@ -124,7 +124,8 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   const bool nv = c->precision == SVDQ_NVFP4;
   const size_t codes = nv ? (size_t)(L.M_pad * K * 2) : (size_t)(L.M_pad * K * 3 / 4);
   const size_t scales = nv ? 0 : (size_t)(G * L.M_pad * 2);
-  const size_t lora = (size_t)(L.M_pad * c->rank * 4);  // fp32 U
+  // fp32 partial U per k-split of the quantizer
+  const size_t lora = (size_t)(svdq::k1_splits((int)K) * L.M_pad * c->rank * 4);
   L.codes = 0;
   L.scales = (size_t)round_up((int64_t)codes, 256);
   L.lora = L.scales + (size_t)round_up((int64_t)scales, 256);
@@ -249,6 +250,20 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
   return ok();
 }
 
+svdq_status svdq_pack_lora_down(const svdq_config* cfg, int64_t K, const uint16_t* lora_down,
+                                uint16_t* packed, hipStream_t stream) {
+  if (!cfg || !lora_down || !packed) return fail(SVDQ_ERR_NULL, "svdq_pack_lora_down: NULL argument");
+  SVDQ_TRY(check_svdq_config(cfg));
+  if (cfg->rank == 0) return fail(SVDQ_ERR_CONFIG, "svdq_pack_lora_down: rank 0 has no lora_down");
+  SVDQ_TRY(check_k(K));
+  if (!aligned16(lora_down) || !aligned16(packed))
+    return fail(SVDQ_ERR_ALIGN, "svdq_pack_lora_down: pointers must be 16-byte aligned");
+  SVDQ_TRY(check_current_device());
+  SVDQ_TRY(hip_check(svdq::launch_pack_lora_down(lora_down, packed, cfg->rank, (int)K, stream),
+                     "pack kernel launch"));
+  return ok();
+}
+
 size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K) {
   if (!cfg || check_svdq_config(cfg) != SVDQ_OK || check_k(K) != SVDQ_OK || check_m(M, K) != SVDQ_OK)
     return 0;
@@ -331,6 +346,7 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
     const EvPair e2 = timer_kernel();
     const float g = act_global * w->w_global;
     SVDQ_TRY(hip_check(svdq::launch_k2_bf16(reinterpret_cast<const uint16_t*>(a_codes), a_lora,
+                                             svdq::k1_splits((int)w->K),
                                              reinterpret_cast<const uint16_t*>(w->qweight),
                                              w->lora_up, w->bias, g, y, (int)M, (int)w->N,
                                              (int)w->K, (int)L.M_pad, cfg->rank, stream, e2.start,
@@ -344,7 +360,8 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
                                            stream, e1.start, e1.end),
                      "quantize kernel launch"));
   const EvPair e2 = timer_kernel();
-  SVDQ_TRY(hip_check(svdq::launch_k2_int4(a_codes, a_scales, a_lora, w->qweight,
+  SVDQ_TRY(hip_check(svdq::launch_k2_int4(a_codes, a_scales, a_lora, svdq::k1_splits((int)w->K),
+                                           w->qweight,
                                            static_cast<const uint16_t*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
                                            cfg->rank, stream, e2.start, e2.end),
