@@ -97,7 +97,11 @@ typedef struct {
 svdq_status svdq_check_device(int hip_device);
 
 /* Bytes of the packed weight buffers for a K x N svdq_w4a4 layer (0 on bad
- * config or shape).  *codes_bytes and *scales_bytes receive the two parts. */
+ * config or shape).  *codes_bytes and *scales_bytes receive the two parts:
+ *   int4:  codes N*K*3/4 (E2M3 lane slots, 6 bits per weight: the layout the GEMM's
+ *          FP6 MFMA reads, chunks of 1536 bytes per 32 output columns and 64-group),
+ *          scales round_up(K/64 * N * 2, 256) + 256 ([K/64][N] bf16, range flag)
+ *   nvfp4: codes N*K*2 (exact dequantized bf16 [N][K]), scales 256 (range flag) */
 size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
                                 size_t* codes_bytes, size_t* scales_bytes);
 

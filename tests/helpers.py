@@ -8,9 +8,6 @@ import numpy as np
 
 from oracle import formats as F
 
-Z0 = 0x18618618
-Z2 = 0x61861861
-
 
 def dev_bf16(bits: np.ndarray):
     import torch
@@ -66,35 +63,6 @@ def check_u(u: np.ndarray, ref: dict, lora_down_bits: np.ndarray, chain: int | N
     bound = chain * 2.0 ** -24 * (xh @ ld.T)
     err = np.abs(np.asarray(u, dtype=np.float64) - ref["lora_act"])
     assert np.all(err <= bound), float((err / np.maximum(bound, 1e-300)).max())
-
-
-def decode_compact_int4(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
-    """Kernel-layout int4 codes (compact E2M3 runs) -> signed codes [rows_pad, K].
-
-    Layout: ((row // 32) * G + g) * 1024 + h * 512 + (row % 32) * 16 + 8 p bytes hold
-    the run (x0, x1) of k = 64 g + 32 h + 16 p + j, j = 0..15.
-    """
-    G = K // 64
-    w = np.asarray(buf, dtype=np.uint8)[: rows_pad * K // 2].view(np.uint32)
-    w = w.reshape(rows_pad // 32, G, 2, 32, 2, 2).astype(np.uint64)   # rb, g, h, r, p, (x0,x1)
-    x0, x1 = w[..., 0], w[..., 1]
-    o0 = x0 & (~Z0 & 0xFFFFFFFF)
-    o2 = x1 & (~Z2 & 0xFFFFFFFF)
-    o1 = (x0 & Z0) | (x1 & Z2)
-    out = np.zeros(o0.shape + (16,), dtype=np.int64)
-    for j in range(16):
-        pos = 6 * j
-        f = np.zeros(o0.shape, dtype=np.uint64)
-        for b in range(6):
-            p = pos + b
-            src = o0 if p < 32 else (o1 if p < 64 else o2)
-            f |= ((src >> np.uint64(p % 32)) & np.uint64(1)) << np.uint64(b)
-        mag = (f & np.uint64(7)).astype(np.int64)
-        assert np.all((f & np.uint64(0x18)) == 0), "exponent bits set in an int4 field"
-        out[..., j] = np.where(f & np.uint64(0x20), -mag, mag)
-    # axes: rb, g, h, r, p, j -> row = rb*32 + r, k = 64 g + 32 h + 16 p + j
-    out = out.transpose(0, 3, 1, 2, 4, 5).reshape(rows_pad, K)
-    return out
 
 
 def int4_interchange(q: np.ndarray) -> np.ndarray:

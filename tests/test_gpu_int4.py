@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import w4a4_rank_corrected_linear_amd as svdq
-from helpers import (check_u, check_y, decode_compact_int4, decode_fp6_operand, dev_bf16,
+from helpers import (check_u, check_y, decode_fp6_operand, dev_bf16,
                      dev_u8, host_bits, int4_interchange)
 from oracle import formats as F
 from oracle import linear as OL
@@ -81,7 +81,7 @@ def test_quantize_act_ties_and_zero_groups():
 def test_pack_weight_layout(tiny):
     _, layer = tiny
     pc, ps = svdq.pack_weight(dev_u8(layer.qweight), dev_bf16(layer.wscales))
-    q = decode_compact_int4(host_bits(pc), layer.N, layer.K)
+    q = decode_fp6_operand(host_bits(pc), layer.N, layer.K)
     assert np.array_equal(q, F.int4_decode(F.unpack_nibbles(layer.qweight)))
     G = layer.K // 64
     st = host_bits(ps)[: G * layer.N * 2].view(np.uint16).reshape(G, layer.N)
@@ -241,7 +241,7 @@ def test_workspace_with_three_k_splits():
     torch.cuda.synchronize()
     ref = Q.quantize_act_int4(x, m, ld)
     w = host_bits(ws)
-    M_pad, G, nsplit = 128, K // 64, 3
+    M_pad, G, nsplit = 256, K // 64, 3
     assert np.array_equal(decode_fp6_operand(w, M_pad, K)[:M], ref["q"])
     off_s = M_pad * K * 3 // 4
     s = w[off_s: off_s + G * M_pad * 2].view(np.uint16).reshape(G, M_pad)

@@ -1,6 +1,6 @@
 // Weight packing: interchange layout -> kernel layout (an offline step).
 //
-// int4: codes [N][K/2] two's complement nibbles -> compact E2M3 layout of common.h
+// int4: codes [N][K/2] two's complement nibbles -> E2M3 lane slots of common.h
 //       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N].
 //       A -8 code cannot be held by the sign-magnitude E2M3 field: it raises the
 //       range flag, which the host turns into SVDQ_ERR_RANGE.
@@ -16,42 +16,38 @@
 
 namespace svdq {
 
-// One thread per (row-block, group, half, row % 32): reads the 16 interchange bytes
-// of 32 codes and writes the 16 compact bytes of the same 32 codes.
+// One thread per (row-block, group, lane slot h*32 + row % 32): reads the 16
+// interchange bytes of 32 codes and writes their six dwords of E2M3 fields.
 __global__ void __launch_bounds__(256)
-k_pack_int4_codes(const uint8_t* __restrict__ codes, uint4* __restrict__ out, int N, int K,
+k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int N, int K,
                   int* __restrict__ flag) {
   const int G = K >> 6;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)N * G * 2;
   if (t >= total) return;
-  const int r = (int)(t & 31);
-  const int h = (int)((t >> 5) & 1);
+  const int slot = (int)(t & 63);
+  const int r = slot & 31, h = slot >> 5;
   const int64_t rest = t >> 6;         // (row-block, group)
   const int g = (int)(rest % G);
   const int64_t rb = rest / G;
   const int64_t n = rb * 32 + r;
   const uint4 v = *reinterpret_cast<const uint4*>(codes + n * (K >> 1) + 32 * g + 16 * h);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t outw[4];
+  uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
   bool bad = false;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    uint32_t t0 = 0, t1 = 0, t2 = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t nib = (w[2 * p + (j >> 3)] >> (4 * (j & 7))) & 0xFu;
-      const int q = (nib & 8u) ? (int)nib - 16 : (int)nib;
-      bad |= (q == -8);
-      const uint32_t f = e2m3_field(q < -7 ? -7 : q);
-      const int pos = 6 * j;
-      if (pos < 32) t0 |= f << pos;
-      if (pos + 6 > 32 && pos < 64) t1 |= (pos >= 32) ? (f << (pos - 32)) : (f >> (32 - pos));
-      if (pos + 6 > 64) t2 |= (pos >= 64) ? (f << (pos - 64)) : (f >> (64 - pos));
-    }
-    fp6_compact(t0, t1, t2, outw[2 * p], outw[2 * p + 1]);
+  for (int f = 0; f < 32; ++f) {
+    const uint32_t nib = (w[f >> 3] >> (4 * (f & 7))) & 0xFu;
+    const int q = (nib & 8u) ? (int)nib - 16 : (int)nib;
+    bad |= (q == -8);
+    const uint32_t fld = e2m3_field(q < -7 ? -7 : q);
+    const int pos = 6 * f, word = pos >> 5, bit = pos & 31;
+    o[word] |= fld << bit;
+    if (bit > 26) o[word + 1] |= fld >> (32 - bit);
   }
-  out[t] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  uint8_t* chunk = out + (size_t)rest * 1536;
+  *reinterpret_cast<uint4*>(chunk + slot * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint2*>(chunk + 1024 + slot * 8) = make_uint2(o[4], o[5]);
   if (bad) atomicOr(flag, 1);
 }
 
@@ -118,7 +114,7 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
   hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
   const int64_t total = (int64_t)N * G * 2;
   hipLaunchKernelGGL(k_pack_int4_codes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     codes, reinterpret_cast<uint4*>(out_codes), N, K, flag);
+                     codes, out_codes, N, K, flag);
   const int64_t ts = (int64_t)N * G;
   hipLaunchKernelGGL(k_transpose_scales_u16, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
                      scales, out_scales, N, G);

@@ -16,7 +16,7 @@ namespace svdq {
 constexpr int kK1SplitK = 1536;
 inline int k1_splits(int K) { return (K + kK1SplitK - 1) / kK1SplitK; }
 
-hipError_t launch_k1_int4(bool compact, const uint16_t* x, int M, int K, const uint16_t* smooth,
+hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, uint16_t* scales,
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);

@@ -117,11 +117,12 @@ struct WsLayout {
 
 WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   WsLayout L;
-  L.M_pad = round_up(M, 128);
-  const int64_t G = K / c->group_size;
-  // int4: GEMM A operand as E2M3 fields, 6 bits per value (3/4 byte), bf16 scales
-  // [G][M_pad]; nvfp4: the exact dequantized operand in bf16 [M_pad][K], no scales
   const bool nv = c->precision == SVDQ_NVFP4;
+  // row padding to the GEMM's row tile: 256 (int4), 128 (nvfp4)
+  L.M_pad = round_up(M, nv ? 128 : 256);
+  const int64_t G = K / c->group_size;
+  // int4: GEMM A operand as E2M3 lane slots, 6 bits per value (3/4 byte), bf16 scales
+  // [G][M_pad]; nvfp4: the exact dequantized operand in bf16 [M_pad][K], no scales
   const size_t codes = nv ? (size_t)(L.M_pad * K * 2) : (size_t)(L.M_pad * K * 3 / 4);
   const size_t scales = nv ? 0 : (size_t)(G * L.M_pad * 2);
   // fp32 partial U per k-split of the quantizer
@@ -204,10 +205,10 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N, si
     return 0;
   }
   const int64_t G = K / cfg->group_size;
-  // int4: compact codes (1/2 byte per weight) and [G][N] bf16 scales; nvfp4: exact
+  // int4: E2M3 lane slots (3/4 byte per weight) and [G][N] bf16 scales; nvfp4: exact
   // dequantized bf16 weights [N][K]; both with a 256-byte range-flag trailer
   const bool nv = cfg->precision == SVDQ_NVFP4;
-  const size_t cb = nv ? (size_t)(N * K * 2) : (size_t)(N * K / 2);
+  const size_t cb = nv ? (size_t)(N * K * 2) : (size_t)(N * K * 3 / 4);
   const size_t sb = nv ? 256 : (size_t)round_up(G * N * 2, 256) + 256;
   if (codes_bytes) *codes_bytes = cb;
   if (scales_bytes) *scales_bytes = sb;
