@@ -278,7 +278,12 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
       for (int j = 0; j < WN; ++j) asm volatile("" : "+v"(acc[i][j]));
   }
 
-  // Epilogue: + bias, round to bf16, 8-byte stores of four consecutive columns.
+  // Epilogue: + bias, round to bf16.  Each wave stages its 64 x BN/2 tile in LDS (the
+  // ring is free once every wave has passed the barrier) and writes Y in 16-byte
+  // pieces, BN/16 consecutive lanes per row, so every row segment of the tile is one
+  // contiguous run of full 64-byte sectors.
+  barrier_lds();
+  uint16_t* tile = reinterpret_cast<uint16_t*>(ring) + wave * (64 * (BN / 2 + 8));
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const int colb = col0 + (wn * WN + j) * 32;
@@ -294,18 +299,24 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int rowm = row0 + wm * 64 + 32 * i + lr;
-      if (rowm < M) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t h[4];
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) h[p] = f32_to_bf16_rne(acc[i][j][4 * q + p] + bv[4 * q + p]);
-          *reinterpret_cast<uint2*>(Y + (size_t)rowm * N + colb + 8 * q + 4 * lh) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        }
+        for (int p = 0; p < 4; ++p) h[p] = f32_to_bf16_rne(acc[i][j][4 * q + p] + bv[4 * q + p]);
+        *reinterpret_cast<uint2*>(tile + (32 * i + lr) * (BN / 2 + 8) + 32 * j + 8 * q + 4 * lh) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
     }
+  }
+  constexpr int CPR = BN / 16;  // 16-byte pieces per staged row
+#pragma unroll
+  for (int r = 0; r < CPR; ++r) {
+    const int c = lane + 64 * r;
+    const int row = c / CPR, ch = c % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + row * (BN / 2 + 8) + ch * 8);
+    const int grow = row0 + wm * 64 + row;
+    if (grow < M) *reinterpret_cast<uint4*>(Y + (size_t)grow * N + col0 + wn * (BN / 2) + ch * 8) = v;
   }
 }
 
