@@ -65,6 +65,14 @@ def check_u(u: np.ndarray, ref: dict, lora_down_bits: np.ndarray, chain: int | N
     assert np.all(err <= bound), float((err / np.maximum(bound, 1e-300)).max())
 
 
+def scale_records(buf: np.ndarray, groups: int, rows: int) -> np.ndarray:
+    """Kernel-layout scale records [groups][rows] of 8 bytes {bf16 s, 0, 0, 0} -> s bits
+    [groups, rows]; asserts the zero padding."""
+    rec = np.asarray(buf, dtype=np.uint8)[: groups * rows * 8].view(np.uint16).reshape(groups, rows, 4)
+    assert np.all(rec[..., 1:] == 0), "nonzero padding in a scale record"
+    return rec[..., 0]
+
+
 def int4_interchange(q: np.ndarray) -> np.ndarray:
     return F.pack_nibbles(F.int4_encode(q))
 

@@ -92,10 +92,10 @@ def test_alignment():
 def test_workspace_size_and_check():
     lib = L.lib()
     need = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 100, 512)
-    # M padded to 256 rows: operand 256*512*3/4, scales 8*256*2, U 1 split x 256*32 fp32
-    assert need == 98304 + 4096 + 32768
+    # M padded to 256 rows: operand 256*512*3/4, scale records 8*256*8, U 1 split x 256*32 fp32
+    assert need == 98304 + 16384 + 32768
     assert linear(cfg(), weight(), M=100, ws_bytes=need - 1) == L.ERR_WORKSPACE
-    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 4096
+    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 16384
 
 
 def test_packed_weight_bytes():
@@ -103,7 +103,7 @@ def test_packed_weight_bytes():
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     tot = lib.svdq_packed_weight_bytes(ctypes.byref(cfg()), 3072, 3072, ctypes.byref(cb), ctypes.byref(sb))
     assert cb.value == 3072 * 3072 * 3 // 4      # E2M3 lane slots, 6 bits per weight
-    assert sb.value == 48 * 3072 * 2 + 256
+    assert sb.value == 48 * 3072 * 8 + 256     # 8-byte scale records + range flag
     assert tot == cb.value + sb.value
 
 

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import w4a4_rank_corrected_linear_amd as svdq
-from helpers import (check_u, check_y, decode_fp6_operand, dev_bf16,
+from helpers import (check_u, check_y, decode_fp6_operand, dev_bf16, scale_records,
                      dev_u8, host_bits, int4_interchange)
 from oracle import formats as F
 from oracle import linear as OL
@@ -84,7 +84,7 @@ def test_pack_weight_layout(tiny):
     q = decode_fp6_operand(host_bits(pc), layer.N, layer.K)
     assert np.array_equal(q, F.int4_decode(F.unpack_nibbles(layer.qweight)))
     G = layer.K // 64
-    st = host_bits(ps)[: G * layer.N * 2].view(np.uint16).reshape(G, layer.N)
+    st = scale_records(host_bits(ps), G, layer.N)
     assert np.array_equal(st, layer.wscales.T)
 
 
@@ -150,9 +150,9 @@ def test_workspace_matches_standalone_quantize(tiny):
     assert np.array_equal(q[:M], ref["q"])
     assert np.all(q[M:] == 0)
     off_s = M_pad * K * 3 // 4
-    s = w[off_s: off_s + G * M_pad * 2].view(np.uint16).reshape(G, M_pad)
+    s = scale_records(w[off_s:], G, M_pad)
     assert np.array_equal(s[:, :M], ref["scales"].T)
-    off_u = off_s + G * M_pad * 2
+    off_u = off_s + G * M_pad * 8
     u = w[off_u: off_u + M_pad * 32 * 4].view(np.float32).reshape(M_pad, 32)
     check_u(u[:M], ref, layer.lora_down)
     assert np.all(u[M:] == 0)
@@ -244,9 +244,9 @@ def test_workspace_with_three_k_splits():
     M_pad, G, nsplit = 256, K // 64, 3
     assert np.array_equal(decode_fp6_operand(w, M_pad, K)[:M], ref["q"])
     off_s = M_pad * K * 3 // 4
-    s = w[off_s: off_s + G * M_pad * 2].view(np.uint16).reshape(G, M_pad)
+    s = scale_records(w[off_s:], G, M_pad)
     assert np.array_equal(s[:, :M], ref["scales"].T)
-    off_u = off_s + -(-G * M_pad * 2 // 256) * 256
+    off_u = off_s + -(-G * M_pad * 8 // 256) * 256
     u = w[off_u: off_u + nsplit * M_pad * r * 4].view(np.float32).reshape(nsplit, M_pad, r)
     check_u(u.astype(np.float64).sum(axis=0)[:M], ref, ld)
     check_y(host_bits(y), OL.w4a4_linear("int4", x, layer)["r"])

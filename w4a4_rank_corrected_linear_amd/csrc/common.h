@@ -15,7 +15,9 @@
 // k = 64 g + 32 h + f, f = 0..31, field f in bits 6f..6f+5 of six dwords; dwords
 // 0-3 sit at chunk + 16 l and dwords 4-5 at chunk + 1024 + 8 l, so a 64-lane
 // 16-byte and a 64-lane 8-byte access read one whole operand.
-// Per-group scales sit group-major: scales[g * R_pad + row] (bf16).
+// Per-group scales sit group-major as 8-byte records: record g * R_pad + row holds
+// the bf16 scale in bits 15:0 and zeros above.  A 64-bit load of a record is
+// directly the bf16x4 operand {s, 0, 0, 0} of the rescale MFMA.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -23,7 +23,8 @@
 // in a 3-slot LDS ring; slot s%3 holds stage s:
 //   A   [row-block 0..7][group 0..1][1536 B]  activation lane slots (written by K1)
 //   B   [col-block][group 0..1][1536 B]       weight lane slots (written by the pack)
-//   SA  [group][256 rows] bf16, SB [group][BN cols] bf16
+//   SA  [group][256 rows], SB [group][BN cols]: 8-byte scale records (common.h), so
+//       each rescale operand is one 64-bit LDS load with no VALU work
 // all copied by LDS DMA (global_load_lds_dwordx4, 16 B per lane).  At the top of
 // iteration t every wave waits for its own copies of stage t+1, the barrier publishes
 // them and frees slot (t+2)%3, and the copies of stage t+2 start.  The twelve (or
@@ -72,9 +73,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 template <int BN>
 __global__ void __launch_bounds__(512, 1)
-k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
+k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
              const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
-             const uint16_t* __restrict__ sB, const uint16_t* __restrict__ L2t,
+             const uint2* __restrict__ sB, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
              int M, int N, int K, int M_pad, int rank) {
   constexpr int BM = 256;
@@ -82,7 +83,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   constexpr int CB = BN / 32;              // 32-column blocks per tile
   constexpr int ASZ = 8 * 2 * 384;         // dwords of A per stage
   constexpr int BSZ = CB * 2 * 384;        // dwords of B per stage
-  constexpr int SLOT = ASZ + BSZ + (2 * BM + 2 * BN) / 2;
+  constexpr int SLOT = ASZ + BSZ + (2 * BM + 2 * BN) * 2;
   constexpr int NB = 4 * WN;               // blocks per wave and stage
   constexpr int NBS = (WN == 3) ? 3 : 4;   // B register sets (divides 2 WN fragments)
   static_assert(WN == 2 || WN == 3, "tile width 128 or 192");
@@ -111,17 +112,13 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
 
   auto slotA = [&](int sl) { return ring + sl * SLOT; };
   auto slotB = [&](int sl) { return ring + sl * SLOT + ASZ; };
-  auto slotSA = [&](int sl) { return reinterpret_cast<uint16_t*>(ring + sl * SLOT + ASZ + BSZ); };
-  auto slotSB = [&](int sl) {
-    return reinterpret_cast<uint16_t*>(ring + sl * SLOT + ASZ + BSZ) + 2 * BM;
-  };
+  auto slotSA = [&](int sl) { return reinterpret_cast<uint2*>(ring + sl * SLOT + ASZ + BSZ); };
+  auto slotSB = [&](int sl) { return reinterpret_cast<uint2*>(ring + sl * SLOT + ASZ + BSZ) + 2 * BM; };
 
   // Copies of stage s: wave w copies A row-block w (3 KiB: both groups); waves below
-  // CB copy B col-block w; wave CB the row scales (1 KiB), wave CB+1 the column
-  // scales (BN/4 lanes).
+  // CB copy B col-block w; wave CB the row scale records (2 x 2 KiB), wave CB+1 the
+  // column scale records (2 x BN * 8 bytes).  A 64-lane copy moves 128 records.
   const uint32_t voff = lane * 16;
-  const uint32_t voffSA = (lane >> 5) * M_pad * 2 + (lane & 31) * 16;
-  const uint32_t voffSB = (lane / (BN / 8)) * N * 2 + (lane % (BN / 8)) * 16;
   auto dma = [&](int s, int sl) {
     {
       const uint8_t* src = A + ((size_t)(rb0 + wave) * G + 2 * s) * 1536;
@@ -135,9 +132,20 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
 #pragma unroll
       for (int t = 0; t < 3; ++t) dma16(voff, src + t * 1024, dst + t * 1024);
     } else if (wave == CB) {
-      dma16(voffSA, sA + (size_t)(2 * s) * M_pad + row0, lds_addr(slotSA(sl)));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int gl = t >> 1, part = t & 1;
+        dma16(voff, sA + (size_t)(2 * s + gl) * M_pad + row0 + 128 * part,
+              lds_addr(slotSA(sl) + gl * BM + 128 * part));
+      }
     } else if (wave == CB + 1) {
-      if (lane < BN / 4) dma16(voffSB, sB + (size_t)(2 * s) * N + col0, lds_addr(slotSB(sl)));
+#pragma unroll
+      for (int gl = 0; gl < 2; ++gl) {
+        const uint2* src = sB + (size_t)(2 * s + gl) * N + col0;
+        const uint32_t dst = lds_addr(slotSB(sl) + gl * BN);
+        dma16(voff, src, dst);
+        if (BN > 128 && lane < (BN - 128) / 2) dma16(voff, src + 128, dst + 1024);
+      }
     }
   };
 
@@ -200,17 +208,17 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   v2i fsa[2][2], fsb[NBS];
   auto loadA = [&](int set, int sl, int gl) {
     const uint32_t* Ab = slotA(sl);
-    const uint16_t* SAb = slotSA(sl);
+    const uint2* SAb = slotSA(sl);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       fa[set][i] = frag(Ab + ((wm * 2 + i) * 2 + gl) * 384);
-      fsa[set][i] = v2i{(int)SAb[gl * BM + wm * 64 + 32 * i + lr], 0};
+      fsa[set][i] = *reinterpret_cast<const v2i*>(SAb + gl * BM + wm * 64 + 32 * i + lr);
     }
   };
   auto loadB = [&](int k, int sl) {
     const int gl = k / WN, j = k % WN;
     fb[k % NBS] = frag(slotB(sl) + ((wn * WN + j) * 2 + gl) * 384);
-    fsb[k % NBS] = v2i{(int)slotSB(sl)[gl * BN + (wn * WN + j) * 32 + lr], 0};
+    fsb[k % NBS] = *reinterpret_cast<const v2i*>(slotSB(sl) + gl * BN + (wn * WN + j) * 32 + lr);
   };
   v16f d[2], sc[2];
   // block b of a stage: group b / (2 WN), column block (b % (2 WN)) / 2, row block b % 2
@@ -249,6 +257,12 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
     }
     if (b == 0) loadA(1, sl, 1);
     if (b == NB / 2 && next) loadA(0, nsl, 0);
+    // issue order within the step: D, the fragment loads, half the FMAs, S, the rest
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -320,8 +334,8 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   }
 }
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U, int nsplit,
-                          const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
+hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
+                          const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
                           int rank, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (M_pad % 256 != 0 || N % 128 != 0 || K % 128 != 0) return hipErrorInvalidValue;

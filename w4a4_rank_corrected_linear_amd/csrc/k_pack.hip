@@ -1,7 +1,8 @@
 // Weight packing: interchange layout -> kernel layout (an offline step).
 //
 // int4: codes [N][K/2] two's complement nibbles -> E2M3 lane slots of common.h
-//       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N].
+//       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N]
+//       8-byte records {s, 0, 0, 0} (common.h).
 //       A -8 code cannot be held by the sign-magnitude E2M3 field: it raises the
 //       range flag, which the host turns into SVDQ_ERR_RANGE.
 // lora_down: [r][K] bf16 -> fragment order of the quantizer's low-rank MFMAs: for
@@ -52,11 +53,11 @@ k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, 
 }
 
 __global__ void __launch_bounds__(256)
-k_transpose_scales_u16(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int N, int G) {
+k_transpose_scales(const uint16_t* __restrict__ in, uint2* __restrict__ out, int N, int G) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= (int64_t)N * G) return;
   const int64_t g = t / N, n = t % N;
-  out[t] = in[n * G + g];
+  out[t] = make_uint2(in[n * G + g], 0u);
 }
 
 // One thread per 8 weights (4 code bytes, one E4M3 scale).
@@ -109,15 +110,15 @@ k_pack_lora_down(const uint16_t* __restrict__ in, uint4* __restrict__ out, int r
 __global__ void k_zero_flag(int* flag) { *flag = 0; }
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
-                            uint16_t* out_scales, int* flag, int N, int K, hipStream_t st) {
+                            void* out_scales, int* flag, int N, int K, hipStream_t st) {
   const int G = K >> 6;
   hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
   const int64_t total = (int64_t)N * G * 2;
   hipLaunchKernelGGL(k_pack_int4_codes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
                      codes, out_codes, N, K, flag);
   const int64_t ts = (int64_t)N * G;
-  hipLaunchKernelGGL(k_transpose_scales_u16, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
-                     scales, out_scales, N, G);
+  hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
+                     scales, reinterpret_cast<uint2*>(out_scales), N, G);
   return hipGetLastError();
 }
 

@@ -17,12 +17,12 @@ constexpr int kK1SplitK = 1536;
 inline int k1_splits(int K) { return (K + kK1SplitK - 1) / kK1SplitK; }
 
 hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
-                          const uint16_t* ldown, int rank, uint8_t* codes, uint16_t* scales,
+                          const uint16_t* ldown, int rank, uint8_t* codes, void* scales,
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint16_t* sA, const float* U, int nsplit,
-                          const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
+hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
+                          const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
                           int rank, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
@@ -47,6 +47,6 @@ hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16
                              int N, int K, hipStream_t st);
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
-                            uint16_t* out_scales, int* flag, int N, int K, hipStream_t st);
+                            void* out_scales, int* flag, int N, int K, hipStream_t st);
 
 }  // namespace svdq

@@ -121,10 +121,11 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   // row padding to the GEMM's row tile: 256 (int4), 128 (nvfp4)
   L.M_pad = round_up(M, nv ? 128 : 256);
   const int64_t G = K / c->group_size;
-  // int4: GEMM A operand as E2M3 lane slots, 6 bits per value (3/4 byte), bf16 scales
-  // [G][M_pad]; nvfp4: the exact dequantized operand in bf16 [M_pad][K], no scales
+  // int4: GEMM A operand as E2M3 lane slots, 6 bits per value (3/4 byte), scale
+  // records [G][M_pad] (8 bytes); nvfp4: the exact dequantized operand in bf16
+  // [M_pad][K], no scales
   const size_t codes = nv ? (size_t)(L.M_pad * K * 2) : (size_t)(L.M_pad * K * 3 / 4);
-  const size_t scales = nv ? 0 : (size_t)(G * L.M_pad * 2);
+  const size_t scales = nv ? 0 : (size_t)(G * L.M_pad * 8);
   // fp32 partial U per k-split of the quantizer
   const size_t lora = (size_t)(svdq::k1_splits((int)K) * L.M_pad * c->rank * 4);
   L.codes = 0;
@@ -205,11 +206,12 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N, si
     return 0;
   }
   const int64_t G = K / cfg->group_size;
-  // int4: E2M3 lane slots (3/4 byte per weight) and [G][N] bf16 scales; nvfp4: exact
-  // dequantized bf16 weights [N][K]; both with a 256-byte range-flag trailer
+  // int4: E2M3 lane slots (3/4 byte per weight) and [G][N] 8-byte scale records;
+  // nvfp4: exact dequantized bf16 weights [N][K]; both with a 256-byte range-flag
+  // trailer
   const bool nv = cfg->precision == SVDQ_NVFP4;
   const size_t cb = nv ? (size_t)(N * K * 2) : (size_t)(N * K * 3 / 4);
-  const size_t sb = nv ? 256 : (size_t)round_up(G * N * 2, 256) + 256;
+  const size_t sb = nv ? 256 : (size_t)round_up(G * N * 8, 256) + 256;
   if (codes_bytes) *codes_bytes = cb;
   if (scales_bytes) *scales_bytes = sb;
   return cb + sb;
@@ -229,7 +231,7 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
   const int64_t G = K / cfg->group_size;
   const bool nv = cfg->precision == SVDQ_NVFP4;
   int* flag = reinterpret_cast<int*>(static_cast<uint8_t*>(packed_scales) +
-                                     (nv ? 0 : round_up(G * N * 2, 256)));
+                                     (nv ? 0 : round_up(G * N * 8, 256)));
   if (nv)
     SVDQ_TRY(hip_check(svdq::launch_pack_nvfp4(codes, static_cast<const uint8_t*>(scales),
                                                 reinterpret_cast<uint16_t*>(packed_codes), flag,
@@ -237,7 +239,7 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
                        "pack kernel launch"));
   else
     SVDQ_TRY(hip_check(svdq::launch_pack_int4(codes, static_cast<const uint16_t*>(scales),
-                                               packed_codes, static_cast<uint16_t*>(packed_scales),
+                                               packed_codes, packed_scales,
                                                flag, (int)N, (int)K, stream),
                        "pack kernel launch"));
   int host_flag = 0;
@@ -333,7 +335,7 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
   SVDQ_TRY(check_current_device());
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* a_codes = ws + L.codes;
-  uint16_t* a_scales = reinterpret_cast<uint16_t*>(ws + L.scales);
+  uint2* a_scales = reinterpret_cast<uint2*>(ws + L.scales);
   float* a_lora = reinterpret_cast<float*>(ws + L.lora);
   timer_begin_call();
   const EvPair e1 = timer_kernel();
@@ -363,7 +365,7 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
   const EvPair e2 = timer_kernel();
   SVDQ_TRY(hip_check(svdq::launch_k2_int4(a_codes, a_scales, a_lora, svdq::k1_splits((int)w->K),
                                            w->qweight,
-                                           static_cast<const uint16_t*>(w->wscales), w->lora_up,
+                                           static_cast<const uint2*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
                                            cfg->rank, stream, e2.start, e2.end),
                      "gemm kernel launch"));
