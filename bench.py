@@ -161,8 +161,8 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
         return files[0]
 
     def short(name):
-        for key in ("k1_quant_int4", "k2_gemm_int4", "MulFunctor", "FillFunctor", "k_pack_int4",
-                    "k_transpose", "k_zero_flag", "copyBuffer"):
+        for key in ("k1_int4_fused", "k2_gemm_int4", "MulFunctor", "FillFunctor", "k_pack_int4",
+                    "k_pack_lora_down", "k_transpose", "k_zero_flag", "copyBuffer"):
             if key in name:
                 return key
         return name[:40]
@@ -193,7 +193,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     f_fetch = per["fetch"]["MulFunctor"] * 1024 / copy_bytes
     f_write = per["write"]["MulFunctor"] * 1024 / copy_bytes
     k2_traffic = per["fetch"]["k2_gemm_int4"] * 1024 / f_fetch + per["write"]["k2_gemm_int4"] * 1024 / f_write
-    k1_traffic = per["fetch"]["k1_quant_int4"] * 1024 / f_fetch + per["write"]["k1_quant_int4"] * 1024 / f_write
+    k1_traffic = per["fetch"]["k1_int4_fused"] * 1024 / f_fetch + per["write"]["k1_int4_fused"] * 1024 / f_write
     t = [f"# HBM traffic per dispatch from rocprofv3 counters, workload {workload} "
          f"(M={M} K={K} N={N} rank {rank}, int4 g64)",
          f"# fetch command: {PROFILE_CMDS['fetch']}",
@@ -205,7 +205,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
          f"copy_write_KiB = {per['write']['MulFunctor']:.1f}",
          f"fetch_factor = {f_fetch:.4f}",
          f"write_factor = {f_write:.4f}"]
-    for k in ("k1_quant_int4", "k2_gemm_int4"):
+    for k in ("k1_int4_fused", "k2_gemm_int4"):
         t.append(f"{k}_fetch_KiB = {per['fetch'][k]:.1f}")
         t.append(f"{k}_write_KiB = {per['write'][k]:.1f}")
     t += [f"k1_traffic_bytes_per_launch = {k1_traffic:.0f}",
