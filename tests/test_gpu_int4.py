@@ -210,6 +210,23 @@ def test_throughput_workload_sampled_rows():
     check_y(y[rows], OL.w4a4_linear_rows("int4", x, layer, rows)["r"])
 
 
+@pytest.mark.parametrize("K,N", [(12288, 3072), (3072, 9216)])
+def test_dit_block_shapes_sampled_rows(K, N):
+    """Seeded prepared-layout layers at the DiT block shapes (M = 4608: MLP-down, whose
+    GEMM runs on 128-wide tiles, and QKV on 192-wide tiles), in one launch each:
+    sampled rows against the oracle."""
+    pb = I.prepared_int4_bytes(3, K, N, 32)
+    sd = I.seeds(3)
+    x = I.activations(4608, K, sd.x, I.outlier_channels(K, I.default_outlier_count(K), sd.outliers),
+                      30.0)
+    layer = P.SvdqLayer(precision="int4", K=K, N=N, rank=32, qweight=pb.qweight,
+                        wscales=pb.wscales, w_global=1.0, act_global=1.0, smooth=pb.smooth,
+                        lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+    y = host_bits(_layer_dev(layer)(dev_bf16(x)))
+    rows = np.unique(np.concatenate([np.arange(5, 4608, 331), [0, 4607]]))
+    check_y(y[rows], OL.w4a4_linear_rows("int4", x, layer, rows)["r"])
+
+
 def test_timing_hook_counts_two_kernels(tiny):
     li, layer = tiny
     dl = _layer_dev(layer)
