@@ -46,15 +46,6 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return e == 0 ? sub : nrm;
 }
 
-// E2M1 magnitude code of |v|: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the
-// even code, saturating at 6.  Each comparison adds one where v passes a midpoint;
-// the midpoints next to an even code are exclusive, the others inclusive.
-__device__ __forceinline__ uint32_t e2m1_mag(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-         (uint32_t)(a > 5.0f);
-}
-
 // Twice the E2M1 magnitude of code mag (0, 1, 2, 3, 4, 6, 8, 12), from a nibble table.
 __device__ __forceinline__ uint32_t e2m1_twice(uint32_t mag) {
   return __builtin_amdgcn_ubfe(0xC8643210u, 4 * mag, 4);
@@ -99,17 +90,27 @@ __device__ __forceinline__ void nvfp4_quant32(const float (&xh)[32], float g, ui
       quot[i] = __builtin_fmaf(e, r[i >> 4], y);
     }
   }
+  // E2M1 magnitudes from the hardware converter (scale 1: nearest, ties to the even
+  // code, saturating at 6; checked against e2m1_mag on every midpoint and its ulp
+  // neighbours); quotients are clamped to 8 first so an overflowed quotient of the
+  // division path saturates too.  The sign is xhat's.
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const float half_s = 0.5f * s[b];
     const uint32_t live = s[b] > 0.f ? 0xFu : 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t xb = __float_as_uint(xh[16 * b + i]);
-      const uint32_t c = (e2m1_mag(fabsf(quot[16 * b + i])) | ((xb >> 28) & 8u)) & live;
-      codes[16 * b + i] = c;
-      const float v = (float)e2m1_twice(c & 7u) * half_s;  // exact
-      deq[16 * b + i] = __uint_as_float(__float_as_uint(v) | ((c & 8u) << 28));
+    for (int i = 0; i < 16; i += 2) {
+      const float q0 = __builtin_amdgcn_fmed3f(quot[16 * b + i], -8.0f, 8.0f);
+      const float q1 = __builtin_amdgcn_fmed3f(quot[16 * b + i + 1], -8.0f, 8.0f);
+      const uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q0, q1, 1.0f, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t xb = __float_as_uint(xh[16 * b + i + h]);
+        const uint32_t c = (((pk >> (4 * h)) & 7u) | ((xb >> 28) & 8u)) & live;
+        codes[16 * b + i + h] = c;
+        const float v = (float)e2m1_twice(c & 7u) * half_s;  // exact
+        deq[16 * b + i + h] = __uint_as_float(__float_as_uint(v) | ((c & 8u) << 28));
+      }
     }
   }
 }
