@@ -169,7 +169,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
 
     _, cid, M, K, N, rank = WORKLOADS[workload]
     lines = [f"# rocprofv3 kernel statistics: bench.py, workload {workload} "
-             f"(M={M} K={K} N={N} rank {rank}, int4 g64), 500 timed + 50 warmup calls",
+             f"(M={M} K={K} N={N} rank {rank}, int4 g64), 50 warmup + 500 timed + 500 event-timed calls",
              f"# command: {PROFILE_CMDS['stats']}",
              "# kernel                      calls     avg_us     min_us     max_us   share_%"]
     for r in csv.DictReader(open(one("prof_stats/**/*kernel_stats.csv"))):
