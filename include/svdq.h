@@ -100,8 +100,9 @@ svdq_status svdq_check_device(int hip_device);
  * config or shape).  *codes_bytes and *scales_bytes receive the two parts:
  *   int4:  codes N*K*3/4 (E2M3 lane slots, 6 bits per weight: the layout the GEMM's
  *          FP6 MFMA reads, chunks of 1536 bytes per 32 output columns and 64-group),
- *          scales round_up(K/64 * N * 8, 256) + 256 ([K/64][N] 8-byte records
- *          {bf16 scale, 0, 0, 0}: the rescale MFMA's operand as stored; range flag)
+ *          scales round_up(K/128 * N * 8, 256) + 256 ([K/128][N] 8-byte records
+ *          {scale of group 2p, scale of group 2p+1, 0, 0} in bf16: the rescale MFMA's
+ *          operand as stored, one record per pair of groups; range flag)
  *   nvfp4: codes N*K*2 (exact dequantized bf16 [N][K]), scales 256 (range flag) */
 size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
                                 size_t* codes_bytes, size_t* scales_bytes);

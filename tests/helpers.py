@@ -66,11 +66,34 @@ def check_u(u: np.ndarray, ref: dict, lora_down_bits: np.ndarray, chain: int | N
 
 
 def scale_records(buf: np.ndarray, groups: int, rows: int) -> np.ndarray:
-    """Kernel-layout scale records [groups][rows] of 8 bytes {bf16 s, 0, 0, 0} -> s bits
-    [groups, rows]; asserts the zero padding."""
+    """Activation scale records [groups][rows] of 8 bytes, {s, 0, 0, 0} for an even
+    group and {0, s, 0, 0} for an odd one (bf16 positions) -> s bits [groups, rows];
+    asserts the zero padding."""
     rec = np.asarray(buf, dtype=np.uint8)[: groups * rows * 8].view(np.uint16).reshape(groups, rows, 4)
-    assert np.all(rec[..., 1:] == 0), "nonzero padding in a scale record"
-    return rec[..., 0]
+    even = np.arange(groups) % 2 == 0
+    assert np.all(rec[even][..., 1:] == 0), "nonzero padding in an even-group scale record"
+    assert np.all(rec[~even][..., [0, 2, 3]] == 0), "nonzero padding in an odd-group scale record"
+    return np.where(even[:, None], rec[..., 0], rec[..., 1])
+
+
+def pair_scale_records(buf: np.ndarray, groups: int, cols: int) -> np.ndarray:
+    """Weight scale records [groups/2][cols] of 8 bytes {s[2p], s[2p+1], 0, 0} -> s bits
+    [groups, cols]; asserts the zero padding."""
+    assert groups % 2 == 0
+    rec = np.asarray(buf, dtype=np.uint8)[: groups // 2 * cols * 8].view(np.uint16).reshape(groups // 2, cols, 4)
+    assert np.all(rec[..., 2:] == 0), "nonzero padding in a weight scale record"
+    return rec[..., :2].transpose(0, 2, 1).reshape(groups, cols)
+
+
+def u_partials(buf: np.ndarray, nsplit: int, rows_pad: int, rank: int) -> np.ndarray:
+    """Partial low-rank activations in the GEMM's fragment layout
+    [split][rows/32][rank/16][2][64 lanes][4] fp32 -> [split, rows, rank]: lane
+    l = row % 32 + 32 * ((j % 16) // 8) holds j = 16 c + 8 (l // 32) + [0, 8), the first
+    four in the first half, the rest in the second."""
+    f = np.asarray(buf, dtype=np.uint8)[: nsplit * rows_pad * rank * 4].view(np.float32)
+    f = f.reshape(nsplit, rows_pad // 32, rank // 16, 2, 2, 32, 4)  # .., half, lh, lr, e
+    # -> split, row block, lr, slice, lh, half, e
+    return f.transpose(0, 1, 5, 2, 4, 3, 6).reshape(nsplit, rows_pad, rank)
 
 
 def int4_interchange(q: np.ndarray) -> np.ndarray:

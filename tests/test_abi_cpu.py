@@ -103,7 +103,7 @@ def test_packed_weight_bytes():
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     tot = lib.svdq_packed_weight_bytes(ctypes.byref(cfg()), 3072, 3072, ctypes.byref(cb), ctypes.byref(sb))
     assert cb.value == 3072 * 3072 * 3 // 4      # E2M3 lane slots, 6 bits per weight
-    assert sb.value == 48 * 3072 * 8 + 256     # 8-byte scale records + range flag
+    assert sb.value == 24 * 3072 * 8 + 256     # 8-byte records per group pair + range flag
     assert tot == cb.value + sb.value
 
 

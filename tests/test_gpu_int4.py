@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import w4a4_rank_corrected_linear_amd as svdq
-from helpers import (check_u, check_y, decode_fp6_operand, dev_bf16, scale_records,
+from helpers import (check_u, check_y, decode_fp6_operand, dev_bf16, pair_scale_records, scale_records,
+                     u_partials,
                      dev_u8, host_bits, int4_interchange)
 from oracle import formats as F
 from oracle import linear as OL
@@ -84,7 +85,7 @@ def test_pack_weight_layout(tiny):
     q = decode_fp6_operand(host_bits(pc), layer.N, layer.K)
     assert np.array_equal(q, F.int4_decode(F.unpack_nibbles(layer.qweight)))
     G = layer.K // 64
-    st = scale_records(host_bits(ps), G, layer.N)
+    st = pair_scale_records(host_bits(ps), G, layer.N)
     assert np.array_equal(st, layer.wscales.T)
 
 
@@ -153,7 +154,7 @@ def test_workspace_matches_standalone_quantize(tiny):
     s = scale_records(w[off_s:], G, M_pad)
     assert np.array_equal(s[:, :M], ref["scales"].T)
     off_u = off_s + G * M_pad * 8
-    u = w[off_u: off_u + M_pad * 32 * 4].view(np.float32).reshape(M_pad, 32)
+    u = u_partials(w[off_u:], 1, M_pad, 32)[0]
     check_u(u[:M], ref, layer.lora_down)
     assert np.all(u[M:] == 0)
 
@@ -264,7 +265,7 @@ def test_workspace_with_three_k_splits():
     s = scale_records(w[off_s:], G, M_pad)
     assert np.array_equal(s[:, :M], ref["scales"].T)
     off_u = off_s + -(-G * M_pad * 8 // 256) * 256
-    u = w[off_u: off_u + nsplit * M_pad * r * 4].view(np.float32).reshape(nsplit, M_pad, r)
+    u = u_partials(w[off_u:], nsplit, M_pad, r)
     check_u(u.astype(np.float64).sum(axis=0)[:M], ref, ld)
     check_y(host_bits(y), OL.w4a4_linear("int4", x, layer)["r"])
 

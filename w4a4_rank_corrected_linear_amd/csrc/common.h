@@ -15,9 +15,23 @@
 // k = 64 g + 32 h + f, f = 0..31, field f in bits 6f..6f+5 of six dwords; dwords
 // 0-3 sit at chunk + 16 l and dwords 4-5 at chunk + 1024 + 8 l, so a 64-lane
 // 16-byte and a 64-lane 8-byte access read one whole operand.
-// Per-group scales sit group-major as 8-byte records: record g * R_pad + row holds
-// the bf16 scale in bits 15:0 and zeros above.  A 64-bit load of a record is
-// directly the bf16x4 operand {s, 0, 0, 0} of the rescale MFMA.
+//
+// Scale records (operands of the rescale MFMA, one 64-bit load each)
+// -------------------------------------------------------------------
+// Activation scales sit group-major as 8-byte records, record g * M_pad + row: the
+// bf16 scale in bits 15:0 for an even group g and in bits 31:16 for an odd one, zeros
+// elsewhere, i.e. the bf16x4 operand {s, 0, 0, 0} or {0, s, 0, 0}.  Weight scales sit
+// as one 8-byte record per pair of groups, record (g / 2) * N + n = {sw[n, g & ~1],
+// sw[n, g | 1], 0, 0}.  The product of the two operands over the four bf16 positions
+// picks sw[n, g] sx[m, g] for either parity, so one weight record serves both groups
+// of a pair.
+//
+// Fragment layout of the low-rank activations U (fp32, the quantizer's partial sums
+// per k-split): [split][M_pad / 32][rank / 16][2][64][4] floats.  For rows of one
+// 32-row block and ranks 16 c .. 16 c + 15, lane l = row % 32 + 32 * ((rank % 16) / 8)
+// holds ranks 16 c + 8 (l / 32) + [0, 8): elements 0-3 in the first 1 KiB, 4-7 in the
+// second, so the GEMM reads each half as one contiguous 64-lane 16-byte load in the
+// B-operand order of v_mfma_f32_32x32x16_bf16.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,5 +62,14 @@ __device__ __forceinline__ uint32_t e2m3_field(int q) {
 }
 
 __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Index (in floats) of U[split][row][j] in the fragment layout above.
+__host__ __device__ __forceinline__ size_t u_frag_index(int split, int row, int j, int M_pad,
+                                                        int rank) {
+  const int lane = (row & 31) + 32 * ((j & 15) >> 3);
+  const int e = j & 7;
+  return ((((size_t)split * (M_pad >> 5) + (row >> 5)) * (rank >> 4) + (j >> 4)) * 2 + (e >> 2)) *
+             256 + lane * 4 + (e & 3);
+}
 
 }  // namespace svdq

@@ -17,9 +17,10 @@
 // Low-rank down projection: MFMA call c (0..3) of v_mfma_f32_16x16x32_bf16 takes the
 // lane's chunk c (k = ... + 8c + [0, 8)) at MFMA k-position 8q + [0, 8); its B operand
 // is lora_down at the same k, read from the packed fragment order in which each
-// call's 64 operands are 1 KiB contiguous.  The four waves' partial tiles are summed in LDS in a
-// fixed order and written as the split's partial U (fp32 [split][M_pad][r]); the GEMM
-// adds the splits in a fixed order, so U is deterministic.
+// call's 64 operands are 1 KiB contiguous.  The four waves' partial tiles are summed
+// in LDS in a fixed order and written as the split's partial U (fp32, the fragment
+// layout of common.h); the GEMM adds the splits in a fixed order, so U is
+// deterministic.
 #pragma once
 #include "common.h"
 #include "kernels.h"
@@ -36,7 +37,7 @@ struct K1Args {
   int rank;
   uint8_t* out;
   void* scales;
-  float* uact;  // [split][M_pad][rank] partial sums
+  float* uact;  // partial sums per k-split, fragment layout (common.h)
   int M_pad;
   float g;
 };
@@ -157,10 +158,9 @@ __device__ __forceinline__ void k1_batch(const K1Args& a) {
       ured[wave][4 * q + i][16 + r] = u1[i];
     }
     __syncthreads();
-    float* up = a.uact + (size_t)blockIdx.y * a.M_pad * rank;
     for (int t = threadIdx.x; t < 16 * rank; t += 256) {
       const int rr = t / rank, cc = t % rank;
-      up[(size_t)(row0 + rr) * rank + cc] =
+      a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)] =
           ((ured[0][rr][cc] + ured[1][rr][cc]) + ured[2][rr][cc]) + ured[3][rr][cc];
     }
   }

@@ -8,8 +8,8 @@
 //
 // Two kernels share the quantizer below:
 //  * k1_int4_fused (the layer's own path) uses the batch skeleton of k1_batch.h and
-//    writes the GEMM operand layout, scales [K/64][M_pad] (8-byte records, see
-//    common.h) and partial U per k-split;
+//    writes the GEMM operand layout, scales [K/64][M_pad] (8-byte records by group
+//    parity, see common.h) and partial U per k-split in the fragment layout;
 //  * k1_int4_interchange (svdq_quantize_act) streams whole rows with register
 //    prefetch and writes codes [M][K/2], scales [M][K/64] and U [M][r].
 // In both, lane l holds half h = q % 2 of the 64-group g = k0 / 64 (q = l / 16): the
@@ -86,7 +86,8 @@ struct QuantInt4Fused {
     const int slot = h * 32 + (row & 31);
     *reinterpret_cast<uint4*>(chunk + slot * 16) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
     *reinterpret_cast<uint2*>(chunk + 1024 + slot * 8) = make_uint2(f6[4], f6[5]);
-    if (h == 0) static_cast<uint2*>(a.scales)[(size_t)g * a.M_pad + row] = make_uint2(s_bits, 0u);
+    if (h == 0)
+      static_cast<uint2*>(a.scales)[(size_t)g * a.M_pad + row] = make_uint2(s_bits << (16 * (g & 1)), 0u);
   }
 };
 
@@ -226,8 +227,8 @@ k1_int4_interchange(const uint16_t* __restrict__ x, int M, int K,
 
 // fused = false: interchange layout (codes [M][K/2], scales [M][K/64], U [M][r] fp32).
 // fused = true : GEMM layout, M_pad rows (operand chunks of 1536 B per 32-row block
-//                and group, scale records [K/64][M_pad], partial U [split][M_pad][r]
-//                fp32);
+//                and group, scale records [K/64][M_pad], partial U per k-split in
+//                the fragment layout of common.h, fp32);
 //                rows >= M are zero.
 hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, void* scales,

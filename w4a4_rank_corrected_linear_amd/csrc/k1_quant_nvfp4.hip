@@ -259,7 +259,8 @@ k1_nvfp4_interchange(const uint16_t* __restrict__ x, int M, int K,
 }
 
 // fused = false: codes [M][K/2], scales [M][K/16] (E4M3 bytes), U [M][r] fp32.
-// fused = true : A' bf16 [M_pad][K] (rows >= M are zero), partial U [split][M_pad][r].
+// fused = true : A' bf16 [M_pad][K] (rows >= M are zero), partial U per k-split in the
+//                fragment layout of common.h.
 hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {

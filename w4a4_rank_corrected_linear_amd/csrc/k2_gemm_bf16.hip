@@ -121,9 +121,10 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
         // U = sum of the quantizer's k-split partials, added in order
         float uf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < nsplit; ++sp) {
-          const float* up = U + ((size_t)sp * M_pad + rowb + lr) * rank + kk + 8 * lh;
+          // fragment layout: ranks 0-3 of the lane's eight, then 4-7 one KiB further
+          const float* up = U + u_frag_index(sp, rowb + lr, kk + 8 * lh, M_pad, rank);
           const float4 u0 = *reinterpret_cast<const float4*>(up);
-          const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
+          const float4 u1 = *reinterpret_cast<const float4*>(up + 256);
           uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w;
           uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z; uf[7] += u1.w;
         }

@@ -11,20 +11,23 @@
 // l%32 is the output row, the 16 accumulator elements are output columns):
 //   D = v_mfma_scale_f32_32x32x64_f8f6f4(W_g, X_g)   E2M3 codes q/8, block scales 2^2
 //                                                    and 2^3: D = P_g / 2 exactly
-//   S = v_mfma_f32_32x32x8_bf16(sw, sx)              sw and sx sit at k = 0 (lanes <
-//                                                    32) and k = 4 (lanes >= 32): the
-//                                                    exact product 2 sw[n] sx[m]
+//   S = v_mfma_f32_32x32x8_bf16(sw, sx)              the scale records of common.h:
+//                                                    sw[g] sx[g] at k = 0 or 1 (lanes
+//                                                    < 32) and k = 4 or 5 (lanes >= 32),
+//                                                    the exact product 2 sw[n] sx[m]
 //   acc = fma(S, D, acc)                             one VALU op per element and group
 // The accumulator starts as U L2t^T (U split into bf16 hi + lo, four bf16 MFMAs per
-// 16 ranks), so the epilogue only adds the bias and stores.
+// 16 ranks), so the epilogue only adds the bias and stores.  All of the seed's global
+// loads (U in the fragment layout of common.h, two k-splits at a time, and lora_up)
+// are issued before the first is used.
 //
 // Tiling: one 512-thread workgroup (8 waves, two per SIMD) per CU, tile 256 x BN,
 // wave tile 64 x BN/2 (2 x BN/64 blocks).  A stage is two 64-groups.  Operands live
 // in a 3-slot LDS ring; slot s%3 holds stage s:
 //   A   [row-block 0..7][group 0..1][1536 B]  activation lane slots (written by K1)
 //   B   [col-block][group 0..1][1536 B]       weight lane slots (written by the pack)
-//   SA  [group][256 rows], SB [group][BN cols]: 8-byte scale records (common.h), so
-//       each rescale operand is one 64-bit LDS load with no VALU work
+//   SA  [group][256 rows], SB [BN cols]       8-byte scale records (common.h): one
+//                                             weight record serves both groups
 // all copied by LDS DMA (global_load_lds_dwordx4, 16 B per lane).  At the top of
 // iteration t every wave waits for its own copies of stage t+1, the barrier publishes
 // them and frees slot (t+2)%3, and the copies of stage t+2 start.  The twelve (or
@@ -32,7 +35,10 @@
 // the two MFMAs of block b+1, rescales block b with the MFMA results of step b-1, and
 // loads the fragments needed two steps later (B fragments into three rotating
 // register sets, A fragments per group parity); the last steps already load and issue
-// stage t+1's first block.
+// stage t+1's first block.  The LDS addresses of the current and the next slot are
+// formed once per stage (lane, wave and slot parts in one register per operand
+// stream), so every fragment read is that register plus an immediate offset.  The
+// tile's bias is copied to LDS at the top of the last stage.
 //
 // The tile order is XCD-aware: workgroup i runs on XCD i % 8, and the eight XCDs
 // take disjoint (tiles_m/4) x (tiles_n/2) sub-grids, so each XCD's L2 holds a quarter
@@ -83,11 +89,12 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   constexpr int CB = BN / 32;              // 32-column blocks per tile
   constexpr int ASZ = 8 * 2 * 384;         // dwords of A per stage
   constexpr int BSZ = CB * 2 * 384;        // dwords of B per stage
-  constexpr int SLOT = ASZ + BSZ + (2 * BM + 2 * BN) * 2;
+  constexpr int SLOT = ASZ + BSZ + 4 * BM + 2 * BN;  // + scale records: SA 2 x BM, SB BN
   constexpr int NB = 4 * WN;               // blocks per wave and stage
   constexpr int NBS = (WN == 3) ? 3 : 4;   // B register sets (divides 2 WN fragments)
   static_assert(WN == 2 || WN == 3, "tile width 128 or 192");
   __shared__ __attribute__((aligned(16))) uint32_t ring[3 * SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t bias_s[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,7 +124,8 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 
   // Copies of stage s: wave w copies A row-block w (3 KiB: both groups); waves below
   // CB copy B col-block w; wave CB the row scale records (2 x 2 KiB), wave CB+1 the
-  // column scale records (2 x BN * 8 bytes).  A 64-lane copy moves 128 records.
+  // column scale records of the group pair (BN * 8 bytes).  A 64-lane copy moves 128
+  // records.
   const uint32_t voff = lane * 16;
   auto dma = [&](int s, int sl) {
     {
@@ -139,13 +147,10 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
               lds_addr(slotSA(sl) + gl * BM + 128 * part));
       }
     } else if (wave == CB + 1) {
-#pragma unroll
-      for (int gl = 0; gl < 2; ++gl) {
-        const uint2* src = sB + (size_t)(2 * s + gl) * N + col0;
-        const uint32_t dst = lds_addr(slotSB(sl) + gl * BN);
-        dma16(voff, src, dst);
-        if (BN > 128 && lane < (BN - 128) / 2) dma16(voff, src + 128, dst + 1024);
-      }
+      const uint2* src = sB + (size_t)s * N + col0;
+      const uint32_t dst = lds_addr(slotSB(sl));
+      dma16(voff, src, dst);
+      if (BN > 128 && lane < (BN - 128) / 2) dma16(voff, src + 128, dst + 1024);
     }
   };
 
@@ -162,63 +167,119 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 
   // Low-rank seed acc^T = L2t U^T.  U (fp32, the sum of the quantizer's k-split
   // partials in split order) is split into bf16 hi + lo; u - hi is exact in fp32 and
-  // what lo drops is below 2^-17 |u|.
-  for (int kk = 0; kk < rank; kk += 16) {
-    v8bf uh[2], ul[2];
+  // what lo drops is below 2^-17 |u|.  rank <= 32: at most two 16-rank slices.
+  if (rank > 0) {
+    uint4 lbv[2][WN];
+    float uf[2][2][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rowm = row0 + wm * 64 + 32 * i + lr;
-      float uf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float* up = U + ((size_t)sp * M_pad + rowm) * rank + kk + 8 * lh;
-        const float4 u0 = *reinterpret_cast<const float4*>(up);
-        const float4 u1 = *reinterpret_cast<const float4*>(up + 4);
-        uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w;
-        uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z; uf[7] += u1.w;
-      }
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uh[i][q] = (__bf16)uf[q];
-        ul[i][q] = (__bf16)(uf[q] - (float)uh[i][q]);
-      }
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) uf[kk][i][q] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      if (16 * kk < rank)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int coln = col0 + (wn * WN + j) * 32 + lr;
+          lbv[kk][j] = *reinterpret_cast<const uint4*>(L2t + (size_t)coln * rank + 16 * kk + 8 * lh);
+        }
+    for (int sp = 0; sp < nsplit; sp += 2) {
+      float4 tv[2][2][2][2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        if (sp + s2 < nsplit)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            if (16 * kk < rank)
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                const float* up =
+                    U + u_frag_index(sp + s2, row0 + wm * 64 + 32 * i, 16 * kk, M_pad, rank) + lane * 4;
+                tv[s2][kk][i][0] = *reinterpret_cast<const float4*>(up);
+                tv[s2][kk][i][1] = *reinterpret_cast<const float4*>(up + 256);
+              }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        if (sp + s2 < nsplit)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            if (16 * kk < rank)
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                const float4 a0 = tv[s2][kk][i][0], a1 = tv[s2][kk][i][1];
+                uf[kk][i][0] += a0.x; uf[kk][i][1] += a0.y; uf[kk][i][2] += a0.z; uf[kk][i][3] += a0.w;
+                uf[kk][i][4] += a1.x; uf[kk][i][5] += a1.y; uf[kk][i][6] += a1.z; uf[kk][i][7] += a1.w;
+              }
     }
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int coln = col0 + (wn * WN + j) * 32 + lr;
-      const uint4 lb = *reinterpret_cast<const uint4*>(L2t + (size_t)coln * rank + kk + 8 * lh);
-      const v8bf lv = __builtin_bit_cast(v8bf, lb);
+    for (int kk = 0; kk < 2; ++kk) {
+      if (16 * kk < rank) {
+        v8bf uh[2], ul[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, uh[i], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, ul[i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            uh[i][q] = (__bf16)uf[kk][i][q];
+            ul[i][q] = (__bf16)(uf[kk][i][q] - (float)uh[i][q]);
+          }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const v8bf lv = __builtin_bit_cast(v8bf, lbv[kk][j]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, uh[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, ul[i], acc[i][j], 0, 0, 0);
+          }
+        }
       }
     }
   }
 
   const v16f zero = {};
-  auto frag = [&](const uint32_t* base) {
-    const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 4);
-    const v2i hi = *reinterpret_cast<const v2i*>(base + 256 + lane * 2);
+  // LDS byte addresses of a ring slot with the lane, wave and slot parts folded in,
+  // formed once per stage and hidden from the optimizer (an empty asm), so that each
+  // read below is one of these registers plus an immediate offset
+  struct Bases { uint32_t a16, a8, b16, b8, sa, sb; };
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)ring;
+  auto bases = [&](int sl) {
+    Bases r;
+    const uint32_t so = ring0 + sl * SLOT * 4;
+    r.a16 = so + (wm * 4 * 384 + lane * 4) * 4;
+    r.a8 = so + (wm * 4 * 384 + 256 + lane * 2) * 4;
+    r.b16 = so + (ASZ + wn * WN * 2 * 384 + lane * 4) * 4;
+    r.b8 = so + (ASZ + wn * WN * 2 * 384 + 256 + lane * 2) * 4;
+    r.sa = so + (ASZ + BSZ + 2 * (wm * 64 + lr)) * 4;
+    r.sb = so + (ASZ + BSZ + 4 * BM + 2 * (wn * WN * 32 + lr)) * 4;
+    asm volatile("" : "+v"(r.a16), "+v"(r.a8), "+v"(r.b16), "+v"(r.b8), "+v"(r.sa), "+v"(r.sb));
+    return r;
+  };
+  typedef __attribute__((address_space(3))) const v4i lds_v4i;
+  typedef __attribute__((address_space(3))) const v2i lds_v2i;
+  auto frag = [&](uint32_t p16, uint32_t p8, int off) {
+    const v4i lo = *(lds_v4i*)(uintptr_t)(p16 + off * 4);
+    const v2i hi = *(lds_v2i*)(uintptr_t)(p8 + off * 4);
     return (v8i)__builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2,
                                         3, 4, 5, -1, -1);
   };
   // register sets: A fragments and row scales by group parity; B fragment k = gl WN + j
-  // (2 WN per stage) and its column scale in set k % NBS
+  // (2 WN per stage) and its column scale record in set k % NBS (the record of j is
+  // loaded with the even group's fragment and serves the odd group's as well)
   v8i fa[2][2], fb[NBS];
   v2i fsa[2][2], fsb[NBS];
-  auto loadA = [&](int set, int sl, int gl) {
-    const uint32_t* Ab = slotA(sl);
-    const uint2* SAb = slotSA(sl);
+  auto loadA = [&](int set, const Bases& q, int gl) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      fa[set][i] = frag(Ab + ((wm * 2 + i) * 2 + gl) * 384);
-      fsa[set][i] = *reinterpret_cast<const v2i*>(SAb + gl * BM + wm * 64 + 32 * i + lr);
+      fa[set][i] = frag(q.a16, q.a8, (i * 2 + gl) * 384);
+      fsa[set][i] = *(lds_v2i*)(uintptr_t)(q.sa + (gl * BM + 32 * i) * 8);
     }
   };
-  auto loadB = [&](int k, int sl) {
+  auto loadB = [&](int k, const Bases& q) {
     const int gl = k / WN, j = k % WN;
-    fb[k % NBS] = frag(slotB(sl) + ((wn * WN + j) * 2 + gl) * 384);
-    fsb[k % NBS] = *reinterpret_cast<const v2i*>(slotSB(sl) + gl * BN + (wn * WN + j) * 32 + lr);
+    fb[k % NBS] = frag(q.b16, q.b8, (j * 2 + gl) * 384);
+    if (gl == 0) fsb[k % NBS] = *(lds_v2i*)(uintptr_t)(q.sb + j * 32 * 8);
+    else if (NBS != WN) fsb[k % NBS] = fsb[(k - WN) % NBS];
   };
   v16f d[2], sc[2];
   // block b of a stage: group b / (2 WN), column block (b % (2 WN)) / 2, row block b % 2
@@ -234,9 +295,12 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   // stages 0 and 1 landed for every wave
   wait_vm0();
   barrier_lds();
-  loadA(0, 0, 0);
-  loadB(0, 0);
-  loadB(1, 0);
+  {
+    const Bases q0 = bases(0);
+    loadA(0, q0, 0);
+    loadB(0, q0);
+    loadB(1, q0);
+  }
   issue(0);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -244,7 +308,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   // at step 2k - 3 (the next stage's first two at steps NB-3 and NB-1), the odd-group
   // A fragments at step 0, the next stage's even-group A fragments at step NB/2 (the
   // last use of that set is the issue of block NB/2 - 1).
-  auto step = [&](int b, int sl, int nsl, bool next) {
+  auto step = [&](int b, const Bases& cq, const Bases& nq, bool next) {
     const int j = (b % (2 * WN)) / 2, i = b % 2;
     if (b + 1 < NB) issue(b + 1);
     else if (next) issue(0);
@@ -252,11 +316,11 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(sc[b & 1][e], d[b & 1][e], acc[i][j][e]);
     if (b & 1) {
       const int k = (b + 3) / 2;
-      if (k < 2 * WN) loadB(k, sl);
-      else if (next) loadB(k - 2 * WN, nsl);
+      if (k < 2 * WN) loadB(k, cq);
+      else if (next) loadB(k - 2 * WN, nq);
     }
-    if (b == 0) loadA(1, sl, 1);
-    if (b == NB / 2 && next) loadA(0, nsl, 0);
+    if (b == 0) loadA(1, cq, 1);
+    if (b == NB / 2 && next) loadA(0, nq, 0);
     // issue order within the step: D, the fragment loads, half the FMAs, S, the rest
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
@@ -273,9 +337,9 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     }
     if (t + 2 < S) dma(t + 2, (t + 2) % 3);
     __builtin_amdgcn_sched_barrier(0);
-    const int sl = t % 3, nsl = (t + 1) % 3;
+    const Bases cq = bases(t % 3), nq = bases((t + 1) % 3);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) step(b, sl, nsl, true);
+    for (int b = 0; b < NB; ++b) step(b, cq, nq, true);
   }
   {
     const int t = S - 1;
@@ -283,8 +347,11 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       wait_vm0();
       barrier_lds();
     }
+    // the tile's bias goes to LDS under the last stage (wave 0, 16 B per lane)
+    if (bias && wave == 0 && lane < BN / 8) dma16(voff, bias + col0, lds_addr(bias_s));
+    const Bases cq = bases(t % 3);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) step(b, t % 3, 0, false);
+    for (int b = 0; b < NB; ++b) step(b, cq, cq, false);
     // keeps the last rescale ahead of the epilogue
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -296,16 +363,16 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   // ring is free once every wave has passed the barrier) and writes Y in 16-byte
   // pieces, BN/16 consecutive lanes per row, so every row segment of the tile is one
   // contiguous run of full 64-byte sectors.
+  wait_vm0();
   barrier_lds();
   uint16_t* tile = reinterpret_cast<uint16_t*>(ring) + wave * (64 * (BN / 2 + 8));
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
-    const int colb = col0 + (wn * WN + j) * 32;
     float bv[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint2 b2 = make_uint2(0, 0);
-      if (bias) b2 = *reinterpret_cast<const uint2*>(bias + colb + 8 * q + 4 * lh);
+      const uint2 b2 = bias ? *reinterpret_cast<const uint2*>(bias_s + (wn * WN + j) * 32 + 8 * q + 4 * lh)
+                            : make_uint2(0, 0);
       bv[4 * q + 0] = __uint_as_float(b2.x << 16);
       bv[4 * q + 1] = __uint_as_float(b2.x & 0xFFFF0000u);
       bv[4 * q + 2] = __uint_as_float(b2.y << 16);

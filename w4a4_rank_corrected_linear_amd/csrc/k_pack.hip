@@ -52,12 +52,13 @@ k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, 
   if (bad) atomicOr(flag, 1);
 }
 
+// Weight scale records, one per pair of groups: {sw[n, 2p], sw[n, 2p + 1], 0, 0}.
 __global__ void __launch_bounds__(256)
-k_transpose_scales(const uint16_t* __restrict__ in, uint2* __restrict__ out, int N, int G) {
+k_pair_scales(const uint16_t* __restrict__ in, uint2* __restrict__ out, int N, int G) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)N * G) return;
-  const int64_t g = t / N, n = t % N;
-  out[t] = make_uint2(in[n * G + g], 0u);
+  if (t >= (int64_t)N * (G / 2)) return;
+  const int64_t p = t / N, n = t % N;
+  out[t] = make_uint2((uint32_t)in[n * G + 2 * p] | ((uint32_t)in[n * G + 2 * p + 1] << 16), 0u);
 }
 
 // One thread per 8 weights (4 code bytes, one E4M3 scale).
@@ -116,8 +117,8 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
   const int64_t total = (int64_t)N * G * 2;
   hipLaunchKernelGGL(k_pack_int4_codes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
                      codes, out_codes, N, K, flag);
-  const int64_t ts = (int64_t)N * G;
-  hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
+  const int64_t ts = (int64_t)N * (G / 2);
+  hipLaunchKernelGGL(k_pair_scales, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
                      scales, reinterpret_cast<uint2*>(out_scales), N, G);
   return hipGetLastError();
 }

@@ -206,12 +206,12 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N, si
     return 0;
   }
   const int64_t G = K / cfg->group_size;
-  // int4: E2M3 lane slots (3/4 byte per weight) and [G][N] 8-byte scale records;
-  // nvfp4: exact dequantized bf16 weights [N][K]; both with a 256-byte range-flag
-  // trailer
+  // int4: E2M3 lane slots (3/4 byte per weight) and [G/2][N] 8-byte scale records,
+  // one per pair of groups; nvfp4: exact dequantized bf16 weights [N][K]; both with a
+  // 256-byte range-flag trailer
   const bool nv = cfg->precision == SVDQ_NVFP4;
   const size_t cb = nv ? (size_t)(N * K * 2) : (size_t)(N * K * 3 / 4);
-  const size_t sb = nv ? 256 : (size_t)round_up(G * N * 8, 256) + 256;
+  const size_t sb = nv ? 256 : (size_t)round_up(G / 2 * N * 8, 256) + 256;
   if (codes_bytes) *codes_bytes = cb;
   if (scales_bytes) *scales_bytes = sb;
   return cb + sb;
@@ -231,7 +231,7 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
   const int64_t G = K / cfg->group_size;
   const bool nv = cfg->precision == SVDQ_NVFP4;
   int* flag = reinterpret_cast<int*>(static_cast<uint8_t*>(packed_scales) +
-                                     (nv ? 0 : round_up(G * N * 8, 256)));
+                                     (nv ? 0 : round_up(G / 2 * N * 8, 256)));
   if (nv)
     SVDQ_TRY(hip_check(svdq::launch_pack_nvfp4(codes, static_cast<const uint8_t*>(scales),
                                                 reinterpret_cast<uint16_t*>(packed_codes), flag,
