@@ -241,25 +241,29 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   // LDS byte addresses of a ring slot with the lane, wave and slot parts folded in,
   // formed once per stage and hidden from the optimizer (an empty asm), so that each
   // read below is one of these registers plus an immediate offset
-  struct Bases { uint32_t a16, a8, b16, b8, sa, sb; };
+  struct Bases { uint32_t a16, a8, a8b, b16, b8, sa, sb; };
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)ring;
   auto bases = [&](int sl) {
     Bases r;
     const uint32_t so = ring0 + sl * SLOT * 4;
     r.a16 = so + (wm * 4 * 384 + lane * 4) * 4;
     r.a8 = so + (wm * 4 * 384 + 256 + lane * 2) * 4;
+    r.a8b = r.a8 + 2 * 384 * 4;
     r.b16 = so + (ASZ + wn * WN * 2 * 384 + lane * 4) * 4;
     r.b8 = so + (ASZ + wn * WN * 2 * 384 + 256 + lane * 2) * 4;
     r.sa = so + (ASZ + BSZ + 2 * (wm * 64 + lr)) * 4;
     r.sb = so + (ASZ + BSZ + 4 * BM + 2 * (wn * WN * 32 + lr)) * 4;
-    asm volatile("" : "+v"(r.a16), "+v"(r.a8), "+v"(r.b16), "+v"(r.b8), "+v"(r.sa), "+v"(r.sb));
+    // a8b (the second A row-block's 8-byte halves) is a register of its own, so the two
+    // halves are not merged into one ds_read2 whose result would need moves
+    asm volatile("" : "+v"(r.a16), "+v"(r.a8), "+v"(r.a8b), "+v"(r.b16), "+v"(r.b8), "+v"(r.sa),
+                 "+v"(r.sb));
     return r;
   };
   typedef __attribute__((address_space(3))) const v4i lds_v4i;
   typedef __attribute__((address_space(3))) const v2i lds_v2i;
-  auto frag = [&](uint32_t p16, uint32_t p8, int off) {
-    const v4i lo = *(lds_v4i*)(uintptr_t)(p16 + off * 4);
-    const v2i hi = *(lds_v2i*)(uintptr_t)(p8 + off * 4);
+  auto frag = [&](uint32_t p16, int off16, uint32_t p8, int off8) {
+    const v4i lo = *(lds_v4i*)(uintptr_t)(p16 + off16 * 4);
+    const v2i hi = *(lds_v2i*)(uintptr_t)(p8 + off8 * 4);
     return (v8i)__builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2,
                                         3, 4, 5, -1, -1);
   };
@@ -271,13 +275,13 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   auto loadA = [&](int set, const Bases& q, int gl) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      fa[set][i] = frag(q.a16, q.a8, (i * 2 + gl) * 384);
+      fa[set][i] = frag(q.a16, (i * 2 + gl) * 384, i == 0 ? q.a8 : q.a8b, gl * 384);
       fsa[set][i] = *(lds_v2i*)(uintptr_t)(q.sa + (gl * BM + 32 * i) * 8);
     }
   };
   auto loadB = [&](int k, const Bases& q) {
     const int gl = k / WN, j = k % WN;
-    fb[k % NBS] = frag(q.b16, q.b8, (j * 2 + gl) * 384);
+    fb[k % NBS] = frag(q.b16, (j * 2 + gl) * 384, q.b8, (j * 2 + gl) * 384);
     if (gl == 0) fsb[k % NBS] = *(lds_v2i*)(uintptr_t)(q.sb + j * 32 * 8);
     else if (NBS != WN) fsb[k % NBS] = fsb[(k - WN) % NBS];
   };
