@@ -162,7 +162,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
 
     def short(name):
         for key in ("k1_int4_fused", "k2_gemm_int4", "MulFunctor", "FillFunctor", "k_pack_int4",
-                    "k_pack_lora_down", "k_transpose", "k_zero_flag", "copyBuffer"):
+                    "k_pack_lora_down", "k_pair_scales", "k_zero_flag", "copyBuffer"):
             if key in name:
                 return key
         return name[:40]
