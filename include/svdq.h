@@ -157,6 +157,15 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w,
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
                              const uint16_t* x, int64_t M, uint16_t* y, hipStream_t stream);
 
+/* Exact GELU of n bf16 values (Diffusers docs "Nunchaku Lite", "Fused kernels": the
+ * activation of the DiT MLP between the MLP-up and MLP-down linears):
+ *   y[i] = bf16_rne( x[i]/2 * erfc(-x[i]/sqrt(2)) ),  computed in fp32 (erfcf).
+ * x, y: device pointers to n bf16 values, 16-byte aligned; y may equal x (in place),
+ * other overlaps are undefined.  n in [0, 2^36]; n = 0 launches nothing.  Errors:
+ * SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ALIGN, SVDQ_ERR_DEVICE, SVDQ_ERR_HIP.  Not
+ * recorded by the timing hook below.  Enqueued on `stream`. */
+svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
+
 /* Per-kernel timing, for measurement tools.  After svdq_timing_start(max_calls) and
  * until svdq_timing_stop, each svdq_w4a4_linear / awq_w4a16_linear call made on the
  * calling thread launches its kernels with a pair of HIP events that receive each

@@ -176,9 +176,11 @@ class PreparedBytes:
 
 
 def prepared_int4_bytes(config_id: int, K: int, N: int, rank: int = 32,
-                        outlier_count: int | None = None) -> PreparedBytes:
+                        outlier_count: int | None = None, layer: int = 0) -> PreparedBytes:
+    """``layer`` tells apart the layers of one config (a block chain); 0 for a single
+    layer."""
     sd = seeds(config_id)
-    rng = np.random.default_rng(sd.w + 500)
+    rng = np.random.default_rng(sd.w + 500 + 17 * layer)
     n_out = default_outlier_count(K) if outlier_count is None else outlier_count
     idx = outlier_channels(K, n_out, sd.outliers)
     smooth = rng.uniform(0.4, 0.6, K).astype(np.float32)
@@ -238,3 +240,24 @@ def prepared_awq_bytes(config_id: int, K: int, N: int) -> PreparedAwqBytes:
         scales=to_bf16_bits((0.003 * np.exp(0.1 * rng.standard_normal((N, K // 64)))).astype(np.float32)),
         zeros=rng.integers(0, 16, size=(N, K // 64), dtype=np.uint16).astype(np.uint8),
         bias=bias(N, seeds(config_id).bias))
+
+
+# The four W4A4 linears of one DiT block (hidden 3072, MLP 12288): name, K, N.
+CHAIN_LAYERS = (("qkv", 3072, 9216), ("out", 3072, 3072), ("up", 3072, 12288),
+                ("down", 12288, 3072))
+CHAIN_CONFIG = 5
+
+
+def chain_layer_bytes(rank: int = 32) -> dict:
+    """Prepared-layout bytes of the block's four int4 layers (config 5), one seed each."""
+    return {name: prepared_int4_bytes(CHAIN_CONFIG, K, N, rank, layer=i + 1)
+            for i, (name, K, N) in enumerate(CHAIN_LAYERS)}
+
+
+def chain_step_activations(M: int, step: int) -> np.ndarray:
+    """Fresh block input of denoise step ``step``: [M, 3072] bf16 bits, N(0, 1) with 1 %
+    outlier channels x30 (the same channels in every step)."""
+    sd = seeds(CHAIN_CONFIG)
+    K = CHAIN_LAYERS[0][1]
+    idx = outlier_channels(K, default_outlier_count(K), sd.outliers)
+    return activations(M, K, sd.step(step), idx, 30.0)

@@ -1,0 +1,86 @@
+"""The exact GELU kernel (every finite bf16 input) and the W4A4 linears of a DiT block
+called in sequence at the block's token counts (M = 4608 for one 1024x1024 image,
+18432 for four), each layer checked against the oracle on its own GPU input."""
+
+import numpy as np
+import pytest
+import torch
+
+import w4a4_rank_corrected_linear_amd as svdq
+from helpers import check_y, dev_bf16, dev_u8, host_bits
+from oracle import activation as A
+from oracle import formats as F
+from oracle import linear as OL
+from oracle import prep as P
+from synth import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _finite_bf16_patterns():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return b[((b >> 7) & 0xFF) != 0xFF]          # exponent all ones: inf / NaN
+
+
+def test_gelu_every_finite_bf16_input():
+    x = _finite_bf16_patterns()
+    y = host_bits(svdq.gelu(dev_bf16(x)))
+    _, ref = A.gelu_bf16(x)
+    d = F.bf16_ulp_distance(y, ref)
+    assert int(d.max()) <= 1, int(d.max())
+    assert np.mean(d == 0) > 0.999, float(np.mean(d == 0))
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 4103])
+def test_gelu_tail_lengths_and_in_place(n):
+    rng = np.random.default_rng(n)
+    x = F.bf16_rne((rng.standard_normal(n) * 3).astype(np.float32))
+    _, ref = A.gelu_bf16(x)
+    t = dev_bf16(x)
+    svdq.gelu(t, out=t)
+    assert int(F.bf16_ulp_distance(host_bits(t), ref).max()) <= 1
+
+
+def _oracle_layer(pb):
+    return P.SvdqLayer(precision="int4", K=pb.K, N=pb.N, rank=pb.rank, qweight=pb.qweight,
+                       wscales=pb.wscales, w_global=1.0, act_global=1.0, smooth=pb.smooth,
+                       lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+
+
+def _dev_layer(pb):
+    return svdq.SvdqLinear.from_interchange(dev_u8(pb.qweight), dev_bf16(pb.wscales),
+                                            dev_bf16(pb.smooth), dev_bf16(pb.lora_down),
+                                            dev_bf16(pb.lora_up), dev_bf16(pb.bias))
+
+
+@pytest.fixture(scope="module")
+def block():
+    pbs = I.chain_layer_bytes()
+    layers = {k: _oracle_layer(v) for k, v in pbs.items()}
+    dev = {k: _dev_layer(v) for k, v in pbs.items()}
+    return layers, svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"])
+
+
+@pytest.mark.parametrize("M,step", [(4608, 0), (18432, 3)])
+def test_block_chain_each_layer_on_its_gpu_input(block, M, step):
+    layers, chain = block
+    x = I.chain_step_activations(M, step)
+    r = chain(dev_bf16(x))
+    torch.cuda.synchronize()
+    out = {k: host_bits(v) for k, v in r.items()}
+    rows = np.unique(np.concatenate([np.arange(11, M, M // 13), [0, M - 1]]))
+    inputs = {"qkv": x, "out": x, "up": out["out"], "down": out["act"]}
+    for name in ("qkv", "out", "up", "down"):
+        ref = OL.w4a4_linear_rows("int4", inputs[name], layers[name], rows)
+        check_y(out[name][rows], ref["r"])
+    _, act_ref = A.gelu_bf16(out["up"][rows])
+    assert int(F.bf16_ulp_distance(out["act"][rows], act_ref).max()) <= 1
+    for v in out.values():
+        assert np.all(np.isfinite(F.bf16_to_f64(v)))
+
+
+def test_block_chain_steps_are_deterministic_and_distinct(block):
+    _, chain = block
+    a = [host_bits(chain(dev_bf16(I.chain_step_activations(4608, s)))["down"]).copy() for s in (0, 1, 0)]
+    assert np.array_equal(a[0], a[2])
+    assert not np.array_equal(a[0], a[1])

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     SvdqLinear,
     awq_w4a16_linear,
     check_device,
+    gelu,
     pack_lora_down,
     pack_weight,
     quantize_act,
@@ -22,3 +23,4 @@ from .api import (  # noqa: F401
     timing_stop,
     workspace_bytes,
 )
+from .chain import DitBlockChain  # noqa: F401

@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.svdq_w4a4_linear.restype = st
     L.awq_w4a16_linear.argtypes = [cfgp, ctypes.POINTER(AwqW4A16Weight), vp, i64, vp, vp]
     L.awq_w4a16_linear.restype = st
+    L.svdq_gelu_bf16.argtypes = [vp, vp, i64, vp]
+    L.svdq_gelu_bf16.restype = st
     L.svdq_timing_start.argtypes = [ctypes.c_int]
     L.svdq_timing_start.restype = st
     ip = ctypes.POINTER(ctypes.c_int)

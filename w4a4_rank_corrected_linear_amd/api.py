@@ -130,8 +130,12 @@ class SvdqLinear:
         ld = None if lora_down is None else pack_lora_down(lora_down, precision)
         return cls(2 * K2, N, pc, ps, smooth, ld, lora_up, bias, precision, w_global, act_global)
 
+    def workspace_bytes(self, M: int) -> int:
+        """svdq_workspace_bytes for M tokens of this layer (at least 256)."""
+        return max(int(L.lib().svdq_workspace_bytes(ctypes.byref(self.cfg), M, self.K)), 256)
+
     def workspace(self, M: int, device) -> torch.Tensor:
-        need = max(int(L.lib().svdq_workspace_bytes(ctypes.byref(self.cfg), M, self.K)), 256)
+        need = self.workspace_bytes(M)
         if self._ws is None or self._ws.numel() < need or self._ws.device != device:
             self._ws = torch.empty(need, dtype=torch.uint8, device=device)
         return self._ws
@@ -177,6 +181,15 @@ def awq_w4a16_linear(x: torch.Tensor, layer: AwqLinear, out: torch.Tensor | None
     st = L.lib().awq_w4a16_linear(ctypes.byref(layer.cfg), ctypes.byref(layer._w), _p(x), M, _p(y),
                                   _stream())
     L.check(st, "awq_w4a16_linear")
+    return y
+
+
+def gelu(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """svdq_gelu_bf16: exact (erf) GELU of a contiguous bf16 device tensor; `out` may
+    be `x` (in place)."""
+    _want(x, torch.bfloat16, "x")
+    y = torch.empty_like(x) if out is None else _want(out, torch.bfloat16, "out", tuple(x.shape))
+    L.check(L.lib().svdq_gelu_bf16(_p(x), _p(y), x.numel(), _stream()), "svdq_gelu_bf16")
     return y
 
 

@@ -1,0 +1,53 @@
+"""The W4A4 linears of one DiT transformer block, called in sequence.
+
+A block of the 1024x1024 DiT (3072 hidden, 4096 image + 512 text tokens) runs four
+svdq_w4a4 linears: the fused QKV projection 3072 -> 9216, the attention output
+projection 3072 -> 3072, and the MLP pair 3072 -> 12288 -> 3072 with an exact GELU
+between (Diffusers docs "Nunchaku Lite", "Fused kernels": the block's projections and
+its GELU MLP).  Attention itself, the norms and the residual adds are not part of the
+layer: the QKV output is produced for the attention that would consume it, and the
+output projection reads the block's input activations in place of the attention
+output.  Every step runs in the library's kernels; this module only orders the calls.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from .api import SvdqLinear, gelu
+
+
+class DitBlockChain:
+    """qkv, out, up, down: SvdqLinear layers of shapes 3072->9216, 3072->3072,
+    3072->12288 and 12288->3072 (any K/N that chain the same way)."""
+
+    def __init__(self, qkv: SvdqLinear, out: SvdqLinear, up: SvdqLinear, down: SvdqLinear):
+        if out.N != up.K or up.N != down.K or qkv.K != out.K:
+            raise ValueError("layer shapes do not chain: "
+                             f"qkv {qkv.K}->{qkv.N}, out {out.K}->{out.N}, up {up.K}->{up.N}, "
+                             f"down {down.K}->{down.N}")
+        self.qkv, self.out, self.up, self.down = qkv, out, up, down
+        self._buf = {}
+
+    def _tensor(self, name: str, shape, device, dtype=torch.bfloat16) -> torch.Tensor:
+        t = self._buf.get(name)
+        if t is None or tuple(t.shape) != tuple(shape) or t.device != device:
+            t = torch.empty(shape, dtype=dtype, device=device)
+            self._buf[name] = t
+        return t
+
+    def forward(self, x: torch.Tensor) -> dict:
+        """x [M, K] bf16 -> {"qkv", "out", "up", "act", "down"}; the buffers are reused
+        by the next call of the same M (copy what must outlive it)."""
+        M, dev = x.shape[0], x.device
+        need = max(layer.workspace_bytes(M) for layer in (self.qkv, self.out, self.up, self.down))
+        ws = self._tensor("ws", (need,), dev, torch.uint8)   # one workspace, calls run in order
+        r = {}
+        r["qkv"] = self.qkv(x, out=self._tensor("qkv", (M, self.qkv.N), dev), workspace=ws)
+        r["out"] = self.out(x, out=self._tensor("out", (M, self.out.N), dev), workspace=ws)
+        r["up"] = self.up(r["out"], out=self._tensor("up", (M, self.up.N), dev), workspace=ws)
+        r["act"] = gelu(r["up"], out=self._tensor("act", (M, self.up.N), dev))
+        r["down"] = self.down(r["act"], out=self._tensor("down", (M, self.down.N), dev), workspace=ws)
+        return r
+
+    __call__ = forward

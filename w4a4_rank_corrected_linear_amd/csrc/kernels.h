@@ -11,8 +11,8 @@
 namespace svdq {
 
 // The fused quantizers split K into pieces of at most kK1SplitK values, one
-// workgroup column each; each piece writes its own partial U [M_pad][r] and the GEMM
-// epilogue adds the pieces in order.
+// workgroup column each; each piece writes its own partial U (fragment layout of
+// common.h) and the GEMM adds the pieces in order.
 constexpr int kK1SplitK = 1536;
 inline int k1_splits(int K) { return (K + kK1SplitK - 1) / kK1SplitK; }
 
@@ -48,5 +48,7 @@ hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
                             void* out_scales, int* flag, int N, int K, hipStream_t st);
+
+hipError_t launch_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t st);
 
 }  // namespace svdq

@@ -396,6 +396,18 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, 
   return ok();
 }
 
+svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream) {
+  if (!x || !y) return fail(SVDQ_ERR_NULL, "svdq_gelu_bf16: NULL argument");
+  if (n < 0 || n > (int64_t(1) << 36))
+    return fail(SVDQ_ERR_SHAPE, "svdq_gelu_bf16: n = %lld out of [0, 2^36]", (long long)n);
+  if (!aligned16(x) || !aligned16(y))
+    return fail(SVDQ_ERR_ALIGN, "svdq_gelu_bf16: pointers must be 16-byte aligned");
+  if (n == 0) return ok();
+  SVDQ_TRY(check_current_device());
+  SVDQ_TRY(hip_check(svdq::launch_gelu_bf16(x, y, n, stream), "gelu kernel launch"));
+  return ok();
+}
+
 svdq_status svdq_timing_start(int max_calls) {
   if (max_calls < 1 || max_calls > 65536)
     return fail(SVDQ_ERR_SHAPE, "svdq_timing_start: max_calls = %d out of [1, 65536]", max_calls);
