@@ -136,6 +136,103 @@ def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 8):
                       f"{t:.3f} s (float64 numpy/BLAS)"}
 
 
+def run_chain(args) -> int:
+    """One DiT block's four W4A4 linears and the GELU per denoise step (config 5): the
+    steps cycle through 8 fresh seeded inputs resident in HBM; K timed steps, then an
+    instrumented pass with an event pair around every call for the per-layer times."""
+    import numpy as np
+    import torch
+    import w4a4_rank_corrected_linear_amd as svdq
+    from synth import inputs as I
+
+    dev = torch.device("cuda:0")
+    M = 4608 * args.batch
+
+    def bf16(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+        return t.view(torch.bfloat16).to(dev)
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
+
+    pbs = I.chain_layer_bytes()
+    lay = {k: svdq.SvdqLinear.from_interchange(u8(pb.qweight), bf16(pb.wscales), bf16(pb.smooth),
+                                               bf16(pb.lora_down), bf16(pb.lora_up), bf16(pb.bias))
+           for k, pb in pbs.items()}
+    chain = svdq.DitBlockChain(lay["qkv"], lay["out"], lay["up"], lay["down"])
+    xs = [bf16(I.chain_step_activations(M, s)) for s in range(8)]
+    print(f"[bench] workload chain: DiT block (QKV, out, MLP-up, GELU, MLP-down), M={M}, 8 fresh "
+          f"step inputs; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        chain(xs[i % 8])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        chain(xs[i % 8])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-layer times: events around each call on the current stream (they include the
+    # dispatch of the call's kernels)
+    names = ["qkv", "out", "up", "gelu", "down"]
+    n_inst = min(args.steps, 200)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in names] for _ in range(n_inst)]
+    ws = torch.empty(max(l.workspace_bytes(M) for l in lay.values()), dtype=torch.uint8, device=dev)
+    bufs = {"qkv": torch.empty((M, lay["qkv"].N), dtype=torch.bfloat16, device=dev),
+            "out": torch.empty((M, lay["out"].N), dtype=torch.bfloat16, device=dev),
+            "up": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
+            "act": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
+            "down": torch.empty((M, lay["down"].N), dtype=torch.bfloat16, device=dev)}
+    calls = [lambda x: lay["qkv"](x, out=bufs["qkv"], workspace=ws),
+             lambda x: lay["out"](x, out=bufs["out"], workspace=ws),
+             lambda x: lay["up"](bufs["out"], out=bufs["up"], workspace=ws),
+             lambda x: svdq.gelu(bufs["up"], out=bufs["act"]),
+             lambda x: lay["down"](bufs["act"], out=bufs["down"], workspace=ws)]
+    for i in range(n_inst):
+        for j, c in enumerate(calls):
+            ev[i][j][0].record()
+            c(xs[i % 8])
+            ev[i][j][1].record()
+    torch.cuda.synchronize()
+    per = {n: sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n_inst)) / n_inst
+           for j, n in enumerate(names)}
+
+    shapes = {n: (K, N) for n, K, N in I.CHAIN_LAYERS}
+    ops_step = sum(2.0 * M * K * N for K, N in shapes.values())
+    ms_per_step = wall * 1e3 / args.steps
+    value = ops_step / (ms_per_step * 1e-3) / 1e12
+    layers = {n: {"ms": round(per[n], 6),
+                  **({"TOPS": round(2.0 * M * shapes[n][0] * shapes[n][1] / (per[n] * 1e-3) / 1e12, 3)}
+                     if n in shapes else {"GBps": round(4.0 * M * shapes["up"][1] / (per[n] * 1e-3) / 1e9, 1)})}
+              for n in names}
+    out = {
+        "metric": f"DiT block chain of svdq_w4a4 int4 linears (QKV, out, MLP-up, GELU, MLP-down) "
+                  f"effective TOPS at M={M}",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": f"chain: DiT block, batch {args.batch} (M={M}), 8 fresh step inputs "
+                               "cycled, int4 g64 rank 32",
+                   "M": M, "layers": {n: {"K": K, "N": N} for n, (K, N) in shapes.items()},
+                   "seeds": {"steps": [I.seeds(I.CHAIN_CONFIG).step(s) for s in range(8)]}},
+        "chain_8_steps_ms": round(8 * ms_per_step, 6),
+        "layers": layers,
+        "sum_of_call_ms": round(sum(per.values()), 6),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 PROFILE_CMDS = {
     "stats": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_stats "
              "-o run --output-format csv -- python3 <repo>/bench.py --no-cpu-baseline",
@@ -224,7 +321,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS) + ["chain"])
+    ap.add_argument("--batch", type=int, default=1, choices=[1, 4],
+                    help="chain workload: images per step (M = 4608 per image)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (scale reference for HBM counters)")
@@ -249,6 +348,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     svdq.check_device(0)
+    if args.workload == "chain":
+        return run_chain(args)
 
     inp = make_inputs(args.workload)
     method = inp["method"]
