@@ -79,7 +79,13 @@ struct QuantInt4Fused {
       ev[j] = cq[2 * j];
       od[j] = cq[2 * j + 1];
     }
-    const v6i f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+    // The converter reads its 32 sources over several passes while writing its six
+    // results, so the results must not share registers with the sources: the builtin
+    // lets the register allocator place them overlapping (seen at an offset of two
+    // registers, which corrupts codes), the early-clobber output of the asm does not.
+    v6i f6;
+    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3"
+                 : "=&v"(f6) : "v"(ev), "v"(od), "s"(8.0f));
     // GEMM A-operand layout: chunk (row-block, group) of 1536 B; lane slot
     // h*32 + row%32 holds dwords 0-3 at slot*16 and dwords 4-5 at 1024 + slot*8.
     uint8_t* chunk = a.out + ((size_t)(row >> 5) * (a.K >> 6) + g) * 1536;
