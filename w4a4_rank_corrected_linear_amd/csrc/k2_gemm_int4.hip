@@ -154,6 +154,21 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     }
   };
 
+  // Copies for the late low-rank term: k-split sp of the tile's U (fragment layout: the
+  // 8 row blocks are contiguous, rank KiB) to the start of slot sl, and with split 0
+  // lora_up's BN rows (BN * rank * 2 bytes) after it.  1 KiB per copy instruction,
+  // spread over the 8 waves.
+  auto seed_copy = [&](int sp, int sl) {
+    const uint8_t* u = reinterpret_cast<const uint8_t*>(U + u_frag_index(sp, row0, 0, M_pad, rank));
+    const uint32_t dst = lds_addr(ring + sl * SLOT);
+    for (int p = wave; p < rank; p += 8) dma16(voff, u + p * 1024, dst + p * 1024);
+    if (sp == 0) {
+      const uint8_t* l = reinterpret_cast<const uint8_t*>(L2t + (size_t)col0 * rank);
+      for (int p = wave; p < BN * rank / 512; p += 8)
+        dma16(voff, l + p * 1024, dst + rank * 1024 + p * 1024);
+    }
+  };
+
   dma(0, 0);
   if (1 < S) dma(1, 1);
 
@@ -165,10 +180,14 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Low-rank seed acc^T = L2t U^T.  U (fp32, the sum of the quantizer's k-split
+  // Low-rank term acc^T += L2t U^T.  U (fp32, the sum of the quantizer's k-split
   // partials in split order) is split into bf16 hi + lo; u - hi is exact in fp32 and
-  // what lo drops is below 2^-17 |u|.  rank <= 32: at most two 16-rank slices.
-  if (rank > 0) {
+  // what lo drops is below 2^-17 |u|.  rank <= 32: at most two 16-rank slices.  With at
+  // most two k-splits and three stages or more, U and lora_up are copied into the ring
+  // slots that the last two stages leave free and the term is added in the epilogue;
+  // otherwise it seeds the accumulator here, from global memory.
+  const bool late_seed = rank > 0 && nsplit <= 2 && S >= 3;
+  if (rank > 0 && !late_seed) {
     uint4 lbv[2][WN];
     float uf[2][2][8];
 #pragma unroll
@@ -340,6 +359,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       barrier_lds();
     }
     if (t + 2 < S) dma(t + 2, (t + 2) % 3);
+    else if (late_seed) seed_copy(0, (t + 2) % 3);
     __builtin_amdgcn_sched_barrier(0);
     const Bases cq = bases(t % 3), nq = bases((t + 1) % 3);
 #pragma unroll
@@ -351,8 +371,10 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       wait_vm0();
       barrier_lds();
     }
-    // the tile's bias goes to LDS under the last stage (wave 0, 16 B per lane)
+    // the tile's bias goes to LDS under the last stage (wave 0, 16 B per lane), and
+    // the second k-split of U to the slot stage t-1 has just freed
     if (bias && wave == 0 && lane < BN / 8) dma16(voff, bias + col0, lds_addr(bias_s));
+    if (late_seed && nsplit == 2) seed_copy(1, (t + 2) % 3);
     const Bases cq = bases(t % 3);
 #pragma unroll
     for (int b = 0; b < NB; ++b) step(b, cq, cq, false);
@@ -369,6 +391,44 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   // contiguous run of full 64-byte sectors.
   wait_vm0();
   barrier_lds();
+  if (late_seed) {
+    // split 0 and lora_up were copied at the top of stage S-2 into slot S % 3, split 1
+    // at the top of stage S-1 into slot (S+1) % 3
+    typedef __attribute__((address_space(3))) const v4f lds_f4;
+    const uint32_t s0 = lds_addr(ring + (S % 3) * SLOT), s1 = lds_addr(ring + ((S + 1) % 3) * SLOT);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (16 * kk < rank) {
+        v8bf uh[2], ul[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t o = ((wm * 2 + i) * (rank >> 4) + kk) * 2048 + lane * 16;
+          v4f a0 = *(lds_f4*)(uintptr_t)(s0 + o), a1 = *(lds_f4*)(uintptr_t)(s0 + o + 1024);
+          if (nsplit == 2) {
+            a0 += *(lds_f4*)(uintptr_t)(s1 + o);
+            a1 += *(lds_f4*)(uintptr_t)(s1 + o + 1024);
+          }
+          const float uf[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            uh[i][q] = (__bf16)uf[q];
+            ul[i][q] = (__bf16)(uf[q] - (float)uh[i][q]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const uint32_t lo = s0 + rank * 1024 + ((wn * WN + j) * 32 + lr) * rank * 2 + kk * 32 + lh * 16;
+          const v8bf lv = __builtin_bit_cast(v8bf, *(lds_v4i*)(uintptr_t)lo);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, uh[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, ul[i], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+    barrier_lds();  // the staging tiles below overwrite the seed copies
+  }
   uint16_t* tile = reinterpret_cast<uint16_t*>(ring) + wave * (64 * (BN / 2 + 8));
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
