@@ -159,7 +159,8 @@ def run_chain(args) -> int:
     lay = {k: svdq.SvdqLinear.from_interchange(u8(pb.qweight), bf16(pb.wscales), bf16(pb.smooth),
                                                bf16(pb.lora_down), bf16(pb.lora_up), bf16(pb.bias))
            for k, pb in pbs.items()}
-    chain = svdq.DitBlockChain(lay["qkv"], lay["out"], lay["up"], lay["down"])
+    chain = svdq.DitBlockChain(lay["qkv"], lay["out"], lay["up"], lay["down"],
+                               fuse_gelu=args.fuse_gelu)
     xs = [bf16(I.chain_step_activations(M, s)) for s in range(8)]
     print(f"[bench] workload chain: DiT block (QKV, out, MLP-up, GELU, MLP-down), M={M}, 8 fresh "
           f"step inputs; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
@@ -174,7 +175,7 @@ def run_chain(args) -> int:
 
     # per-layer times: events around each call on the current stream (they include the
     # dispatch of the call's kernels)
-    names = ["qkv", "out", "up", "gelu", "down"]
+    names = ["qkv", "out", "up", "down"] if args.fuse_gelu else ["qkv", "out", "up", "gelu", "down"]
     n_inst = min(args.steps, 200)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in names] for _ in range(n_inst)]
@@ -185,10 +186,13 @@ def run_chain(args) -> int:
             "act": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
             "down": torch.empty((M, lay["down"].N), dtype=torch.bfloat16, device=dev)}
     calls = [lambda x: lay["qkv"](x, out=bufs["qkv"], workspace=ws),
-             lambda x: lay["out"](x, out=bufs["out"], workspace=ws),
-             lambda x: lay["up"](bufs["out"], out=bufs["up"], workspace=ws),
-             lambda x: svdq.gelu(bufs["up"], out=bufs["act"]),
-             lambda x: lay["down"](bufs["act"], out=bufs["down"], workspace=ws)]
+             lambda x: lay["out"](x, out=bufs["out"], workspace=ws)]
+    if args.fuse_gelu:
+        calls.append(lambda x: lay["up"](bufs["out"], out=bufs["act"], workspace=ws, gelu=True))
+    else:
+        calls += [lambda x: lay["up"](bufs["out"], out=bufs["up"], workspace=ws),
+                  lambda x: svdq.gelu(bufs["up"], out=bufs["act"])]
+    calls.append(lambda x: lay["down"](bufs["act"], out=bufs["down"], workspace=ws))
     for i in range(n_inst):
         for j, c in enumerate(calls):
             ev[i][j][0].record()
@@ -208,7 +212,7 @@ def run_chain(args) -> int:
               for n in names}
     out = {
         "metric": f"DiT block chain of svdq_w4a4 int4 linears (QKV, out, MLP-up, GELU, MLP-down) "
-                  f"effective TOPS at M={M}",
+                  f"effective TOPS at M={M}" + (", GELU fused into MLP-up" if args.fuse_gelu else ""),
         "value": round(value, 3),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -221,7 +225,8 @@ def run_chain(args) -> int:
         "dtype": "int4",
         "data": "synthetic",
         "config": {"workload": f"chain: DiT block, batch {args.batch} (M={M}), 8 fresh step inputs "
-                               "cycled, int4 g64 rank 32",
+                               "cycled, int4 g64 rank 32" + (", GELU in the MLP-up epilogue"
+                                                             if args.fuse_gelu else ""),
                    "M": M, "layers": {n: {"K": K, "N": N} for n, (K, N) in shapes.items()},
                    "seeds": {"steps": [I.seeds(I.CHAIN_CONFIG).step(s) for s in range(8)]}},
         "chain_8_steps_ms": round(8 * ms_per_step, 6),
@@ -324,6 +329,8 @@ def main() -> int:
     ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS) + ["chain"])
     ap.add_argument("--batch", type=int, default=1, choices=[1, 4],
                     help="chain workload: images per step (M = 4608 per image)")
+    ap.add_argument("--fuse-gelu", action="store_true",
+                    help="chain workload: GELU in the MLP-up GEMM's epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (scale reference for HBM counters)")

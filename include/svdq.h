@@ -152,6 +152,16 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w,
                              const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same call with the exact GELU applied to each fp32 result before the single bf16
+ * rounding (Diffusers docs "Nunchaku Lite", "Fused kernels": the DiT MLP's GELU fused
+ * into its first projection):
+ *   Y = bf16( gelu(r) ),  gelu(v) = v/2 * erfc(-v/sqrt(2)) in fp32 (erfc to ~1e-7),
+ * with r the svdq_w4a4_linear result before rounding.  Arguments, layouts, ownership
+ * and errors as for svdq_w4a4_linear. */
+svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                  const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* The AWQ W4A16 comparison layer: Y[M][N] (bf16) from bf16 X[M][K].  cfg must be
  * {int4, 64, rank 0, bf16}. */
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
@@ -159,7 +169,8 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
 
 /* Exact GELU of n bf16 values (Diffusers docs "Nunchaku Lite", "Fused kernels": the
  * activation of the DiT MLP between the MLP-up and MLP-down linears):
- *   y[i] = bf16_rne( x[i]/2 * erfc(-x[i]/sqrt(2)) ),  computed in fp32 (erfcf).
+ *   y[i] = bf16_rne( x[i]/2 * erfc(-x[i]/sqrt(2)) ),  computed in fp32, erfc accurate to
+ *   about 1e-7 relative (within 1 bf16 ulp of the exact value).
  * x, y: device pointers to n bf16 values, 16-byte aligned; y may equal x (in place),
  * other overlaps are undefined.  n in [0, 2^36]; n = 0 launches nothing.  Errors:
  * SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ALIGN, SVDQ_ERR_DEVICE, SVDQ_ERR_HIP.  Not

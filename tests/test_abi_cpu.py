@@ -176,3 +176,17 @@ def test_pack_lora_down_argument_rules():
     assert lib.svdq_pack_lora_down(ctypes.byref(cfg(rank=0)), 512, FAKE, FAKE, None) == L.ERR_CONFIG
     assert lib.svdq_pack_lora_down(ctypes.byref(cfg()), 500, FAKE, FAKE, None) == L.ERR_SHAPE
     assert lib.svdq_pack_lora_down(ctypes.byref(cfg()), 512, FAKE_MISALIGNED, FAKE, None) == L.ERR_ALIGN
+
+
+def test_gelu_entry_points_validate_like_the_linear():
+    lib = L.lib()
+    c, w = cfg(), weight()
+    args = lambda x=FAKE, M=16: (ctypes.byref(c), ctypes.byref(w), x, M, 1.0, FAKE, FAKE, 1 << 30, None)
+    assert lib.svdq_w4a4_linear_gelu(*args(x=None)) == L.ERR_NULL
+    assert lib.svdq_w4a4_linear_gelu(*args(x=FAKE_MISALIGNED)) == L.ERR_ALIGN
+    assert lib.svdq_w4a4_linear_gelu(*args(M=0)) == L.OK
+    assert "svdq_w4a4_linear_gelu" in (lib.svdq_w4a4_linear_gelu(*args(x=None)) and L.last_error())
+    assert lib.svdq_gelu_bf16(None, FAKE, 8, None) == L.ERR_NULL
+    assert lib.svdq_gelu_bf16(FAKE_MISALIGNED, FAKE, 8, None) == L.ERR_ALIGN
+    assert lib.svdq_gelu_bf16(FAKE, FAKE, -1, None) == L.ERR_SHAPE
+    assert lib.svdq_gelu_bf16(FAKE, FAKE, 0, None) == L.OK

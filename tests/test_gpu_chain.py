@@ -58,12 +58,12 @@ def block():
     pbs = I.chain_layer_bytes()
     layers = {k: _oracle_layer(v) for k, v in pbs.items()}
     dev = {k: _dev_layer(v) for k, v in pbs.items()}
-    return layers, svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"])
+    return layers, svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"]), dev
 
 
 @pytest.mark.parametrize("M,step", [(4608, 0), (18432, 3)])
 def test_block_chain_each_layer_on_its_gpu_input(block, M, step):
-    layers, chain = block
+    layers, chain, _ = block
     x = I.chain_step_activations(M, step)
     r = chain(dev_bf16(x))
     torch.cuda.synchronize()
@@ -80,7 +80,25 @@ def test_block_chain_each_layer_on_its_gpu_input(block, M, step):
 
 
 def test_block_chain_steps_are_deterministic_and_distinct(block):
-    _, chain = block
+    _, chain, _ = block
     a = [host_bits(chain(dev_bf16(I.chain_step_activations(4608, s)))["down"]).copy() for s in (0, 1, 0)]
     assert np.array_equal(a[0], a[2])
     assert not np.array_equal(a[0], a[1])
+
+
+def test_block_chain_with_gelu_fused_into_mlp_up(block):
+    """MLP-up with the GELU in its epilogue: gelu of the unrounded result, rounded once,
+    against the oracle's gelu(r) on the layer's GPU input; the other layers as before."""
+    layers, _, dev = block
+    chain = svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"], fuse_gelu=True)
+    M = 4608
+    x = I.chain_step_activations(M, 5)
+    r = chain(dev_bf16(x))
+    torch.cuda.synchronize()
+    out = {k: host_bits(v) for k, v in r.items()}
+    assert "up" not in out
+    rows = np.unique(np.concatenate([np.arange(7, M, M // 11), [0, M - 1]]))
+    ref_up = OL.w4a4_linear_rows("int4", out["out"], layers["up"], rows)["r"]
+    check_y(out["act"][rows], A.gelu_f64(ref_up))
+    ref_down = OL.w4a4_linear_rows("int4", out["act"], layers["down"], rows)["r"]
+    check_y(out["down"][rows], ref_down)

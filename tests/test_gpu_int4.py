@@ -10,6 +10,7 @@ import w4a4_rank_corrected_linear_amd as svdq
 from helpers import (check_u, check_y, decode_fp6_operand, dev_bf16, pair_scale_records, scale_records,
                      u_partials,
                      dev_u8, host_bits, int4_interchange)
+from oracle import activation as A
 from oracle import formats as F
 from oracle import linear as OL
 from oracle import prep as P
@@ -105,6 +106,15 @@ def test_linear_tiny(tiny, M):
     y = dl(dev_bf16(li.x[:M]))
     ref = OL.w4a4_linear("int4", li.x[:M], layer)
     check_y(host_bits(y), ref["r"])
+
+
+@pytest.mark.parametrize("M", [256, 37])
+def test_linear_gelu_epilogue(tiny, M):
+    """svdq_w4a4_linear_gelu: the exact GELU of the unrounded result, rounded once,
+    against the oracle's gelu(r) (128-wide tiles here; the chain test covers 192)."""
+    li, layer = tiny
+    y = _layer_dev(layer)(dev_bf16(li.x[:M]), gelu=True)
+    check_y(host_bits(y), A.gelu_f64(OL.w4a4_linear("int4", li.x[:M], layer)["r"]))
 
 
 def test_linear_rank0_no_bias_and_rank16():

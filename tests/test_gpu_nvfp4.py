@@ -8,6 +8,7 @@ import torch
 
 import w4a4_rank_corrected_linear_amd as svdq
 from helpers import check_u, check_y, dev_bf16, dev_u8, host_bits
+from oracle import activation as A
 from oracle import formats as F
 from oracle import linear as OL
 from oracle import prep as P
@@ -126,6 +127,12 @@ def test_linear_nvfp4_tiny(tiny, M):
     li, layer = tiny
     y = _layer_dev(layer)(dev_bf16(li.x[:M]))
     check_y(host_bits(y), OL.w4a4_linear("nvfp4", li.x[:M], layer)["r"])
+
+
+def test_linear_nvfp4_gelu_epilogue(tiny):
+    li, layer = tiny
+    y = _layer_dev(layer)(dev_bf16(li.x), gelu=True)
+    check_y(host_bits(y), A.gelu_f64(OL.w4a4_linear("nvfp4", li.x, layer)["r"]))
 
 
 def test_linear_nvfp4_rank0_no_bias_and_rank16():

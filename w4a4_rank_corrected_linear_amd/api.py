@@ -141,7 +141,10 @@ class SvdqLinear:
         return self._ws
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, act_global: float | None = None):
+                workspace: torch.Tensor | None = None, act_global: float | None = None,
+                gelu: bool = False):
+        """y = layer(x); with gelu=True the exact GELU of each result is taken before the
+        bf16 rounding (svdq_w4a4_linear_gelu)."""
         _want(x, torch.bfloat16, "x")
         M, K = x.shape
         if K != self.K:
@@ -149,9 +152,10 @@ class SvdqLinear:
         y = torch.empty((M, self.N), dtype=torch.bfloat16, device=x.device) if out is None else out
         ws = self.workspace(M, x.device) if workspace is None else workspace
         g = self.act_global if act_global is None else float(act_global)
-        st = L.lib().svdq_w4a4_linear(ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), M, g,
-                                      _p(y), _p(ws), ws.numel(), _stream())
-        L.check(st, "svdq_w4a4_linear")
+        fn = "svdq_w4a4_linear_gelu" if gelu else "svdq_w4a4_linear"
+        st = getattr(L.lib(), fn)(ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), M, g,
+                                  _p(y), _p(ws), ws.numel(), _stream())
+        L.check(st, fn)
         return y
 
     __call__ = forward

@@ -7,7 +7,9 @@ between (Diffusers docs "Nunchaku Lite", "Fused kernels": the block's projection
 its GELU MLP).  Attention itself, the norms and the residual adds are not part of the
 layer: the QKV output is produced for the attention that would consume it, and the
 output projection reads the block's input activations in place of the attention
-output.  Every step runs in the library's kernels; this module only orders the calls.
+output.  The GELU runs either as its own kernel or fused into the MLP-up GEMM's
+epilogue (on the fp32 result, before the bf16 rounding).  Every step runs in the
+library's kernels; this module only orders the calls.
 """
 
 from __future__ import annotations
@@ -21,12 +23,14 @@ class DitBlockChain:
     """qkv, out, up, down: SvdqLinear layers of shapes 3072->9216, 3072->3072,
     3072->12288 and 12288->3072 (any K/N that chain the same way)."""
 
-    def __init__(self, qkv: SvdqLinear, out: SvdqLinear, up: SvdqLinear, down: SvdqLinear):
+    def __init__(self, qkv: SvdqLinear, out: SvdqLinear, up: SvdqLinear, down: SvdqLinear,
+                 fuse_gelu: bool = False):
         if out.N != up.K or up.N != down.K or qkv.K != out.K:
             raise ValueError("layer shapes do not chain: "
                              f"qkv {qkv.K}->{qkv.N}, out {out.K}->{out.N}, up {up.K}->{up.N}, "
                              f"down {down.K}->{down.N}")
         self.qkv, self.out, self.up, self.down = qkv, out, up, down
+        self.fuse_gelu = fuse_gelu
         self._buf = {}
 
     def _tensor(self, name: str, shape, device, dtype=torch.bfloat16) -> torch.Tensor:
@@ -37,16 +41,21 @@ class DitBlockChain:
         return t
 
     def forward(self, x: torch.Tensor) -> dict:
-        """x [M, K] bf16 -> {"qkv", "out", "up", "act", "down"}; the buffers are reused
-        by the next call of the same M (copy what must outlive it)."""
+        """x [M, K] bf16 -> {"qkv", "out", "up", "act", "down"} ("up" absent when the GELU
+        is fused into MLP-up's epilogue); the buffers are reused by the next call of the
+        same M (copy what must outlive it)."""
         M, dev = x.shape[0], x.device
         need = max(layer.workspace_bytes(M) for layer in (self.qkv, self.out, self.up, self.down))
         ws = self._tensor("ws", (need,), dev, torch.uint8)   # one workspace, calls run in order
         r = {}
         r["qkv"] = self.qkv(x, out=self._tensor("qkv", (M, self.qkv.N), dev), workspace=ws)
         r["out"] = self.out(x, out=self._tensor("out", (M, self.out.N), dev), workspace=ws)
-        r["up"] = self.up(r["out"], out=self._tensor("up", (M, self.up.N), dev), workspace=ws)
-        r["act"] = gelu(r["up"], out=self._tensor("act", (M, self.up.N), dev))
+        if self.fuse_gelu:
+            r["act"] = self.up(r["out"], out=self._tensor("act", (M, self.up.N), dev), workspace=ws,
+                               gelu=True)
+        else:
+            r["up"] = self.up(r["out"], out=self._tensor("up", (M, self.up.N), dev), workspace=ws)
+            r["act"] = gelu(r["up"], out=self._tensor("act", (M, self.up.N), dev))
         r["down"] = self.down(r["act"], out=self._tensor("down", (M, self.down.N), dev), workspace=ws)
         return r
 

@@ -63,6 +63,42 @@ __device__ __forceinline__ uint32_t e2m3_field(int q) {
 
 __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+// exp(y) for y <= 0 with a two-part reduction: y = n ln2 + r, |r| <= ln2/2, ln2 split
+// into a 12-bit head (n ln2_hi exact) and a tail; exp(r) = 2^(r log2 e) on the hardware
+// exponential (its argument stays within 1/2, so the product's rounding is negligible),
+// then the exponent n by ldexp, which also yields fp32 subnormals below FLT_MIN.
+__device__ __forceinline__ float exp_nonpos(float y) {
+  const float n = __builtin_rintf(y * 1.4426950408889634f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, y);
+  r = __builtin_fmaf(-n, 1.4286068203094173e-6f, r);
+  return __builtin_ldexpf(__builtin_amdgcn_exp2f(r * 1.4426950408889634f), (int)n);
+}
+
+// erfc(z) for z >= 0 after Numerical Recipes' erfcc (Press et al., "Incomplete Gamma
+// Function, Error Function ...", Chebyshev-fitted: erfc(z) = t exp(-z^2 + P(t)),
+// t = 1 / (1 + z/2), fractional error below 1.2e-7 everywhere).
+__device__ __forceinline__ float erfc_nonneg(float z) {
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = __builtin_fmaf(p, t, -0.82215223f);
+  p = __builtin_fmaf(p, t, 1.48851587f);
+  p = __builtin_fmaf(p, t, -1.13520398f);
+  p = __builtin_fmaf(p, t, 0.27886807f);
+  p = __builtin_fmaf(p, t, -0.18628806f);
+  p = __builtin_fmaf(p, t, 0.09678418f);
+  p = __builtin_fmaf(p, t, 0.37409196f);
+  p = __builtin_fmaf(p, t, 1.00002368f);
+  p = __builtin_fmaf(p, t, -1.26551223f);
+  return t * exp_nonpos(fmaxf(__builtin_fmaf(-z, z, p), -200.0f));
+}
+
+// Exact (erf) GELU in fp32: v Phi(v) = v/2 * erfc(-v/sqrt 2); erfc of the negative
+// argument is 2 - erfc(|.|), so the v < 0 side keeps its relative accuracy.
+__device__ __forceinline__ float gelu_f32(float v) {
+  const float e = erfc_nonneg(fabsf(v) * 0.70710678118654752f);
+  return 0.5f * v * (v < 0.f ? e : 2.0f - e);
+}
+
 // Index (in floats) of U[split][row][j] in the fragment layout above.
 __host__ __device__ __forceinline__ size_t u_frag_index(int split, int row, int j, int M_pad,
                                                         int rank) {

@@ -23,6 +23,7 @@
 
 namespace svdq {
 
+template <bool GELU>
 __global__ void __launch_bounds__(256, 2)
 k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int nsplit,
              const uint16_t* __restrict__ B, const uint16_t* __restrict__ L2t,
@@ -142,7 +143,8 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
-        tile[rin * 40 + lr] = (uint16_t)f32_to_bf16_rne(c[e] + bv);
+        const float v = c[e] + bv;
+        tile[rin * 40 + lr] = (uint16_t)f32_to_bf16_rne(GELU ? gelu_f32(v) : v);
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -158,11 +160,11 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
 
 hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
                           const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
-                          int N, int K, int M_pad, int rank, hipStream_t st, hipEvent_t ev0,
-                          hipEvent_t ev1) {
+                          int N, int K, int M_pad, int rank, bool gelu, hipStream_t st,
+                          hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((N / 128) * (M_pad / 128));
-  hipExtLaunchKernelGGL(k2_gemm_bf16, grid, dim3(256), 0, st, ev0, ev1, 0, A, U, nsplit, B, L2t, bias, g,
-                        Y, M, N, K, M_pad, rank);
+  hipExtLaunchKernelGGL(gelu ? k2_gemm_bf16<true> : k2_gemm_bf16<false>, grid, dim3(256), 0, st, ev0,
+                        ev1, 0, A, U, nsplit, B, L2t, bias, g, Y, M, N, K, M_pad, rank);
   return hipGetLastError();
 }
 

@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 }  // namespace
 
-template <int BN>
+template <int BN, bool GELU>
 __global__ void __launch_bounds__(512, 1)
 k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
              const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
@@ -415,16 +415,24 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
             ul[i][q] = (__bf16)(uf[q] - (float)uh[i][q]);
           }
         }
+        v8bf lv[WN];
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const uint32_t lo = s0 + rank * 1024 + ((wn * WN + j) * 32 + lr) * rank * 2 + kk * 32 + lh * 16;
-          const v8bf lv = __builtin_bit_cast(v8bf, *(lds_v4i*)(uintptr_t)lo);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, uh[i], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, ul[i], acc[i][j], 0, 0, 0);
-          }
+          lv[j] = __builtin_bit_cast(v8bf, *(lds_v4i*)(uintptr_t)lo);
         }
+        // the hi products of all blocks, then the lo ones: an accumulator's two MFMAs
+        // are 2 WN apart instead of back to back
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv[j], uh[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv[j], ul[i], acc[i][j], 0, 0, 0);
       }
     }
     barrier_lds();  // the staging tiles below overwrite the seed copies
@@ -448,7 +456,10 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       for (int q = 0; q < 4; ++q) {
         uint32_t h[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) h[p] = f32_to_bf16_rne(acc[i][j][4 * q + p] + bv[4 * q + p]);
+        for (int p = 0; p < 4; ++p) {
+          const float v = acc[i][j][4 * q + p] + bv[4 * q + p];
+          h[p] = f32_to_bf16_rne(GELU ? gelu_f32(v) : v);
+        }
         *reinterpret_cast<uint2*>(tile + (32 * i + lr) * (BN / 2 + 8) + 32 * j + 8 * q + 4 * lh) =
             make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
@@ -495,7 +506,7 @@ double fill(int64_t tiles, int cus) {
 hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
                           const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                          int rank, bool gelu, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (M_pad % 256 != 0 || N % 128 != 0 || K % 128 != 0) return hipErrorInvalidValue;
   bool wide = N % 192 == 0;
   if (wide) {
@@ -503,15 +514,11 @@ hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int
     const int64_t t192 = (int64_t)(N / 192) * (M_pad / 256), t128 = (int64_t)(N / 128) * (M_pad / 256);
     if (fill(t128, cus) > 1.1 * fill(t192, cus)) wide = false;
   }
-  if (wide) {
-    const dim3 grid((unsigned)((N / 192) * (M_pad / 256)));
-    hipExtLaunchKernelGGL(k2_gemm_int4<192>, grid, dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit,
-                          B, sB, L2t, bias, Y, M, N, K, M_pad, rank);
-  } else {
-    const dim3 grid((unsigned)((N / 128) * (M_pad / 256)));
-    hipExtLaunchKernelGGL(k2_gemm_int4<128>, grid, dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit,
-                          B, sB, L2t, bias, Y, M, N, K, M_pad, rank);
-  }
+  const unsigned g = (unsigned)((N / (wide ? 192 : 128)) * (M_pad / 256));
+  auto k = wide ? (gelu ? k2_gemm_int4<192, true> : k2_gemm_int4<192, false>)
+                : (gelu ? k2_gemm_int4<128, true> : k2_gemm_int4<128, false>);
+  hipExtLaunchKernelGGL(k, dim3(g), dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB, L2t,
+                        bias, Y, M, N, K, M_pad, rank);
   return hipGetLastError();
 }
 

@@ -4,8 +4,8 @@
 //
 //   y = bf16( x/2 * erfc(-x / sqrt 2) )        (= x Phi(x), one rounding)
 //
-// erfc(-z) equals 1 + erf(z) but keeps its relative accuracy where 1 + erf(z) cancels
-// (z < 0), so the negative tail stays accurate down to bf16's subnormal range.
+// with erfc from gelu_f32 (common.h): a Chebyshev-fitted form accurate to ~1e-7
+// relative on both sides, down to bf16's subnormal range.
 // Memory-bound: one 16-byte load and store per 8 values, grid-stride.
 #include <algorithm>
 
@@ -17,9 +17,7 @@ namespace svdq {
 namespace {
 
 __device__ __forceinline__ uint32_t gelu_bits(uint32_t b16) {
-  const float x = bf16_to_f32(b16);
-  const float v = 0.5f * x * erfcf(x * -0.70710678118654752f);
-  return f32_to_bf16_rne(v);
+  return f32_to_bf16_rne(gelu_f32(bf16_to_f32(b16)));
 }
 
 __global__ void __launch_bounds__(256)

@@ -2,7 +2,8 @@
 // enqueues on `st` and returns hipGetLastError() of its launches.  Shapes were
 // validated by the C ABI before any of these is called.  `ev0` / `ev1` (may be
 // null) are HIP events that receive the kernel's start and end timestamps
-// (hipExtLaunchKernelGGL), used by the per-kernel timing hook.
+// (hipExtLaunchKernelGGL), used by the per-kernel timing hook.  `gelu` selects the GEMM
+// epilogue that applies the exact GELU to the fp32 result before the bf16 rounding.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -24,7 +25,7 @@ hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uin
 hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
                           const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, hipStream_t st, hipEvent_t ev0 = nullptr,
+                          int rank, bool gelu, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
 
 hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
@@ -34,7 +35,7 @@ hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const ui
 
 hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
                           const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
-                          int N, int K, int M_pad, int rank, hipStream_t st,
+                          int N, int K, int M_pad, int rank, bool gelu, hipStream_t st,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc, const uint8_t* Z,

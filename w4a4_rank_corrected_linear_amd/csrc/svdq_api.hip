@@ -305,11 +305,14 @@ svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t
   return ok();
 }
 
-svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, const uint16_t* x,
-                             int64_t M, float act_global, uint16_t* y, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The layer call behind svdq_w4a4_linear (gelu = false) and svdq_w4a4_linear_gelu.
+svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_weight* w,
+                        const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                        void* workspace, size_t workspace_bytes, bool gelu, hipStream_t stream) {
   if (!cfg || !w || !x || !y || !workspace || !w->qweight || !w->wscales || !w->smooth)
-    return fail(SVDQ_ERR_NULL, "svdq_w4a4_linear: NULL argument");
+    return fail(SVDQ_ERR_NULL, "%s: NULL argument", fn);
   SVDQ_TRY(check_svdq_config(cfg));
   const bool nv = cfg->precision == SVDQ_NVFP4;
   if (nv) {
@@ -317,7 +320,7 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
     SVDQ_TRY(check_global(w->w_global, "weight"));
   }
   if (cfg->rank > 0 && (!w->lora_down || !w->lora_up))
-    return fail(SVDQ_ERR_NULL, "svdq_w4a4_linear: rank %d needs lora_down and lora_up", cfg->rank);
+    return fail(SVDQ_ERR_NULL, "%s: rank %d needs lora_down and lora_up", fn, cfg->rank);
   SVDQ_TRY(check_k(w->K));
   SVDQ_TRY(check_n(w->N));
   SVDQ_TRY(check_m(M, w->K));
@@ -326,7 +329,7 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
   if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || !aligned16(w->qweight) ||
       !aligned16(w->wscales) || !aligned16(w->smooth) || (w->bias && !aligned16(w->bias)) ||
       (cfg->rank > 0 && (!aligned16(w->lora_down) || !aligned16(w->lora_up))))
-    return fail(SVDQ_ERR_ALIGN, "svdq_w4a4_linear: pointers must be 16-byte aligned");
+    return fail(SVDQ_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   const WsLayout L = ws_layout(cfg, M, w->K);
   if (workspace_bytes < L.total)
     return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -352,8 +355,8 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
                                              svdq::k1_splits((int)w->K),
                                              reinterpret_cast<const uint16_t*>(w->qweight),
                                              w->lora_up, w->bias, g, y, (int)M, (int)w->N,
-                                             (int)w->K, (int)L.M_pad, cfg->rank, stream, e2.start,
-                                             e2.end),
+                                             (int)w->K, (int)L.M_pad, cfg->rank, gelu, stream,
+                                             e2.start, e2.end),
                        "gemm kernel launch"));
     return ok();
   }
@@ -367,9 +370,25 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
                                            w->qweight,
                                            static_cast<const uint2*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
-                                           cfg->rank, stream, e2.start, e2.end),
+                                           cfg->rank, gelu, stream, e2.start, e2.end),
                      "gemm kernel launch"));
   return ok();
+}
+
+}  // namespace
+
+svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, const uint16_t* x,
+                             int64_t M, float act_global, uint16_t* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return linear_impl("svdq_w4a4_linear", cfg, w, x, M, act_global, y, workspace, workspace_bytes,
+                     false, stream);
+}
+
+svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                  const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return linear_impl("svdq_w4a4_linear_gelu", cfg, w, x, M, act_global, y, workspace,
+                     workspace_bytes, true, stream);
 }
 
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, const uint16_t* x,
