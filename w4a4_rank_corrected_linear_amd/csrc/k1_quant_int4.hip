@@ -7,9 +7,9 @@
 // clamped to [-7, 7], U = xhat @ lora_down^T (fp32 accumulation, not rounded).
 //
 // Two kernels share the quantizer below:
-//  * k1_int4_fused (the layer's own path) uses the batch skeleton of k1_batch.h and
-//    writes the GEMM operand layout, scales [K/64][M_pad] (8-byte records by group
-//    parity, see common.h) and partial U per k-split in the fragment layout;
+//  * k1_int4_fused (the layer's own path) uses the row-pair skeleton of k1_rows32.h
+//    and writes the GEMM operand layout, scales [K/64][M_pad] (8-byte records by
+//    group parity, see common.h) and partial U per k-split in the fragment layout;
 //  * k1_int4_interchange (svdq_quantize_act) streams whole rows with register
 //    prefetch and writes codes [M][K/2], scales [M][K/64] and U [M][r].
 // In both, lane l holds half h = q % 2 of the 64-group g = k0 / 64 (q = l / 16): the
@@ -18,6 +18,7 @@
 // is produced in registers by v_cvt_scalef32_2xpk16_fp6_f32.
 #include "common.h"
 #include "k1_batch.h"
+#include "k1_rows32.h"
 #include "kernels.h"
 
 namespace svdq {
@@ -97,7 +98,7 @@ struct QuantInt4Fused {
   }
 };
 
-__global__ void __launch_bounds__(256, 2) k1_int4_fused(K1Args a) { k1_batch<QuantInt4Fused>(a); }
+__global__ void __launch_bounds__(768, 1) k1_int4_fused(K1Args a) { k1_rows32<QuantInt4Fused>(a); }
 
 // Interchange kernel: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide
 // k-blocks kb = w, w+8, ... and prefetches the next block's X, smoothing and
@@ -242,8 +243,8 @@ hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uin
                           hipEvent_t ev1) {
   if (fused) {
     K1Args a{x, M, K, smooth, ldown, rank, codes, scales, uact, M_pad, 1.0f};
-    dim3 grid(M_pad / 16, k1_splits(K));
-    hipExtLaunchKernelGGL(k1_int4_fused, grid, dim3(256), 0, st, ev0, ev1, 0, a);
+    dim3 grid(M_pad / 32, k1_splits(K));
+    hipExtLaunchKernelGGL(k1_int4_fused, grid, dim3(64 * kK1RowsWaves), 0, st, ev0, ev1, 0, a);
   } else {
     dim3 grid((M + 15) / 16);
     hipExtLaunchKernelGGL(k1_int4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,
