@@ -172,6 +172,39 @@ def run_chain(args) -> int:
         chain(xs[i % 8])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    eager_ms = wall * 1e3 / args.steps
+    graph_info = None
+    if args.graph:
+        # the 8 steps recorded once into one HIP graph, replayed ceil(K/8) times
+        g = chain.capture(xs)
+        reps = -(-args.steps // 8)
+        for _ in range(-(-args.warmup // 8)):
+            g.launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.launch()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * args.steps / (8 * reps)
+        # host time to enqueue 8 steps: the calls one by one against one graph launch
+        # (median of 5, from an idle queue)
+        host_e, host_g = [], []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for x in xs:
+                chain(x)
+            host_e.append(time.perf_counter() - t0)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.launch()
+            host_g.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        g.destroy()
+        graph_info = {"replays": reps, "steps_per_replay": 8, "eager_ms_per_step": round(eager_ms, 6),
+                      "host_enqueue_us_per_step": {
+                          "eager": round(sorted(host_e)[2] * 1e6 / 8, 1),
+                          "graph": round(sorted(host_g)[2] * 1e6 / 8, 1)}}
 
     # per-layer times: events around each call on the current stream (they include the
     # dispatch of the call's kernels)
@@ -212,7 +245,8 @@ def run_chain(args) -> int:
               for n in names}
     out = {
         "metric": f"DiT block chain of svdq_w4a4 int4 linears (QKV, out, MLP-up, GELU, MLP-down) "
-                  f"effective TOPS at M={M}" + (", GELU fused into MLP-up" if args.fuse_gelu else ""),
+                  f"effective TOPS at M={M}" + (", GELU fused into MLP-up" if args.fuse_gelu else "")
+                  + (", 8 steps per HIP graph" if args.graph else ""),
         "value": round(value, 3),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -226,12 +260,14 @@ def run_chain(args) -> int:
         "data": "synthetic",
         "config": {"workload": f"chain: DiT block, batch {args.batch} (M={M}), 8 fresh step inputs "
                                "cycled, int4 g64 rank 32" + (", GELU in the MLP-up epilogue"
-                                                             if args.fuse_gelu else ""),
+                                                             if args.fuse_gelu else "")
+                               + (", 8 steps per HIP graph replay" if args.graph else ""),
                    "M": M, "layers": {n: {"K": K, "N": N} for n, (K, N) in shapes.items()},
                    "seeds": {"steps": [I.seeds(I.CHAIN_CONFIG).step(s) for s in range(8)]}},
         "chain_8_steps_ms": round(8 * ms_per_step, 6),
         "layers": layers,
         "sum_of_call_ms": round(sum(per.values()), 6),
+        **({"graph": graph_info} if graph_info else {}),
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -331,6 +367,8 @@ def main() -> int:
                     help="chain workload: images per step (M = 4608 per image)")
     ap.add_argument("--fuse-gelu", action="store_true",
                     help="chain workload: GELU in the MLP-up GEMM's epilogue")
+    ap.add_argument("--graph", action="store_true",
+                    help="chain: record the 8 steps into one HIP graph and time its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (scale reference for HBM counters)")

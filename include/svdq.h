@@ -177,6 +177,42 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
  * recorded by the timing hook below.  Enqueued on `stream`. */
 svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 
+/* Graph capture of a sequence of calls (Diffusers docs "Nunchaku Lite", "Fused kernels"
+ * and the tutorial's torch.compile section: once the kernels are fused, what is left of
+ * a denoise step's latency is launch overhead, which compiling the model recovers).
+ * Here a caller records the launches of any sequence of the calls above, for example
+ * the four linears and the GELU of a DiT block over several denoise steps, into one HIP
+ * graph and replays it with one launch.
+ *
+ * svdq_capture_begin(stream) starts capturing `stream` in thread-local mode: until
+ * svdq_capture_end, the calls that the calling thread makes on `stream` record their
+ * kernels instead of running them.  `stream` must be a created stream (not the null
+ * stream, which cannot be captured: SVDQ_ERR_CONFIG), per-kernel timing must be off
+ * (SVDQ_ERR_CONFIG), and the calls made during capture must not allocate or
+ * synchronize.  Nothing runs until the graph is launched; every buffer that a
+ * recorded call names (inputs, outputs, workspace, weights) is bound by address and
+ * must stay allocated, at the same address, while the graph may run.
+ *
+ * svdq_capture_end(stream, &graph) ends the capture, instantiates the recorded graph
+ * and returns it through *graph (a handle that the caller owns; *graph is NULL on
+ * error).  It must be called after every successful svdq_capture_begin, also when a
+ * call during capture failed: a failed launch invalidates the capture, and then
+ * svdq_capture_end returns SVDQ_ERR_HIP and no graph.  The instantiated graph holds
+ * device resources of its own (HIP's), released by svdq_graph_destroy.
+ *
+ * svdq_graph_launch(graph, stream) enqueues one replay on `stream` (any stream of the
+ * graph's device, the null stream included).  Replays on one stream run in order;
+ * replays that overlap in time (on different streams) race on the shared buffers.
+ *
+ * svdq_graph_destroy(graph) releases the graph; NULL is allowed and does nothing.
+ * Replays already enqueued complete normally.  Errors: SVDQ_ERR_NULL, SVDQ_ERR_CONFIG,
+ * SVDQ_ERR_DEVICE, SVDQ_ERR_HIP. */
+typedef struct svdq_graph svdq_graph;
+svdq_status svdq_capture_begin(hipStream_t stream);
+svdq_status svdq_capture_end(hipStream_t stream, svdq_graph** graph);
+svdq_status svdq_graph_launch(const svdq_graph* graph, hipStream_t stream);
+svdq_status svdq_graph_destroy(svdq_graph* graph);
+
 /* Per-kernel timing, for measurement tools.  After svdq_timing_start(max_calls) and
  * until svdq_timing_stop, each svdq_w4a4_linear / awq_w4a16_linear call made on the
  * calling thread launches its kernels with a pair of HIP events that receive each

@@ -190,3 +190,17 @@ def test_gelu_entry_points_validate_like_the_linear():
     assert lib.svdq_gelu_bf16(FAKE_MISALIGNED, FAKE, 8, None) == L.ERR_ALIGN
     assert lib.svdq_gelu_bf16(FAKE, FAKE, -1, None) == L.ERR_SHAPE
     assert lib.svdq_gelu_bf16(FAKE, FAKE, 0, None) == L.OK
+
+
+def test_graph_entry_validation():
+    """Graph capture entry points reject bad arguments on the host: the null stream
+    cannot be captured, NULL handles are errors (destroying NULL is a no-op)."""
+    lib = L.lib()
+    assert lib.svdq_capture_begin(None) == L.ERR_CONFIG
+    assert "null stream" in L.last_error()
+    assert lib.svdq_capture_end(FAKE, None) == L.ERR_NULL
+    g = ctypes.c_void_p(FAKE)
+    assert lib.svdq_capture_end(None, ctypes.byref(g)) == L.ERR_CONFIG
+    assert g.value is None
+    assert lib.svdq_graph_launch(None, None) == L.ERR_NULL
+    assert lib.svdq_graph_destroy(None) == L.OK

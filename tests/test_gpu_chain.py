@@ -102,3 +102,60 @@ def test_block_chain_with_gelu_fused_into_mlp_up(block):
     check_y(out["act"][rows], A.gelu_f64(ref_up))
     ref_down = OL.w4a4_linear_rows("int4", out["act"], layers["down"], rows)["r"]
     check_y(out["down"][rows], ref_down)
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+def test_block_chain_graph_replays_match_eager(block, fuse):
+    """Three denoise steps recorded into one HIP graph (svdq_capture_begin/end): every
+    replay, with eager calls and synchronizations between replays, leaves exactly the
+    eager results of the last step; the eager calls in between see their own results."""
+    layers, _, dev = block
+    chain = svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"], fuse_gelu=fuse)
+    M = 4608
+    steps = (2, 6, 7)
+    xs = [dev_bf16(I.chain_step_activations(M, s)) for s in steps]
+    x_other = dev_bf16(I.chain_step_activations(M, 4))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {k: host_bits(v).copy() for k, v in chain.results().items()}
+
+    chain(x_other)
+    other = snapshot()
+    chain(xs[-1])
+    ref = snapshot()
+    assert not np.array_equal(ref["down"], other["down"])
+    graph = chain.capture(xs)
+    for rep in range(3):
+        graph.launch()
+        got = snapshot()
+        assert got.keys() == ref.keys()
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), f"replay {rep}: {k} differs from the eager result"
+        chain(x_other)
+        got = snapshot()
+        for k in other:
+            assert np.array_equal(got[k], other[k]), f"eager call after replay {rep}: {k}"
+    graph.destroy()
+    # the replayed last step against the oracle on sampled rows
+    rows = np.array([0, 1234, M - 1])
+    ref_down = OL.w4a4_linear_rows("int4", ref["act"], layers["down"], rows)["r"]
+    check_y(ref["down"][rows], ref_down)
+
+
+def test_capture_rejects_the_null_stream_and_timing():
+    """The null stream cannot be captured, and capture is refused while the per-kernel
+    timing hook is on; nothing is left capturing after either error."""
+    lib = svdq.lib()
+    assert lib.svdq_capture_begin(None) != 0
+    svdq.timing_start(4)
+    try:
+        s = torch.cuda.Stream()
+        assert lib.svdq_capture_begin(s.cuda_stream) != 0
+        assert "timing" in svdq._lib.last_error()
+    finally:
+        svdq.timing_stop()
+    x = dev_bf16(np.zeros(64, np.uint16))
+    y = svdq.gelu(x)
+    torch.cuda.synchronize()
+    assert not host_bits(y).any()

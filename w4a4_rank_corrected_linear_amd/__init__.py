@@ -12,8 +12,10 @@ and the current HIP stream; all arithmetic runs in the library's kernels.
 from ._lib import SvdqError, lib  # noqa: F401
 from .api import (  # noqa: F401
     AwqLinear,
+    Graph,
     SvdqLinear,
     awq_w4a16_linear,
+    capture,
     check_device,
     gelu,
     pack_lora_down,

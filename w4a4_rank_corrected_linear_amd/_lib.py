@@ -81,6 +81,14 @@ def lib() -> ctypes.CDLL:
     L.awq_w4a16_linear.restype = st
     L.svdq_gelu_bf16.argtypes = [vp, vp, i64, vp]
     L.svdq_gelu_bf16.restype = st
+    L.svdq_capture_begin.argtypes = [vp]
+    L.svdq_capture_begin.restype = st
+    L.svdq_capture_end.argtypes = [vp, ctypes.POINTER(vp)]
+    L.svdq_capture_end.restype = st
+    L.svdq_graph_launch.argtypes = [vp, vp]
+    L.svdq_graph_launch.restype = st
+    L.svdq_graph_destroy.argtypes = [vp]
+    L.svdq_graph_destroy.restype = st
     L.svdq_timing_start.argtypes = [ctypes.c_int]
     L.svdq_timing_start.restype = st
     ip = ctypes.POINTER(ctypes.c_int)

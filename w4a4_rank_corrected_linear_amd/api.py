@@ -197,6 +197,60 @@ def gelu(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     return y
 
 
+class Graph:
+    """An instantiated HIP graph of recorded library calls (svdq_capture_end); replay it
+    with ``launch``.  The buffers the recorded calls named must stay alive while it may
+    run; ``keep`` holds references to them."""
+
+    def __init__(self, handle: int, keep=()):
+        self._h = ctypes.c_void_p(handle)
+        self.keep = tuple(keep)
+
+    def launch(self) -> None:
+        """Enqueue one replay on the current stream."""
+        if not self._h.value:
+            raise RuntimeError("graph was destroyed")
+        L.check(L.lib().svdq_graph_launch(self._h, _stream()), "svdq_graph_launch")
+
+    def destroy(self) -> None:
+        if self._h.value:
+            L.check(L.lib().svdq_graph_destroy(self._h), "svdq_graph_destroy")
+            self._h = ctypes.c_void_p(None)
+        self.keep = ()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def capture(fn, keep=()) -> Graph:
+    """Record the library calls that fn() makes into one HIP graph.  fn runs on a side
+    stream under thread-local capture (the null stream cannot be captured); it must not
+    allocate device memory or synchronize, so create its buffers before (one eager call
+    does).  Returns the instantiated Graph; nothing has run yet."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st = _stream()
+        L.check(L.lib().svdq_capture_begin(st), "svdq_capture_begin")
+        err = None
+        try:
+            fn()
+        except BaseException as e:  # the capture must still be ended
+            err = e
+        h = ctypes.c_void_p()
+        st_end = L.lib().svdq_capture_end(st, ctypes.byref(h))
+    torch.cuda.current_stream().wait_stream(side)
+    if err is not None:
+        if h.value:
+            L.lib().svdq_graph_destroy(h)
+        raise err
+    L.check(st_end, "svdq_capture_end")
+    return Graph(h.value, keep)
+
+
 def timing_start(max_calls: int) -> None:
     """svdq_timing_start: record per-kernel HIP events in the next `max_calls` layer
     calls made on this thread."""

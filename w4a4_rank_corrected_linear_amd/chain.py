@@ -8,15 +8,17 @@ its GELU MLP).  Attention itself, the norms and the residual adds are not part o
 layer: the QKV output is produced for the attention that would consume it, and the
 output projection reads the block's input activations in place of the attention
 output.  The GELU runs either as its own kernel or fused into the MLP-up GEMM's
-epilogue (on the fp32 result, before the bf16 rounding).  Every step runs in the
-library's kernels; this module only orders the calls.
+epilogue (on the fp32 result, before the bf16 rounding).  Several denoise steps can be
+recorded into one HIP graph and replayed with one launch (the launch overhead that the
+tutorial's torch.compile section recovers).  Every step runs in the library's kernels;
+this module only orders the calls.
 """
 
 from __future__ import annotations
 
 import torch
 
-from .api import SvdqLinear, gelu
+from .api import Graph, SvdqLinear, capture, gelu
 
 
 class DitBlockChain:
@@ -60,3 +62,26 @@ class DitBlockChain:
         return r
 
     __call__ = forward
+
+    def results(self) -> dict:
+        """The result buffers of the last call or replay, by name (see forward)."""
+        names = ("qkv", "out", "act", "down") if self.fuse_gelu else ("qkv", "out", "up", "act", "down")
+        return {n: self._buf[n] for n in names if n in self._buf}
+
+    def capture(self, xs) -> "Graph":
+        """One HIP graph of len(xs) consecutive steps, step i on input xs[i] (all of one
+        M): 4 or 5 kernels' worth of calls per step, replayed with one launch
+        (Graph.launch).  After a replay the buffers hold the last step's results, as
+        after the same eager calls.  The inputs and this chain's buffers must stay alive
+        and in place while the graph may run; the graph keeps references to them."""
+        xs = list(xs)
+        if not xs or any(x.shape != xs[0].shape for x in xs):
+            raise ValueError("capture needs one or more step inputs of one shape")
+        self.forward(xs[0])          # creates the buffers outside the capture
+        torch.cuda.current_stream().synchronize()
+
+        def steps():
+            for x in xs:
+                self.forward(x)
+
+        return capture(steps, keep=(tuple(xs), dict(self._buf)))

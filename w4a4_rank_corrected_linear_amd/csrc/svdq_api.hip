@@ -7,10 +7,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
 #include "svdq.h"
+
 #include "kernels.h"
 
 namespace {
@@ -425,6 +427,63 @@ svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_
   SVDQ_TRY(check_current_device());
   SVDQ_TRY(hip_check(svdq::launch_gelu_bf16(x, y, n, stream), "gelu kernel launch"));
   return ok();
+}
+
+struct svdq_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+svdq_status svdq_capture_begin(hipStream_t stream) {
+  if (!stream)
+    return fail(SVDQ_ERR_CONFIG, "svdq_capture_begin: the null stream cannot be captured; "
+                                 "pass a created stream");
+  if (g_timer.on)
+    return fail(SVDQ_ERR_CONFIG, "svdq_capture_begin: per-kernel timing is on; stop it first");
+  SVDQ_TRY(check_current_device());
+  return hip_check(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal),
+                   "hipStreamBeginCapture");
+}
+
+svdq_status svdq_capture_end(hipStream_t stream, svdq_graph** graph) {
+  if (!graph) return fail(SVDQ_ERR_NULL, "svdq_capture_end: NULL graph pointer");
+  *graph = nullptr;
+  if (!stream) return fail(SVDQ_ERR_CONFIG, "svdq_capture_end: the null stream is never captured");
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(stream, &g);
+  if (e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return fail(SVDQ_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  }
+  if (!g) return fail(SVDQ_ERR_HIP, "hipStreamEndCapture returned no graph");
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(SVDQ_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  }
+  svdq_graph* h = new (std::nothrow) svdq_graph{g, x};
+  if (!h) {
+    (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    return fail(SVDQ_ERR_HIP, "svdq_capture_end: out of host memory");
+  }
+  *graph = h;
+  return ok();
+}
+
+svdq_status svdq_graph_launch(const svdq_graph* graph, hipStream_t stream) {
+  if (!graph) return fail(SVDQ_ERR_NULL, "svdq_graph_launch: NULL graph");
+  return hip_check(hipGraphLaunch(graph->exec, stream), "hipGraphLaunch");
+}
+
+svdq_status svdq_graph_destroy(svdq_graph* graph) {
+  if (!graph) return ok();
+  const hipError_t e1 = hipGraphExecDestroy(graph->exec);
+  const hipError_t e2 = hipGraphDestroy(graph->graph);
+  delete graph;
+  SVDQ_TRY(hip_check(e1, "hipGraphExecDestroy"));
+  return hip_check(e2, "hipGraphDestroy");
 }
 
 svdq_status svdq_timing_start(int max_calls) {
