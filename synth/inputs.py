@@ -261,3 +261,40 @@ def chain_step_activations(M: int, step: int) -> np.ndarray:
     K = CHAIN_LAYERS[0][1]
     idx = outlier_channels(K, default_outlier_count(K), sd.outliers)
     return activations(M, K, sd.step(step), idx, 30.0)
+
+
+# Rotary table and Q/K norm weights of the block's attention (config 3 shapes: 24 heads
+# of 128 in a 3072 hidden).  The angles follow the positional layout of a 1024x1024
+# DiT: 512 text tokens at position (0, 0, 0), then the 64 x 64 latent patches at
+# (0, row, column); 128 = 2 (16 + 56 + 56) channels split over the three axes, each
+# axis with base 10000: angle of pair j of an axis of width d at position p is
+# p * 10000^(-2j/d).  Batch b repeats the table b times (one sequence per image).
+ROPE_AXES = (16, 56, 56)
+ROPE_THETA = 10000.0
+QK_NORM_EPS = 1e-6
+
+
+def _rope_positions() -> np.ndarray:
+    text = np.zeros((512, 3), dtype=np.float64)
+    rr, cc = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    img = np.stack([np.zeros(4096), rr.ravel(), cc.ravel()], axis=1).astype(np.float64)
+    return np.concatenate([text, img], axis=0)
+
+
+def rope_table(M: int) -> np.ndarray:
+    """[M, 64, 2] float32 (cos, sin) per token and pair, token m at position m % 4608."""
+    pos = _rope_positions()
+    ang = []
+    for a, d in enumerate(ROPE_AXES):
+        freq = ROPE_THETA ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+        ang.append(pos[:, a:a + 1] * freq[None, :])
+    ang = np.concatenate(ang, axis=1)                       # [4608, 64]
+    ang = ang[np.arange(M) % ang.shape[0]]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=2).astype(np.float32)
+
+
+def qk_norm_weights(config_id: int = 3, head_dim: int = 128):
+    """(norm_q, norm_k) bf16 bits [head_dim] each, 1 + 0.1 N(0, 1)."""
+    rng = np.random.default_rng(seeds(config_id).w + 900)
+    w = 1.0 + 0.1 * rng.standard_normal((2, head_dim))
+    return to_bf16_bits(w[0].astype(np.float32)), to_bf16_bits(w[1].astype(np.float32))
