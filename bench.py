@@ -159,24 +159,29 @@ def run_chain(args) -> int:
     lay = {k: svdq.SvdqLinear.from_interchange(u8(pb.qweight), bf16(pb.wscales), bf16(pb.smooth),
                                                bf16(pb.lora_down), bf16(pb.lora_up), bf16(pb.bias))
            for k, pb in pbs.items()}
+    qk_norm, rope = None, None
+    if args.qkv_norm_rope:
+        nq, nk = (bf16(b) for b in I.qk_norm_weights())
+        qk_norm = (nq, nk, I.QK_NORM_EPS)
+        rope = torch.from_numpy(I.rope_table(M)).to(dev)
     chain = svdq.DitBlockChain(lay["qkv"], lay["out"], lay["up"], lay["down"],
-                               fuse_gelu=args.fuse_gelu)
+                               fuse_gelu=args.fuse_gelu, qk_norm=qk_norm)
     xs = [bf16(I.chain_step_activations(M, s)) for s in range(8)]
     print(f"[bench] workload chain: DiT block (QKV, out, MLP-up, GELU, MLP-down), M={M}, 8 fresh "
           f"step inputs; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        chain(xs[i % 8])
+        chain(xs[i % 8], rope)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        chain(xs[i % 8])
+        chain(xs[i % 8], rope)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     eager_ms = wall * 1e3 / args.steps
     graph_info = None
     if args.graph:
         # the 8 steps recorded once into one HIP graph, replayed ceil(K/8) times
-        g = chain.capture(xs)
+        g = chain.capture(xs, rope)
         reps = -(-args.steps // 8)
         for _ in range(-(-args.warmup // 8)):
             g.launch()
@@ -193,7 +198,7 @@ def run_chain(args) -> int:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for x in xs:
-                chain(x)
+                chain(x, rope)
             host_e.append(time.perf_counter() - t0)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
@@ -218,7 +223,9 @@ def run_chain(args) -> int:
             "up": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
             "act": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
             "down": torch.empty((M, lay["down"].N), dtype=torch.bfloat16, device=dev)}
-    calls = [lambda x: lay["qkv"](x, out=bufs["qkv"], workspace=ws),
+    calls = [(lambda x: lay["qkv"].qkv_norm_rope(x, *qk_norm[:2], qk_norm[2], rope, out=bufs["qkv"],
+                                                 workspace=ws)) if qk_norm else
+             (lambda x: lay["qkv"](x, out=bufs["qkv"], workspace=ws)),
              lambda x: lay["out"](x, out=bufs["out"], workspace=ws)]
     if args.fuse_gelu:
         calls.append(lambda x: lay["up"](bufs["out"], out=bufs["act"], workspace=ws, gelu=True))
@@ -246,6 +253,7 @@ def run_chain(args) -> int:
     out = {
         "metric": f"DiT block chain of svdq_w4a4 int4 linears (QKV, out, MLP-up, GELU, MLP-down) "
                   f"effective TOPS at M={M}" + (", GELU fused into MLP-up" if args.fuse_gelu else "")
+                  + (", Q/K norm + rotary fused into QKV" if args.qkv_norm_rope else "")
                   + (", 8 steps per HIP graph" if args.graph else ""),
         "value": round(value, 3),
         "unit": "TOPS",
@@ -261,7 +269,9 @@ def run_chain(args) -> int:
         "config": {"workload": f"chain: DiT block, batch {args.batch} (M={M}), 8 fresh step inputs "
                                "cycled, int4 g64 rank 32" + (", GELU in the MLP-up epilogue"
                                                              if args.fuse_gelu else "")
-                               + (", 8 steps per HIP graph replay" if args.graph else ""),
+                               + (", 8 steps per HIP graph replay" if args.graph else "")
+                               + (", Q/K RMSNorm + rotary in the QKV epilogue"
+                                  if args.qkv_norm_rope else ""),
                    "M": M, "layers": {n: {"K": K, "N": N} for n, (K, N) in shapes.items()},
                    "seeds": {"steps": [I.seeds(I.CHAIN_CONFIG).step(s) for s in range(8)]}},
         "chain_8_steps_ms": round(8 * ms_per_step, 6),
@@ -369,6 +379,9 @@ def main() -> int:
                     help="chain workload: GELU in the MLP-up GEMM's epilogue")
     ap.add_argument("--graph", action="store_true",
                     help="chain: record the 8 steps into one HIP graph and time its replays")
+    ap.add_argument("--qkv-norm-rope", action="store_true",
+                    help="qkv and chain workloads: the fused QKV epilogue with per-head Q/K RMSNorm and the "
+                         "rotary embedding (1024x1024 DiT table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (scale reference for HBM counters)")
@@ -395,6 +408,9 @@ def main() -> int:
     svdq.check_device(0)
     if args.workload == "chain":
         return run_chain(args)
+    if args.qkv_norm_rope and args.workload != "qkv":
+        print("--qkv-norm-rope applies to the qkv and chain workloads only", file=sys.stderr)
+        return 2
 
     inp = make_inputs(args.workload)
     method = inp["method"]
@@ -422,6 +438,12 @@ def main() -> int:
             act_global=getattr(pb, "act_global", 1.0))
         ws = layer.workspace(M, dev)
         call = lambda: layer(x, out=y, workspace=ws)  # noqa: E731
+        if args.qkv_norm_rope:
+            from synth import inputs as I
+            nq, nk = (bf16(b) for b in I.qk_norm_weights())
+            rope = torch.from_numpy(I.rope_table(M)).to(dev)
+            call = lambda: layer.qkv_norm_rope(x, nq, nk, I.QK_NORM_EPS, rope, out=y,  # noqa: E731
+                                               workspace=ws)
         n_kernels = 2
     print(f"[bench] workload {args.workload} ({method}) M={M} K={K} N={N} rank={rank}; warmup "
           f"{args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
@@ -487,6 +509,9 @@ def main() -> int:
             "awq": "awq_w4a16 int4 g64"}[method]
     metric = METRIC if args.workload == "attn_proj" else (
         f"{desc} linear effective TOPS at M={M},K={K},N={N}")
+    if args.qkv_norm_rope:
+        metric += ", Q/K RMSNorm + rotary fused in the epilogue"
+        desc += ", Q/K RMSNorm + rotary epilogue"
 
     out = {
         "metric": metric,

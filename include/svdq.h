@@ -162,6 +162,31 @@ svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight
                                   const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The fused QKV projection of a DiT attention block with its per-head Q/K RMSNorm and
+ * rotary embedding in the GEMM epilogue (Diffusers docs "Nunchaku Lite", "Fused
+ * kernels": the original engine fuses the Q, K, V projections with RMSNorm and RoPE;
+ * the infolabhq tutorial's section on structural rewrites shows the unfused sequence:
+ * split into heads, norm_q / norm_k, apply_rotary_emb).  The layer is the svdq_w4a4
+ * linear with N = 3 H 128 output columns: [0, N/3) are Q, [N/3, 2N/3) K, [2N/3, N) V,
+ * head h of Q (or K) the 128 columns [128 h, 128 h + 128) of its third.  With r the
+ * linear's unrounded result (as svdq_w4a4_linear, bias included), for every token m and
+ * every head of Q (weights norm_q) and of K (weights norm_k):
+ *   n_c      = r_c / sqrt( mean_c(r_c^2) + eps ) * w_c        (c = 0..127, fp32)
+ *   y_{2i}   = bf16_rne( n_{2i} cos[m][i] - n_{2i+1} sin[m][i] )
+ *   y_{2i+1} = bf16_rne( n_{2i+1} cos[m][i] + n_{2i} sin[m][i] )  (i = 0..63)
+ * and y = bf16_rne(r) on the V columns; one rounding per output.
+ * norm_q, norm_k: device, bf16 [128].  rope: device, fp32 [M][64][2], (cos, sin) of
+ * token m and pair i at rope[(m * 64 + i) * 2 + {0, 1}], the same for every head and
+ * for Q and K.  eps: finite and positive (SVDQ_ERR_RANGE).  cfg must be int4 (nvfp4:
+ * SVDQ_ERR_CONFIG); N a multiple of 384 (SVDQ_ERR_SHAPE); every pointer 16-byte
+ * aligned.  Workspace, stream and other errors as for svdq_w4a4_linear. */
+svdq_status svdq_w4a4_linear_qkv_norm_rope(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                           const uint16_t* x, int64_t M, float act_global,
+                                           const uint16_t* norm_q, const uint16_t* norm_k,
+                                           float eps, const float* rope, uint16_t* y,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
 /* The AWQ W4A16 comparison layer: Y[M][N] (bf16) from bf16 X[M][K].  cfg must be
  * {int4, 64, rank 0, bf16}. */
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,

@@ -204,3 +204,22 @@ def test_graph_entry_validation():
     assert g.value is None
     assert lib.svdq_graph_launch(None, None) == L.ERR_NULL
     assert lib.svdq_graph_destroy(None) == L.OK
+
+
+def test_qkv_norm_rope_entry_validation():
+    """The fused QKV entry point: NULL norm weights or table, nvfp4, N not a multiple
+    of 384, eps not finite and positive, misaligned table."""
+    lib = L.lib()
+
+    def call(c, w, nq=FAKE, nk=FAKE, eps=1e-6, rope=FAKE):
+        return lib.svdq_w4a4_linear_qkv_norm_rope(ctypes.byref(c), ctypes.byref(w), FAKE, 16, 1.0,
+                                                  nq, nk, eps, rope, FAKE, FAKE, 1 << 30, None)
+
+    w = weight(K=512, N=768)
+    assert call(cfg(), w, nq=None) == L.ERR_NULL
+    assert call(cfg(), w, rope=None) == L.ERR_NULL
+    assert call(cfg(precision=L.NVFP4, group=16), w) == L.ERR_CONFIG
+    assert call(cfg(), weight(K=512, N=512)) == L.ERR_SHAPE
+    for bad in (0.0, -1e-6, float("nan"), float("inf")):
+        assert call(cfg(), w, eps=bad) == L.ERR_RANGE
+    assert call(cfg(), w, rope=FAKE_MISALIGNED) == L.ERR_ALIGN

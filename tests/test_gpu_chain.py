@@ -159,3 +159,33 @@ def test_capture_rejects_the_null_stream_and_timing():
     y = svdq.gelu(x)
     torch.cuda.synchronize()
     assert not host_bits(y).any()
+
+
+def test_block_chain_fully_fused_with_graph(block):
+    """The chain with the Q/K norm + rotary fused into QKV and the GELU into MLP-up,
+    recorded into a graph over two steps: the replay equals the eager calls, and the
+    QKV and MLP-down outputs of the last step match the oracle on sampled rows."""
+    from oracle import attention as AT
+    layers, _, dev = block
+    M = 4608
+    nq, nk = I.qk_norm_weights()
+    rope_np = I.rope_table(M)
+    rope = torch.from_numpy(rope_np).cuda()
+    chain = svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"], fuse_gelu=True,
+                               qk_norm=(dev_bf16(nq), dev_bf16(nk), I.QK_NORM_EPS))
+    x_np = [I.chain_step_activations(M, s) for s in (1, 3)]
+    xs = [dev_bf16(v) for v in x_np]
+    chain(xs[-1], rope)
+    torch.cuda.synchronize()
+    ref = {k: host_bits(v).copy() for k, v in chain.results().items()}
+    assert set(ref) == {"qkv", "out", "act", "down"}
+    g = chain.capture(xs, rope)
+    g.launch()
+    torch.cuda.synchronize()
+    for k, v in chain.results().items():
+        assert np.array_equal(host_bits(v), ref[k]), k
+    g.destroy()
+    rows = np.array([0, 511, 512, 2049, M - 1])
+    r = OL.w4a4_linear_rows("int4", x_np[-1], layers["qkv"], rows)["r"]
+    check_y(ref["qkv"][rows], AT.qkv_norm_rope_f64(r, nq, nk, I.QK_NORM_EPS, rope_np[rows]))
+    check_y(ref["down"][rows], OL.w4a4_linear_rows("int4", ref["act"], layers["down"], rows)["r"])

@@ -1,0 +1,103 @@
+"""The fused QKV projection with per-head Q/K RMSNorm and rotary embedding in the GEMM
+epilogue (svdq_w4a4_linear_qkv_norm_rope) against the oracle: on an oracle-prepared
+layer with ragged token counts, and on the DiT block's 3072 -> 9216 projection at
+M = 4608 with the 1024x1024 rotary table (sampled rows, text and image tokens)."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import w4a4_rank_corrected_linear_amd as svdq
+from helpers import check_y, dev_bf16, dev_u8, host_bits
+from oracle import attention as AT
+from oracle import linear as OL
+from oracle import prep as P
+from synth import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+EPS = I.QK_NORM_EPS
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _layer_dev(layer, bias=True):
+    return svdq.SvdqLinear.from_interchange(
+        dev_u8(layer.qweight), dev_bf16(layer.wscales), dev_bf16(layer.smooth),
+        dev_bf16(layer.lora_down), dev_bf16(layer.lora_up),
+        dev_bf16(layer.bias) if bias else None)
+
+
+@pytest.fixture(scope="module")
+def tiny_qkv():
+    """K = 512, N = 768: two heads each of Q, K and V; random angles per token."""
+    li = I.layer_inputs(config_id=1, M=300, K=512, N=768, outlier_count=4, factor=20.0)
+    layer = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=32)
+    rng = np.random.default_rng(31)
+    ang = rng.uniform(-np.pi, np.pi, (300, 64))
+    rope = np.stack([np.cos(ang), np.sin(ang)], axis=2).astype(np.float32)
+    nq, nk = I.qk_norm_weights()
+    return li, layer, rope, nq, nk
+
+
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("M", [1, 37, 256, 300])
+def test_qkv_norm_rope_tiny(tiny_qkv, M, bias):
+    li, layer, rope, nq, nk = tiny_qkv
+    dev = _layer_dev(layer, bias)
+    y = dev.qkv_norm_rope(dev_bf16(li.x[:M]), dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope[:M]))
+    torch.cuda.synchronize()
+    ol = layer if bias else dataclasses.replace(layer, bias=None)
+    r = OL.w4a4_linear("int4", li.x[:M], ol)["r"]
+    check_y(host_bits(y), AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[:M]))
+
+
+def test_qkv_v_columns_equal_the_plain_linear(tiny_qkv):
+    """V is the plain linear, bit for bit; Q and K are not."""
+    li, layer, rope, nq, nk = tiny_qkv
+    dev = _layer_dev(layer)
+    x = dev_bf16(li.x)
+    plain = host_bits(dev(x))
+    fused = host_bits(dev.qkv_norm_rope(x, dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope)))
+    assert np.array_equal(fused[:, 512:], plain[:, 512:])
+    assert not np.array_equal(fused[:, :256], plain[:, :256])
+    assert not np.array_equal(fused[:, 256:512], plain[:, 256:512])
+
+
+def test_qkv_norm_rope_zero_rows_and_m0(tiny_qkv):
+    """Zero activations give r = bias: heads of the bias alone are normalised; M = 0
+    launches nothing."""
+    li, layer, rope, nq, nk = tiny_qkv
+    dev = _layer_dev(layer)
+    x = np.zeros((5, 512), np.uint16)
+    y = dev.qkv_norm_rope(dev_bf16(x), dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope[:5]))
+    r = OL.w4a4_linear("int4", x, layer)["r"]
+    check_y(host_bits(y), AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[:5]))
+    e = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    out = dev.qkv_norm_rope(e, dev_bf16(nq), dev_bf16(nk), EPS,
+                            torch.empty((0, 64, 2), dtype=torch.float32, device="cuda"))
+    assert out.shape == (0, 768)
+
+
+def test_qkv_norm_rope_dit_block_full_size():
+    """The block's QKV projection at M = 4608 (512 text + 4096 image tokens) with the
+    1024x1024 rotary table, sampled rows of both kinds against the oracle."""
+    pb = I.chain_layer_bytes()["qkv"]
+    layer = P.SvdqLayer(precision="int4", K=pb.K, N=pb.N, rank=pb.rank, qweight=pb.qweight,
+                        wscales=pb.wscales, w_global=1.0, act_global=1.0, smooth=pb.smooth,
+                        lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+    dev = svdq.SvdqLinear.from_interchange(dev_u8(pb.qweight), dev_bf16(pb.wscales),
+                                           dev_bf16(pb.smooth), dev_bf16(pb.lora_down),
+                                           dev_bf16(pb.lora_up), dev_bf16(pb.bias))
+    M = 4608
+    x = I.chain_step_activations(M, 0)
+    rope = I.rope_table(M)
+    nq, nk = I.qk_norm_weights()
+    y = host_bits(dev.qkv_norm_rope(dev_bf16(x), dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope)))
+    rows = np.array([0, 1, 300, 511, 512, 513, 1000, 2222, 4000, 4606, 4607])
+    r = OL.w4a4_linear_rows("int4", x, layer, rows)["r"]
+    check_y(y[rows], AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[rows]))

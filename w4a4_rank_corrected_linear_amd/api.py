@@ -150,6 +150,8 @@ class SvdqLinear:
         if K != self.K:
             raise ValueError(f"x has K = {K}, layer expects {self.K}")
         y = torch.empty((M, self.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+        if M == 0:  # nothing to compute (empty tensors carry no device address)
+            return y
         ws = self.workspace(M, x.device) if workspace is None else workspace
         g = self.act_global if act_global is None else float(act_global)
         fn = "svdq_w4a4_linear_gelu" if gelu else "svdq_w4a4_linear"
@@ -159,6 +161,31 @@ class SvdqLinear:
         return y
 
     __call__ = forward
+
+    def qkv_norm_rope(self, x: torch.Tensor, norm_q: torch.Tensor, norm_k: torch.Tensor,
+                      eps: float, rope: torch.Tensor, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, act_global: float | None = None):
+        """The fused QKV projection (svdq_w4a4_linear_qkv_norm_rope): per-head RMSNorm
+        (norm_q / norm_k, bf16 [128]) and the rotary turn (rope, float32 [M, 64, 2] of
+        cos, sin) on the Q and K thirds of the output; V as the plain linear."""
+        _want(x, torch.bfloat16, "x")
+        M, K = x.shape
+        if K != self.K:
+            raise ValueError(f"x has K = {K}, layer expects {self.K}")
+        _want(norm_q, torch.bfloat16, "norm_q", (128,))
+        _want(norm_k, torch.bfloat16, "norm_k", (128,))
+        _want(rope, torch.float32, "rope", (M, 64, 2))
+        y = torch.empty((M, self.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+        if M == 0:  # nothing to compute (empty tensors carry no device address)
+            return y
+        ws = self.workspace(M, x.device) if workspace is None else workspace
+        g = self.act_global if act_global is None else float(act_global)
+        fn = "svdq_w4a4_linear_qkv_norm_rope"
+        st = getattr(L.lib(), fn)(ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), M, g,
+                                  _p(norm_q), _p(norm_k), float(eps), _p(rope), _p(y), _p(ws),
+                                  ws.numel(), _stream())
+        L.check(st, fn)
+        return y
 
 
 class AwqLinear:

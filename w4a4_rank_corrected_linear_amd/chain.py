@@ -26,13 +26,17 @@ class DitBlockChain:
     3072->12288 and 12288->3072 (any K/N that chain the same way)."""
 
     def __init__(self, qkv: SvdqLinear, out: SvdqLinear, up: SvdqLinear, down: SvdqLinear,
-                 fuse_gelu: bool = False):
+                 fuse_gelu: bool = False, qk_norm=None):
+        """qk_norm: None, or (norm_q, norm_k, eps) to run the QKV projection with its
+        per-head Q/K RMSNorm and rotary embedding fused into the epilogue; forward then
+        takes the rotary table (float32 [M, 64, 2])."""
         if out.N != up.K or up.N != down.K or qkv.K != out.K:
             raise ValueError("layer shapes do not chain: "
                              f"qkv {qkv.K}->{qkv.N}, out {out.K}->{out.N}, up {up.K}->{up.N}, "
                              f"down {down.K}->{down.N}")
         self.qkv, self.out, self.up, self.down = qkv, out, up, down
         self.fuse_gelu = fuse_gelu
+        self.qk_norm = qk_norm
         self._buf = {}
 
     def _tensor(self, name: str, shape, device, dtype=torch.bfloat16) -> torch.Tensor:
@@ -42,15 +46,24 @@ class DitBlockChain:
             self._buf[name] = t
         return t
 
-    def forward(self, x: torch.Tensor) -> dict:
+    def forward(self, x: torch.Tensor, rope: torch.Tensor | None = None) -> dict:
         """x [M, K] bf16 -> {"qkv", "out", "up", "act", "down"} ("up" absent when the GELU
         is fused into MLP-up's epilogue); the buffers are reused by the next call of the
-        same M (copy what must outlive it)."""
+        same M (copy what must outlive it).  rope: the rotary table, needed when the
+        chain fuses the Q/K norm and rotary embedding into the QKV projection."""
         M, dev = x.shape[0], x.device
         need = max(layer.workspace_bytes(M) for layer in (self.qkv, self.out, self.up, self.down))
         ws = self._tensor("ws", (need,), dev, torch.uint8)   # one workspace, calls run in order
         r = {}
-        r["qkv"] = self.qkv(x, out=self._tensor("qkv", (M, self.qkv.N), dev), workspace=ws)
+        if self.qk_norm is not None:
+            if rope is None:
+                raise ValueError("this chain fuses the Q/K norm and rotary embedding: pass rope")
+            nq, nk, eps = self.qk_norm
+            r["qkv"] = self.qkv.qkv_norm_rope(x, nq, nk, eps, rope,
+                                              out=self._tensor("qkv", (M, self.qkv.N), dev),
+                                              workspace=ws)
+        else:
+            r["qkv"] = self.qkv(x, out=self._tensor("qkv", (M, self.qkv.N), dev), workspace=ws)
         r["out"] = self.out(x, out=self._tensor("out", (M, self.out.N), dev), workspace=ws)
         if self.fuse_gelu:
             r["act"] = self.up(r["out"], out=self._tensor("act", (M, self.up.N), dev), workspace=ws,
@@ -68,7 +81,7 @@ class DitBlockChain:
         names = ("qkv", "out", "act", "down") if self.fuse_gelu else ("qkv", "out", "up", "act", "down")
         return {n: self._buf[n] for n in names if n in self._buf}
 
-    def capture(self, xs) -> "Graph":
+    def capture(self, xs, rope: torch.Tensor | None = None) -> "Graph":
         """One HIP graph of len(xs) consecutive steps, step i on input xs[i] (all of one
         M): 4 or 5 kernels' worth of calls per step, replayed with one launch
         (Graph.launch).  After a replay the buffers hold the last step's results, as
@@ -77,11 +90,11 @@ class DitBlockChain:
         xs = list(xs)
         if not xs or any(x.shape != xs[0].shape for x in xs):
             raise ValueError("capture needs one or more step inputs of one shape")
-        self.forward(xs[0])          # creates the buffers outside the capture
+        self.forward(xs[0], rope)    # creates the buffers outside the capture
         torch.cuda.current_stream().synchronize()
 
         def steps():
             for x in xs:
-                self.forward(x)
+                self.forward(x, rope)
 
-        return capture(steps, keep=(tuple(xs), dict(self._buf)))
+        return capture(steps, keep=(tuple(xs), rope, dict(self._buf)))

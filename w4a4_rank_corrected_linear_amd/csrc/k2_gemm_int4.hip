@@ -16,10 +16,18 @@
 //                                                    < 32) and k = 4 or 5 (lanes >= 32),
 //                                                    the exact product 2 sw[n] sx[m]
 //   acc = fma(S, D, acc)                             one VALU op per element and group
-// The accumulator starts as U L2t^T (U split into bf16 hi + lo, four bf16 MFMAs per
-// 16 ranks), so the epilogue only adds the bias and stores.  All of the seed's global
-// loads (U in the fragment layout of common.h, two k-splits at a time, and lora_up)
-// are issued before the first is used.
+// The low-rank term U L2t^T (U split into bf16 hi + lo, four bf16 MFMAs per 16 ranks)
+// either seeds the accumulator before the main loop (all of its global loads issued
+// before the first is used) or, when K has at most two k-splits, is added in the
+// epilogue from copies of U and lora_up that the last two stages DMA into the ring
+// slots they leave free.
+//
+// Epilogues (EPI): + bias and the bf16 store; the same with the exact GELU of each
+// result before the rounding; or the fused QKV epilogue (128-wide tiles, one head
+// each): on Q and K tiles the RMSNorm of every row over the head (the two waves of a
+// row exchange their sums of squares through LDS), the channel weights, and the
+// rotary turn of adjacent column pairs by the row's (cos, sin), all in fp32 on the
+// unrounded result, then one rounding.
 //
 // Tiling: one 512-thread workgroup (8 waves, two per SIMD) per CU, tile 256 x BN,
 // wave tile 64 x BN/2 (2 x BN/64 blocks).  A stage is two 64-groups.  Operands live
@@ -77,13 +85,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 }  // namespace
 
-template <int BN, bool GELU>
+template <int BN, int EPI>
 __global__ void __launch_bounds__(512, 1)
 k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
              const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
              const uint2* __restrict__ sB, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-             int M, int N, int K, int M_pad, int rank) {
+             int M, int N, int K, int M_pad, int rank, QkEpi qk) {
   constexpr int BM = 256;
   constexpr int WN = BN / 64;              // 32-column blocks per wave
   constexpr int CB = BN / 32;              // 32-column blocks per tile
@@ -93,8 +101,10 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   constexpr int NB = 4 * WN;               // blocks per wave and stage
   constexpr int NBS = (WN == 3) ? 3 : 4;   // B register sets (divides 2 WN fragments)
   static_assert(WN == 2 || WN == 3, "tile width 128 or 192");
+  static_assert(EPI != kEpiQkNormRope || BN == 128, "the QKV epilogue needs one head per tile");
   __shared__ __attribute__((aligned(16))) uint32_t ring[3 * SLOT];
   __shared__ __attribute__((aligned(16))) uint16_t bias_s[BN];
+  __shared__ float red[EPI == kEpiQkNormRope ? 512 : 1];  // per-row sums of squares, by wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -391,6 +401,30 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   // contiguous run of full 64-byte sectors.
   wait_vm0();
   barrier_lds();
+  // fused QKV epilogue: the row's rotary pairs and the head's channel weights are
+  // loaded here so that their latency hides under the low-rank MFMAs below.  Lane
+  // element 4q + p of block j is channel c = 64 wn + 32 j + 8 q + 4 lh + p of the head,
+  // so its four channels are the pairs c/2 and c/2 + 1 (one 16-byte load of cos, sin).
+  [[maybe_unused]] const bool qk_tile = EPI == kEpiQkNormRope && col0 < 2 * (N / 3);
+  [[maybe_unused]] float4 rcs[2][WN][4];
+  [[maybe_unused]] uint2 nwv[WN][4];
+  if constexpr (EPI == kEpiQkNormRope) {
+    if (qk_tile) {
+      const uint16_t* nw = col0 < N / 3 ? qk.norm_q : qk.norm_k;
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * 64 + j * 32 + 8 * q + 4 * lh;
+          nwv[j][q] = *reinterpret_cast<const uint2*>(nw + c);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int row = min(row0 + wm * 64 + 32 * i + lr, M - 1);  // pad rows are not stored
+            rcs[i][j][q] = *reinterpret_cast<const float4*>(qk.rope + (size_t)row * 128 + c);
+          }
+        }
+    }
+  }
   if (late_seed) {
     // split 0 and lora_up were copied at the top of stage S-2 into slot S % 3, split 1
     // at the top of stage S-1 into slot (S+1) % 3
@@ -437,10 +471,9 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     }
     barrier_lds();  // the staging tiles below overwrite the seed copies
   }
-  uint16_t* tile = reinterpret_cast<uint16_t*>(ring) + wave * (64 * (BN / 2 + 8));
-#pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    float bv[16];
+  // bias of the lane's 16 columns of block j (column 32 j' + 8 q + 4 lh + p of the
+  // tile, j' = wn WN + j)
+  auto bias16 = [&](int j, float (&bv)[16]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint2 b2 = bias ? *reinterpret_cast<const uint2*>(bias_s + (wn * WN + j) * 32 + 8 * q + 4 * lh)
@@ -450,6 +483,70 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       bv[4 * q + 2] = __uint_as_float(b2.y << 16);
       bv[4 * q + 3] = __uint_as_float(b2.y & 0xFFFF0000u);
     }
+  };
+  bool done = false;  // acc already holds the final values (bias included)
+  if constexpr (EPI == kEpiQkNormRope) {
+    // Q and K tiles (the first two thirds of the columns) hold one head each: RMSNorm
+    // over the head's 128 columns of a row, the channel weights, then the rotary turn
+    // of adjacent column pairs by the row's angles.  The tile is uniform, so the
+    // barrier below is reached by every wave or by none.
+    if (qk_tile) {
+      float ss[2] = {0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        float bv[16];
+        bias16(j, bv);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float v = acc[i][j][e] + bv[e];
+            acc[i][j][e] = v;
+            ss[i] = fmaf(v, v, ss[i]);
+          }
+      }
+      // the lane pair (l, l + 32) holds one row's 32 + 32 columns of the wave; the
+      // partner wave (wave ^ 1, same rows) the other 64 columns of the head
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ss[i] += __shfl_xor(ss[i], 32);
+      if (lh == 0) {
+        red[wave * 64 + lr] = ss[0];
+        red[wave * 64 + 32 + lr] = ss[1];
+      }
+      barrier_lds();
+      float inv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float tot = ss[i] + red[(wave ^ 1) * 64 + 32 * i + lr];
+        inv[i] = 1.0f / sqrtf(tot * (1.0f / 128.0f) + qk.eps);
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint2 w2 = nwv[j][q];
+          const float w[4] = {__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xFFFF0000u),
+                              __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xFFFF0000u)};
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const float4 cs = rcs[i][j][q];
+            float n[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) n[p] = acc[i][j][4 * q + p] * inv[i] * w[p];
+            acc[i][j][4 * q + 0] = n[0] * cs.x - n[1] * cs.y;
+            acc[i][j][4 * q + 1] = n[1] * cs.x + n[0] * cs.y;
+            acc[i][j][4 * q + 2] = n[2] * cs.z - n[3] * cs.w;
+            acc[i][j][4 * q + 3] = n[3] * cs.z + n[2] * cs.w;
+          }
+        }
+      done = true;
+    }
+  }
+  uint16_t* tile = reinterpret_cast<uint16_t*>(ring) + wave * (64 * (BN / 2 + 8));
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    float bv[16];
+    bias16(j, bv);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -457,8 +554,8 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
         uint32_t h[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float v = acc[i][j][4 * q + p] + bv[4 * q + p];
-          h[p] = f32_to_bf16_rne(GELU ? gelu_f32(v) : v);
+          const float v = done ? acc[i][j][4 * q + p] : acc[i][j][4 * q + p] + bv[4 * q + p];
+          h[p] = f32_to_bf16_rne(EPI == kEpiGelu ? gelu_f32(v) : v);
         }
         *reinterpret_cast<uint2*>(tile + (32 * i + lr) * (BN / 2 + 8) + 32 * j + 8 * q + 4 * lh) =
             make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
@@ -506,19 +603,23 @@ double fill(int64_t tiles, int cus) {
 hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
                           const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, bool gelu, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                          int rank, int epi, const QkEpi& qk, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   if (M_pad % 256 != 0 || N % 128 != 0 || K % 128 != 0) return hipErrorInvalidValue;
-  bool wide = N % 192 == 0;
+  if (epi == kEpiQkNormRope && (N % 384 != 0 || !qk.norm_q || !qk.norm_k || !qk.rope))
+    return hipErrorInvalidValue;
+  bool wide = N % 192 == 0 && epi != kEpiQkNormRope;
   if (wide) {
     const int cus = cu_count();
     const int64_t t192 = (int64_t)(N / 192) * (M_pad / 256), t128 = (int64_t)(N / 128) * (M_pad / 256);
     if (fill(t128, cus) > 1.1 * fill(t192, cus)) wide = false;
   }
   const unsigned g = (unsigned)((N / (wide ? 192 : 128)) * (M_pad / 256));
-  auto k = wide ? (gelu ? k2_gemm_int4<192, true> : k2_gemm_int4<192, false>)
-                : (gelu ? k2_gemm_int4<128, true> : k2_gemm_int4<128, false>);
+  auto k = epi == kEpiQkNormRope ? k2_gemm_int4<128, kEpiQkNormRope>
+           : wide ? (epi == kEpiGelu ? k2_gemm_int4<192, kEpiGelu> : k2_gemm_int4<192, kEpiPlain>)
+                  : (epi == kEpiGelu ? k2_gemm_int4<128, kEpiGelu> : k2_gemm_int4<128, kEpiPlain>);
   hipExtLaunchKernelGGL(k, dim3(g), dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB, L2t,
-                        bias, Y, M, N, K, M_pad, rank);
+                        bias, Y, M, N, K, M_pad, rank, qk);
   return hipGetLastError();
 }
 

@@ -22,11 +22,23 @@ hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uin
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
 
+// Epilogue of the GEMMs: plain (+ bias, bf16), exact GELU before the rounding, or the
+// fused QKV epilogue (per-head RMSNorm and rotary embedding on the Q and K thirds of
+// the columns, heads of 128; V plain).
+enum Epilogue { kEpiPlain = 0, kEpiGelu = 1, kEpiQkNormRope = 2 };
+
+struct QkEpi {
+  const uint16_t* norm_q;  // bf16 [128]
+  const uint16_t* norm_k;  // bf16 [128]
+  const float* rope;       // fp32 [M][64][2]: (cos, sin) per token and pair
+  float eps;
+};
+
 hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
                           const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, bool gelu, hipStream_t st, hipEvent_t ev0 = nullptr,
-                          hipEvent_t ev1 = nullptr);
+                          int rank, int epi, const QkEpi& qk, hipStream_t st,
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,

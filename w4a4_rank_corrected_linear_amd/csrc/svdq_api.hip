@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -312,11 +313,16 @@ namespace {
 // The layer call behind svdq_w4a4_linear (gelu = false) and svdq_w4a4_linear_gelu.
 svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_weight* w,
                         const uint16_t* x, int64_t M, float act_global, uint16_t* y,
-                        void* workspace, size_t workspace_bytes, bool gelu, hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, int epi, const svdq::QkEpi& qk,
+                        hipStream_t stream) {
   if (!cfg || !w || !x || !y || !workspace || !w->qweight || !w->wscales || !w->smooth)
     return fail(SVDQ_ERR_NULL, "%s: NULL argument", fn);
+  if (epi == svdq::kEpiQkNormRope && (!qk.norm_q || !qk.norm_k || !qk.rope))
+    return fail(SVDQ_ERR_NULL, "%s: NULL norm weight or rotary table", fn);
   SVDQ_TRY(check_svdq_config(cfg));
   const bool nv = cfg->precision == SVDQ_NVFP4;
+  if (epi == svdq::kEpiQkNormRope && nv)
+    return fail(SVDQ_ERR_CONFIG, "%s: the fused QKV epilogue is built for int4 only", fn);
   if (nv) {
     SVDQ_TRY(check_global(act_global, "activation"));
     SVDQ_TRY(check_global(w->w_global, "weight"));
@@ -328,6 +334,14 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
   SVDQ_TRY(check_m(M, w->K));
   if (M * w->N > (int64_t(1) << 36))
     return fail(SVDQ_ERR_SHAPE, "M * N too large");
+  if (epi == svdq::kEpiQkNormRope && w->N % 384 != 0)
+    return fail(SVDQ_ERR_SHAPE, "%s: N = %lld must be 3 x (a multiple of 128): Q, K, V of heads "
+                "of 128", fn, (long long)w->N);
+  if (epi == svdq::kEpiQkNormRope && !(std::isfinite(qk.eps) && qk.eps > 0.f))
+    return fail(SVDQ_ERR_RANGE, "%s: eps = %g must be finite and positive", fn, (double)qk.eps);
+  if (epi == svdq::kEpiQkNormRope &&
+      (!aligned16(qk.norm_q) || !aligned16(qk.norm_k) || !aligned16(qk.rope)))
+    return fail(SVDQ_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || !aligned16(w->qweight) ||
       !aligned16(w->wscales) || !aligned16(w->smooth) || (w->bias && !aligned16(w->bias)) ||
       (cfg->rank > 0 && (!aligned16(w->lora_down) || !aligned16(w->lora_up))))
@@ -357,7 +371,8 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                                              svdq::k1_splits((int)w->K),
                                              reinterpret_cast<const uint16_t*>(w->qweight),
                                              w->lora_up, w->bias, g, y, (int)M, (int)w->N,
-                                             (int)w->K, (int)L.M_pad, cfg->rank, gelu, stream,
+                                             (int)w->K, (int)L.M_pad, cfg->rank,
+                                             epi == svdq::kEpiGelu, stream,
                                              e2.start, e2.end),
                        "gemm kernel launch"));
     return ok();
@@ -372,7 +387,7 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                                            w->qweight,
                                            static_cast<const uint2*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
-                                           cfg->rank, gelu, stream, e2.start, e2.end),
+                                           cfg->rank, epi, qk, stream, e2.start, e2.end),
                      "gemm kernel launch"));
   return ok();
 }
@@ -383,14 +398,25 @@ svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, 
                              int64_t M, float act_global, uint16_t* y, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
   return linear_impl("svdq_w4a4_linear", cfg, w, x, M, act_global, y, workspace, workspace_bytes,
-                     false, stream);
+                     svdq::kEpiPlain, svdq::QkEpi{}, stream);
 }
 
 svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight* w,
                                   const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return linear_impl("svdq_w4a4_linear_gelu", cfg, w, x, M, act_global, y, workspace,
-                     workspace_bytes, true, stream);
+                     workspace_bytes, svdq::kEpiGelu, svdq::QkEpi{}, stream);
+}
+
+svdq_status svdq_w4a4_linear_qkv_norm_rope(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                           const uint16_t* x, int64_t M, float act_global,
+                                           const uint16_t* norm_q, const uint16_t* norm_k,
+                                           float eps, const float* rope, uint16_t* y,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  return linear_impl("svdq_w4a4_linear_qkv_norm_rope", cfg, w, x, M, act_global, y, workspace,
+                     workspace_bytes, svdq::kEpiQkNormRope, svdq::QkEpi{norm_q, norm_k, rope, eps},
+                     stream);
 }
 
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, const uint16_t* x,
