@@ -165,7 +165,8 @@ def run_chain(args) -> int:
         qk_norm = (nq, nk, I.QK_NORM_EPS)
         rope = torch.from_numpy(I.rope_table(M)).to(dev)
     chain = svdq.DitBlockChain(lay["qkv"], lay["out"], lay["up"], lay["down"],
-                               fuse_gelu=args.fuse_gelu, qk_norm=qk_norm)
+                               fuse_gelu=args.fuse_gelu, qk_norm=qk_norm,
+                               fuse_qk=not args.qk_separate)
     xs = [bf16(I.chain_step_activations(M, s)) for s in range(8)]
     print(f"[bench] workload chain: DiT block (QKV, out, MLP-up, GELU, MLP-down), M={M}, 8 fresh "
           f"step inputs; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
@@ -213,7 +214,8 @@ def run_chain(args) -> int:
 
     # per-layer times: events around each call on the current stream (they include the
     # dispatch of the call's kernels)
-    names = ["qkv", "out", "up", "down"] if args.fuse_gelu else ["qkv", "out", "up", "gelu", "down"]
+    names = ["qkv"] + (["qk_norm_rope"] if args.qkv_norm_rope and args.qk_separate else []) + (
+        ["out", "up", "down"] if args.fuse_gelu else ["out", "up", "gelu", "down"])
     n_inst = min(args.steps, 200)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in names] for _ in range(n_inst)]
@@ -223,9 +225,14 @@ def run_chain(args) -> int:
             "up": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
             "act": torch.empty((M, lay["up"].N), dtype=torch.bfloat16, device=dev),
             "down": torch.empty((M, lay["down"].N), dtype=torch.bfloat16, device=dev)}
+    sep = bool(qk_norm) and args.qk_separate
     calls = [(lambda x: lay["qkv"].qkv_norm_rope(x, *qk_norm[:2], qk_norm[2], rope, out=bufs["qkv"],
-                                                 workspace=ws)) if qk_norm else
-             (lambda x: lay["qkv"](x, out=bufs["qkv"], workspace=ws)),
+                                                 workspace=ws)) if qk_norm and not sep else
+             (lambda x: lay["qkv"](x, out=bufs["qkv"], workspace=ws))]
+    if sep:
+        calls.append(lambda x: svdq.qk_norm_rope(bufs["qkv"], *qk_norm[:2], qk_norm[2], rope,
+                                                 out=bufs["qkv"]))
+    calls += [
              lambda x: lay["out"](x, out=bufs["out"], workspace=ws)]
     if args.fuse_gelu:
         calls.append(lambda x: lay["up"](bufs["out"], out=bufs["act"], workspace=ws, gelu=True))
@@ -248,12 +255,15 @@ def run_chain(args) -> int:
     value = ops_step / (ms_per_step * 1e-3) / 1e12
     layers = {n: {"ms": round(per[n], 6),
                   **({"TOPS": round(2.0 * M * shapes[n][0] * shapes[n][1] / (per[n] * 1e-3) / 1e12, 3)}
-                     if n in shapes else {"GBps": round(4.0 * M * shapes["up"][1] / (per[n] * 1e-3) / 1e9, 1)})}
+                     if n in shapes else {"GBps": round(
+                         (4.0 * M * shapes["up"][1] if n == "gelu" else
+                          4.0 * M * shapes["qkv"][1] * 2 / 3 + M * 512) / (per[n] * 1e-3) / 1e9, 1)})}
               for n in names}
     out = {
         "metric": f"DiT block chain of svdq_w4a4 int4 linears (QKV, out, MLP-up, GELU, MLP-down) "
                   f"effective TOPS at M={M}" + (", GELU fused into MLP-up" if args.fuse_gelu else "")
-                  + (", Q/K norm + rotary fused into QKV" if args.qkv_norm_rope else "")
+                  + ((", Q/K norm + rotary as a separate pass" if args.qk_separate else
+                      ", Q/K norm + rotary fused into QKV") if args.qkv_norm_rope else "")
                   + (", 8 steps per HIP graph" if args.graph else ""),
         "value": round(value, 3),
         "unit": "TOPS",
@@ -382,6 +392,9 @@ def main() -> int:
     ap.add_argument("--qkv-norm-rope", action="store_true",
                     help="qkv and chain workloads: the fused QKV epilogue with per-head Q/K RMSNorm and the "
                          "rotary embedding (1024x1024 DiT table)")
+    ap.add_argument("--qk-separate", action="store_true",
+                    help="chain with --qkv-norm-rope: the Q/K norm + rotary as a separate pass "
+                         "over the bf16 QKV output instead of the fused epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (scale reference for HBM counters)")

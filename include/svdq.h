@@ -187,6 +187,18 @@ svdq_status svdq_w4a4_linear_qkv_norm_rope(const svdq_config* cfg, const svdq_w4
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 
+/* The same per-head Q/K RMSNorm and rotary embedding as a separate pass over a bf16
+ * QKV output x [M][N] (the unfused form: the projection is rounded to bf16 first, then
+ * normalised and turned, in fp32, and rounded again).  y [M][N] receives the Q and K
+ * thirds so transformed and, when y != x, a copy of the V third; y == x works in
+ * place, other overlaps are undefined.  norm_q, norm_k, rope, eps and N as for
+ * svdq_w4a4_linear_qkv_norm_rope; M >= 0 (M = 0 launches nothing).  Device pointers,
+ * 16-byte aligned.  Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_RANGE,
+ * SVDQ_ERR_ALIGN, SVDQ_ERR_DEVICE, SVDQ_ERR_HIP.  Not recorded by the timing hook. */
+svdq_status svdq_qk_norm_rope_bf16(const uint16_t* x, uint16_t* y, int64_t M, int64_t N,
+                                   const uint16_t* norm_q, const uint16_t* norm_k, float eps,
+                                   const float* rope, hipStream_t stream);
+
 /* The AWQ W4A16 comparison layer: Y[M][N] (bf16) from bf16 X[M][K].  cfg must be
  * {int4, 64, rank 0, bf16}. */
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,

@@ -96,6 +96,8 @@ def test_workspace_size_and_check():
     assert need == 98304 + 16384 + 32768
     assert linear(cfg(), weight(), M=100, ws_bytes=need - 1) == L.ERR_WORKSPACE
     assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 16384
+    nv = lib.svdq_workspace_bytes(ctypes.byref(cfg(precision=L.NVFP4, group=16)), 100, 512)
+    assert nv == 128 * 512 * 2 + 128 * 32 * 4   # exact bf16 operand [M_pad][K] and U
 
 
 def test_packed_weight_bytes():
@@ -223,3 +225,18 @@ def test_qkv_norm_rope_entry_validation():
     for bad in (0.0, -1e-6, float("nan"), float("inf")):
         assert call(cfg(), w, eps=bad) == L.ERR_RANGE
     assert call(cfg(), w, rope=FAKE_MISALIGNED) == L.ERR_ALIGN
+
+
+def test_separate_qk_norm_rope_validation():
+    lib = L.lib()
+
+    def call(M=16, N=768, eps=1e-6, x=FAKE, rope=FAKE):
+        return lib.svdq_qk_norm_rope_bf16(x, FAKE, M, N, FAKE, FAKE, eps, rope, None)
+
+    assert call(x=None) == L.ERR_NULL
+    assert call(rope=None) == L.ERR_NULL
+    assert call(N=512) == L.ERR_SHAPE
+    assert call(M=-1) == L.ERR_SHAPE
+    assert call(eps=0.0) == L.ERR_RANGE
+    assert call(rope=FAKE_MISALIGNED) == L.ERR_ALIGN
+    assert call(M=0) == L.OK

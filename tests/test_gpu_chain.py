@@ -189,3 +189,20 @@ def test_block_chain_fully_fused_with_graph(block):
     r = OL.w4a4_linear_rows("int4", x_np[-1], layers["qkv"], rows)["r"]
     check_y(ref["qkv"][rows], AT.qkv_norm_rope_f64(r, nq, nk, I.QK_NORM_EPS, rope_np[rows]))
     check_y(ref["down"][rows], OL.w4a4_linear_rows("int4", ref["act"], layers["down"], rows)["r"])
+
+
+def test_block_chain_with_separate_qk_pass(block):
+    """fuse_qk=False: the plain QKV projection, then the separate Q/K norm + rotary pass
+    on its bf16 output (in place); checked against the oracle on that bf16 output."""
+    from oracle import attention as AT
+    _, _, dev = block
+    M = 1000
+    nq, nk = I.qk_norm_weights()
+    rope_np = I.rope_table(M)
+    x = dev_bf16(I.chain_step_activations(M, 2))
+    plain = host_bits(dev["qkv"](x)).copy()
+    chain = svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"], fuse_gelu=True,
+                               qk_norm=(dev_bf16(nq), dev_bf16(nk), I.QK_NORM_EPS), fuse_qk=False)
+    got = host_bits(chain(x, torch.from_numpy(rope_np).cuda())["qkv"])
+    check_y(got, AT.qkv_norm_rope_f64(F.bf16_to_f64(plain), nq, nk, I.QK_NORM_EPS, rope_np))
+    assert np.array_equal(got[:, 6144:], plain[:, 6144:])

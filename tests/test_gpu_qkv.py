@@ -12,6 +12,7 @@ import torch
 import w4a4_rank_corrected_linear_amd as svdq
 from helpers import check_y, dev_bf16, dev_u8, host_bits
 from oracle import attention as AT
+from oracle import formats as F
 from oracle import linear as OL
 from oracle import prep as P
 from synth import inputs as I
@@ -101,3 +102,23 @@ def test_qkv_norm_rope_dit_block_full_size():
     rows = np.array([0, 1, 300, 511, 512, 513, 1000, 2222, 4000, 4606, 4607])
     r = OL.w4a4_linear_rows("int4", x, layer, rows)["r"]
     check_y(y[rows], AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[rows]))
+
+
+@pytest.mark.parametrize("M,N", [(1, 384), (37, 768), (4608, 9216)])
+def test_separate_qk_norm_rope_pass(M, N):
+    """svdq_qk_norm_rope_bf16 on a bf16 QKV output: the oracle's norm + rotation of the
+    bf16 values, once rounded; V copied out of place and untouched in place."""
+    rng = np.random.default_rng(M + N)
+    x = I.to_bf16_bits((rng.standard_normal((M, N)) * 3.0).astype(np.float32))
+    if M > 1:
+        x[M // 2, : 2 * N // 3] = 0          # an all-zero row of Q and K heads
+    rope = I.rope_table(M) if N == 9216 else np.stack(
+        [np.cos(a := rng.uniform(-4, 4, (M, 64))), np.sin(a)], axis=2).astype(np.float32)
+    nq, nk = I.qk_norm_weights()
+    xd = dev_bf16(x)
+    y = host_bits(svdq.qk_norm_rope(xd, dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope)))
+    ref = AT.qkv_norm_rope_f64(F.bf16_to_f64(x), nq, nk, EPS, rope)
+    check_y(y, ref)
+    assert np.array_equal(y[:, 2 * N // 3:], x[:, 2 * N // 3:])
+    svdq.qk_norm_rope(xd, dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope), out=xd)
+    assert np.array_equal(host_bits(xd), y)

@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     gelu,
     pack_lora_down,
     pack_weight,
+    qk_norm_rope,
     quantize_act,
     timing_start,
     timing_stop,

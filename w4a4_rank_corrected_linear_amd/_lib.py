@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.svdq_w4a4_linear_qkv_norm_rope.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32,
                                                  vp, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]
     L.svdq_w4a4_linear_qkv_norm_rope.restype = st
+    L.svdq_qk_norm_rope_bf16.argtypes = [vp, vp, i64, i64, vp, vp, f32, vp, vp]
+    L.svdq_qk_norm_rope_bf16.restype = st
     L.awq_w4a16_linear.argtypes = [cfgp, ctypes.POINTER(AwqW4A16Weight), vp, i64, vp, vp]
     L.awq_w4a16_linear.restype = st
     L.svdq_gelu_bf16.argtypes = [vp, vp, i64, vp]

@@ -278,6 +278,24 @@ def capture(fn, keep=()) -> Graph:
     return Graph(h.value, keep)
 
 
+def qk_norm_rope(x: torch.Tensor, norm_q: torch.Tensor, norm_k: torch.Tensor, eps: float,
+                 rope: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """svdq_qk_norm_rope_bf16: per-head Q/K RMSNorm + rotary embedding of a bf16 QKV
+    output [M, N] (out=x works in place; V is copied when out is another tensor)."""
+    _want(x, torch.bfloat16, "x")
+    M, N = x.shape
+    _want(norm_q, torch.bfloat16, "norm_q", (128,))
+    _want(norm_k, torch.bfloat16, "norm_k", (128,))
+    _want(rope, torch.float32, "rope", (M, 64, 2))
+    y = torch.empty_like(x) if out is None else _want(out, torch.bfloat16, "out", (M, N))
+    if M == 0:
+        return y
+    L.check(L.lib().svdq_qk_norm_rope_bf16(_p(x), _p(y), M, N, _p(norm_q), _p(norm_k),
+                                           float(eps), _p(rope), _stream()),
+            "svdq_qk_norm_rope_bf16")
+    return y
+
+
 def timing_start(max_calls: int) -> None:
     """svdq_timing_start: record per-kernel HIP events in the next `max_calls` layer
     calls made on this thread."""

@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import torch
 
-from .api import Graph, SvdqLinear, capture, gelu
+from .api import Graph, SvdqLinear, capture, gelu, qk_norm_rope
 
 
 class DitBlockChain:
@@ -26,10 +26,11 @@ class DitBlockChain:
     3072->12288 and 12288->3072 (any K/N that chain the same way)."""
 
     def __init__(self, qkv: SvdqLinear, out: SvdqLinear, up: SvdqLinear, down: SvdqLinear,
-                 fuse_gelu: bool = False, qk_norm=None):
-        """qk_norm: None, or (norm_q, norm_k, eps) to run the QKV projection with its
-        per-head Q/K RMSNorm and rotary embedding fused into the epilogue; forward then
-        takes the rotary table (float32 [M, 64, 2])."""
+                 fuse_gelu: bool = False, qk_norm=None, fuse_qk: bool = True):
+        """qk_norm: None, or (norm_q, norm_k, eps) to apply the per-head Q/K RMSNorm and
+        rotary embedding to the QKV output, fused into the projection's epilogue
+        (fuse_qk) or as a separate pass over its bf16 output; forward then takes the
+        rotary table (float32 [M, 64, 2])."""
         if out.N != up.K or up.N != down.K or qkv.K != out.K:
             raise ValueError("layer shapes do not chain: "
                              f"qkv {qkv.K}->{qkv.N}, out {out.K}->{out.N}, up {up.K}->{up.N}, "
@@ -37,6 +38,7 @@ class DitBlockChain:
         self.qkv, self.out, self.up, self.down = qkv, out, up, down
         self.fuse_gelu = fuse_gelu
         self.qk_norm = qk_norm
+        self.fuse_qk = fuse_qk
         self._buf = {}
 
     def _tensor(self, name: str, shape, device, dtype=torch.bfloat16) -> torch.Tensor:
@@ -59,9 +61,12 @@ class DitBlockChain:
             if rope is None:
                 raise ValueError("this chain fuses the Q/K norm and rotary embedding: pass rope")
             nq, nk, eps = self.qk_norm
-            r["qkv"] = self.qkv.qkv_norm_rope(x, nq, nk, eps, rope,
-                                              out=self._tensor("qkv", (M, self.qkv.N), dev),
-                                              workspace=ws)
+            qkv = self._tensor("qkv", (M, self.qkv.N), dev)
+            if self.fuse_qk:
+                r["qkv"] = self.qkv.qkv_norm_rope(x, nq, nk, eps, rope, out=qkv, workspace=ws)
+            else:
+                self.qkv(x, out=qkv, workspace=ws)
+                r["qkv"] = qk_norm_rope(qkv, nq, nk, eps, rope, out=qkv)
         else:
             r["qkv"] = self.qkv(x, out=self._tensor("qkv", (M, self.qkv.N), dev), workspace=ws)
         r["out"] = self.out(x, out=self._tensor("out", (M, self.out.N), dev), workspace=ws)

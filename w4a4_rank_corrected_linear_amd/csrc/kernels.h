@@ -64,4 +64,10 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
 
 hipError_t launch_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t st);
 
+// Per-head Q/K RMSNorm + rotary embedding on a bf16 [M][N] QKV output (N = 3 H 128);
+// the V third is copied when y != x.
+hipError_t launch_qk_norm_rope_bf16(const uint16_t* x, uint16_t* y, int64_t M, int N,
+                                    const uint16_t* norm_q, const uint16_t* norm_k, float eps,
+                                    const float* rope, hipStream_t st);
+
 }  // namespace svdq

@@ -512,6 +512,29 @@ svdq_status svdq_graph_destroy(svdq_graph* graph) {
   return hip_check(e2, "hipGraphDestroy");
 }
 
+svdq_status svdq_qk_norm_rope_bf16(const uint16_t* x, uint16_t* y, int64_t M, int64_t N,
+                                   const uint16_t* norm_q, const uint16_t* norm_k, float eps,
+                                   const float* rope, hipStream_t stream) {
+  if (!x || !y || !norm_q || !norm_k || !rope)
+    return fail(SVDQ_ERR_NULL, "svdq_qk_norm_rope_bf16: NULL argument");
+  if (N <= 0 || N % 384 != 0 || N > (int64_t(1) << 20))
+    return fail(SVDQ_ERR_SHAPE, "svdq_qk_norm_rope_bf16: N = %lld must be a positive multiple "
+                "of 384 (<= 2^20)", (long long)N);
+  if (M < 0 || M * N > (int64_t(1) << 36))
+    return fail(SVDQ_ERR_SHAPE, "svdq_qk_norm_rope_bf16: M = %lld out of range", (long long)M);
+  if (!(std::isfinite(eps) && eps > 0.f))
+    return fail(SVDQ_ERR_RANGE, "svdq_qk_norm_rope_bf16: eps = %g must be finite and positive",
+                (double)eps);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(norm_q) || !aligned16(norm_k) ||
+      !aligned16(rope))
+    return fail(SVDQ_ERR_ALIGN, "svdq_qk_norm_rope_bf16: pointers must be 16-byte aligned");
+  if (M == 0) return ok();
+  SVDQ_TRY(check_current_device());
+  return hip_check(svdq::launch_qk_norm_rope_bf16(x, y, M, (int)N, norm_q, norm_k, eps, rope,
+                                                  stream),
+                   "qk norm kernel launch");
+}
+
 svdq_status svdq_timing_start(int max_calls) {
   if (max_calls < 1 || max_calls > 65536)
     return fail(SVDQ_ERR_SHAPE, "svdq_timing_start: max_calls = %d out of [1, 65536]", max_calls);
