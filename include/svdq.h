@@ -177,9 +177,9 @@ svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight
  * and y = bf16_rne(r) on the V columns; one rounding per output.
  * norm_q, norm_k: device, bf16 [128].  rope: device, fp32 [M][64][2], (cos, sin) of
  * token m and pair i at rope[(m * 64 + i) * 2 + {0, 1}], the same for every head and
- * for Q and K.  eps: finite and positive (SVDQ_ERR_RANGE).  cfg must be int4 (nvfp4:
- * SVDQ_ERR_CONFIG); N a multiple of 384 (SVDQ_ERR_SHAPE); every pointer 16-byte
- * aligned.  Workspace, stream and other errors as for svdq_w4a4_linear. */
+ * for Q and K.  eps: finite and positive (SVDQ_ERR_RANGE).  int4 and nvfp4 (act_global
+ * as for svdq_w4a4_linear); N a multiple of 384 (SVDQ_ERR_SHAPE); every pointer
+ * 16-byte aligned.  Workspace, stream and other errors as for svdq_w4a4_linear. */
 svdq_status svdq_w4a4_linear_qkv_norm_rope(const svdq_config* cfg, const svdq_w4a4_weight* w,
                                            const uint16_t* x, int64_t M, float act_global,
                                            const uint16_t* norm_q, const uint16_t* norm_k,

@@ -209,8 +209,8 @@ def test_graph_entry_validation():
 
 
 def test_qkv_norm_rope_entry_validation():
-    """The fused QKV entry point: NULL norm weights or table, nvfp4, N not a multiple
-    of 384, eps not finite and positive, misaligned table."""
+    """The fused QKV entry point: NULL norm weights or table, an unsupported config, N
+    not a multiple of 384, eps not finite and positive, misaligned table."""
     lib = L.lib()
 
     def call(c, w, nq=FAKE, nk=FAKE, eps=1e-6, rope=FAKE):
@@ -220,7 +220,7 @@ def test_qkv_norm_rope_entry_validation():
     w = weight(K=512, N=768)
     assert call(cfg(), w, nq=None) == L.ERR_NULL
     assert call(cfg(), w, rope=None) == L.ERR_NULL
-    assert call(cfg(precision=L.NVFP4, group=16), w) == L.ERR_CONFIG
+    assert call(cfg(precision=L.NVFP4, group=16, rank=48), w) == L.ERR_CONFIG
     assert call(cfg(), weight(K=512, N=512)) == L.ERR_SHAPE
     for bad in (0.0, -1e-6, float("nan"), float("inf")):
         assert call(cfg(), w, eps=bad) == L.ERR_RANGE

@@ -122,3 +122,30 @@ def test_separate_qk_norm_rope_pass(M, N):
     assert np.array_equal(y[:, 2 * N // 3:], x[:, 2 * N // 3:])
     svdq.qk_norm_rope(xd, dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope), out=xd)
     assert np.array_equal(host_bits(xd), y)
+
+
+@pytest.fixture(scope="module")
+def tiny_qkv_nvfp4():
+    li = I.layer_inputs(config_id=1, M=300, K=512, N=768, outlier_count=4, factor=20.0)
+    layer = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=32, precision="nvfp4")
+    rng = np.random.default_rng(41)
+    ang = rng.uniform(-np.pi, np.pi, (300, 64))
+    rope = np.stack([np.cos(ang), np.sin(ang)], axis=2).astype(np.float32)
+    return li, layer, rope
+
+
+@pytest.mark.parametrize("M", [1, 129, 300])
+def test_qkv_norm_rope_nvfp4(tiny_qkv_nvfp4, M):
+    """The NVFP4 GEMM's fused QKV epilogue against the oracle; V equals the plain
+    NVFP4 linear bit for bit."""
+    li, layer, rope = tiny_qkv_nvfp4
+    nq, nk = I.qk_norm_weights()
+    dev = svdq.SvdqLinear.from_interchange(
+        dev_u8(layer.qweight), dev_u8(layer.wscales), dev_bf16(layer.smooth),
+        dev_bf16(layer.lora_down), dev_bf16(layer.lora_up), dev_bf16(layer.bias),
+        precision="nvfp4", w_global=layer.w_global, act_global=layer.act_global)
+    x = dev_bf16(li.x[:M])
+    y = host_bits(dev.qkv_norm_rope(x, dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope[:M])))
+    r = OL.w4a4_linear("nvfp4", li.x[:M], layer)["r"]
+    check_y(y, AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[:M]))
+    assert np.array_equal(y[:, 512:], host_bits(dev(x))[:, 512:])

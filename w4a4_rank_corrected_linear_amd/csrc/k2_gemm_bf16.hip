@@ -18,20 +18,28 @@
 // tile as 16-byte units u = row * 8 + (c ^ (row & 7)), c = k / 8 within the stage: the
 // XOR swizzle puts the eight rows that one MFMA operand read touches at once in
 // distinct bank groups; it is applied by choosing each lane's source address.
+//
+// The accumulator blocks are held transposed (the weight fragment is the MFMA's first
+// operand): lane l % 32 is the output row, its 16 elements are columns
+// 8 q + 4 (l / 32) + p of the block (element 4 q + p).  Epilogues: + bias and the bf16
+// store; the same with the exact GELU before the rounding; or the fused QKV epilogue
+// (per-head RMSNorm over the 128 columns of a tile, the channel weights and the rotary
+// turn of adjacent column pairs, on the Q and K tiles), as in the int4 GEMM.
 #include "common.h"
 #include "kernels.h"
 
 namespace svdq {
 
-template <bool GELU>
+template <int EPI>
 __global__ void __launch_bounds__(256, 2)
 k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int nsplit,
              const uint16_t* __restrict__ B, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, float g, uint16_t* __restrict__ Y, int M, int N,
-             int K, int M_pad, int rank) {
+             int K, int M_pad, int rank, QkEpi qk) {
   constexpr int BM = 128, BN = 128;
   constexpr int TILE = 128 * 64;  // bf16 elements of one operand tile per stage
   __shared__ __attribute__((aligned(16))) uint16_t A0[TILE], A1[TILE], B0[TILE], B1[TILE];
+  __shared__ float red[EPI == kEpiQkNormRope ? 256 : 1];  // per-row sums of squares, by wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -83,7 +91,7 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -105,10 +113,10 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
   }
   sync_all();
 
-  // Epilogue: acc * g, + U @ L2t^T (U split into bf16 hi + lo), + bias, bf16 stores
-  // through a per-wave LDS tile (rows of 80 B).
+  // Epilogue: acc * g, + U @ L2t^T (U split into bf16 hi + lo), + bias, then (QKV
+  // mode) the per-head norm and rotation, and bf16 stores through a per-wave LDS tile
+  // (rows of 80 B).
   const int lr = lane & 31, lh = lane >> 5;
-  uint16_t* tile = A0 + wave * (32 * 40);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rowb = row0 + wm * 64 + 32 * i;
@@ -136,15 +144,86 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
           lo[t] = (__bf16)(uf[t] - (float)hi[t]);
         }
         const uint4 lb = *reinterpret_cast<const uint4*>(L2t + (size_t)(colb + lr) * rank + kk + 8 * lh);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(v8bf, lb), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), hi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), lo, c, 0, 0, 0);
       }
-      const float bv = bias ? bf16_to_f32(bias[colb + lr]) : 0.f;
+      if (bias) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
-        const float v = c[e] + bv;
-        tile[rin * 40 + lr] = (uint16_t)f32_to_bf16_rne(GELU ? gelu_f32(v) : v);
+        for (int q = 0; q < 4; ++q) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + colb + 8 * q + 4 * lh);
+          c[4 * q + 0] += __uint_as_float(b2.x << 16);
+          c[4 * q + 1] += __uint_as_float(b2.x & 0xFFFF0000u);
+          c[4 * q + 2] += __uint_as_float(b2.y << 16);
+          c[4 * q + 3] += __uint_as_float(b2.y & 0xFFFF0000u);
+        }
+      }
+      acc[i][j] = c;
+    }
+  }
+  if constexpr (EPI == kEpiQkNormRope) {
+    // Q and K tiles (the first two thirds of the columns) are one head each: the lane
+    // pair (l, l + 32) holds one row's 32 + 32 columns of the wave, the partner wave
+    // (wave ^ 1, same rows) the other 64.  Tile-uniform branch around the barrier.
+    const int third = N / 3;
+    if (col0 < 2 * third) {
+      const uint16_t* nw = col0 < third ? qk.norm_q : qk.norm_k;
+      float ss[2] = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss[i] = fmaf(acc[i][j][e], acc[i][j][e], ss[i]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ss[i] += __shfl_xor(ss[i], 32);
+      sync_all();  // every wave is past its LDS operand reads before red is written
+      if (lh == 0) {
+        red[wave * 64 + lr] = ss[0];
+        red[wave * 64 + 32 + lr] = ss[1];
+      }
+      sync_all();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float inv = 1.0f / sqrtf((ss[i] + red[(wave ^ 1) * 64 + 32 * i + lr]) * (1.0f / 128.0f) +
+                                       qk.eps);
+        const int row = min(row0 + wm * 64 + 32 * i + lr, M - 1);  // pad rows are not stored
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * 64 + 32 * j + 8 * q + 4 * lh;  // channel of element 4q
+            const uint2 w2 = *reinterpret_cast<const uint2*>(nw + c);
+            const float w[4] = {__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xFFFF0000u),
+                                __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xFFFF0000u)};
+            const float4 cs = *reinterpret_cast<const float4*>(qk.rope + (size_t)row * 128 + c);
+            float n[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) n[p] = acc[i][j][4 * q + p] * inv * w[p];
+            acc[i][j][4 * q + 0] = n[0] * cs.x - n[1] * cs.y;
+            acc[i][j][4 * q + 1] = n[1] * cs.x + n[0] * cs.y;
+            acc[i][j][4 * q + 2] = n[2] * cs.z - n[3] * cs.w;
+            acc[i][j][4 * q + 3] = n[3] * cs.z + n[2] * cs.w;
+          }
+      }
+    }
+  }
+  uint16_t* tile = A0 + wave * (32 * 40);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rowb = row0 + wm * 64 + 32 * i;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int colb = col0 + wn * 64 + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float v = acc[i][j][4 * q + p];
+          h[p] = f32_to_bf16_rne(EPI == kEpiGelu ? gelu_f32(v) : v);
+        }
+        *reinterpret_cast<uint2*>(tile + lr * 40 + 8 * q + 4 * lh) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -160,11 +239,17 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
 
 hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
                           const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
-                          int N, int K, int M_pad, int rank, bool gelu, hipStream_t st,
-                          hipEvent_t ev0, hipEvent_t ev1) {
+                          int N, int K, int M_pad, int rank, int epi, const QkEpi& qk,
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (M_pad % 128 != 0 || N % 128 != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  if (epi == kEpiQkNormRope && (N % 384 != 0 || !qk.norm_q || !qk.norm_k || !qk.rope))
+    return hipErrorInvalidValue;
   dim3 grid((N / 128) * (M_pad / 128));
-  hipExtLaunchKernelGGL(gelu ? k2_gemm_bf16<true> : k2_gemm_bf16<false>, grid, dim3(256), 0, st, ev0,
-                        ev1, 0, A, U, nsplit, B, L2t, bias, g, Y, M, N, K, M_pad, rank);
+  auto k = epi == kEpiQkNormRope ? k2_gemm_bf16<kEpiQkNormRope>
+           : epi == kEpiGelu     ? k2_gemm_bf16<kEpiGelu>
+                                 : k2_gemm_bf16<kEpiPlain>;
+  hipExtLaunchKernelGGL(k, grid, dim3(256), 0, st, ev0, ev1, 0, A, U, nsplit, B, L2t, bias, g, Y,
+                        M, N, K, M_pad, rank, qk);
   return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@ hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const ui
 
 hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
                           const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
-                          int N, int K, int M_pad, int rank, bool gelu, hipStream_t st,
-                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                          int N, int K, int M_pad, int rank, int epi, const QkEpi& qk,
+                          hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc, const uint8_t* Z,
                          const uint16_t* bias, uint16_t* Y, int M, int N, int K, hipStream_t st,

@@ -321,8 +321,6 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
     return fail(SVDQ_ERR_NULL, "%s: NULL norm weight or rotary table", fn);
   SVDQ_TRY(check_svdq_config(cfg));
   const bool nv = cfg->precision == SVDQ_NVFP4;
-  if (epi == svdq::kEpiQkNormRope && nv)
-    return fail(SVDQ_ERR_CONFIG, "%s: the fused QKV epilogue is built for int4 only", fn);
   if (nv) {
     SVDQ_TRY(check_global(act_global, "activation"));
     SVDQ_TRY(check_global(w->w_global, "weight"));
@@ -371,8 +369,7 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                                              svdq::k1_splits((int)w->K),
                                              reinterpret_cast<const uint16_t*>(w->qweight),
                                              w->lora_up, w->bias, g, y, (int)M, (int)w->N,
-                                             (int)w->K, (int)L.M_pad, cfg->rank,
-                                             epi == svdq::kEpiGelu, stream,
+                                             (int)w->K, (int)L.M_pad, cfg->rank, epi, qk, stream,
                                              e2.start, e2.end),
                        "gemm kernel launch"));
     return ok();
