@@ -128,7 +128,12 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N,
 svdq_status svdq_pack_lora_down(const svdq_config* cfg, int64_t K, const uint16_t* lora_down,
                                 uint16_t* packed, hipStream_t stream);
 
-/* Workspace bytes svdq_w4a4_linear needs for M tokens of K inputs. */
+/* Workspace bytes svdq_w4a4_linear needs for M tokens of K inputs.  For int4 this
+ * includes 48 MiB for the GEMM's K-split of a last, partial round of tiles: when the
+ * tile count leaves the CUs' last round part empty, those tiles are split along K,
+ * their fp32 partial tiles stored here and added up (in a fixed order) by a second,
+ * small kernel.  A workspace that stops short of that area (at least the size without
+ * it) is accepted; the GEMM then runs every tile whole. */
 size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);
 
 /* Activation side of the layer (smoothing, low-rank down projection, quantization)

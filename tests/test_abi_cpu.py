@@ -92,10 +92,14 @@ def test_alignment():
 def test_workspace_size_and_check():
     lib = L.lib()
     need = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 100, 512)
-    # M padded to 256 rows: operand 256*512*3/4, scale records 8*256*8, U 1 split x 256*32 fp32
-    assert need == 98304 + 16384 + 32768
-    assert linear(cfg(), weight(), M=100, ws_bytes=need - 1) == L.ERR_WORKSPACE
-    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 16384
+    # M padded to 256 rows: operand 256*512*3/4, scale records 8*256*8, U 1 split x 256*32
+    # fp32; then the GEMM's K-split area, 256 partial tiles of 256 x 192 fp32, which is
+    # optional (a workspace without it is accepted)
+    base = 98304 + 16384 + 32768
+    split = 256 * 256 * 192 * 4
+    assert need == base + split
+    assert linear(cfg(), weight(), M=100, ws_bytes=base - 1) == L.ERR_WORKSPACE
+    assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 16384 + split
     nv = lib.svdq_workspace_bytes(ctypes.byref(cfg(precision=L.NVFP4, group=16)), 100, 512)
     assert nv == 128 * 512 * 2 + 128 * 32 * 4   # exact bf16 operand [M_pad][K] and U
 

@@ -288,3 +288,48 @@ def test_pack_lora_down_fragment_order():
         units = packed.reshape(K // 128, rank // 16, 4, 4, 16, 8)       # kb, sl, c, q, i, 8
         expect = ld.reshape(rank // 16, 16, K // 128, 4, 4, 8)          # sl, i, kb, q, c, 8
         assert np.array_equal(units, expect.transpose(2, 0, 4, 3, 1, 5))
+
+
+@pytest.fixture(scope="module")
+def split_layer():
+    """K = 3072 (24 stages), N = 768: at M = 600 the GEMM has 12 tiles for 256 CUs, all
+    in its last partial round, so every tile is split along K (6 pieces of 4 stages)."""
+    li = I.layer_inputs(config_id=1, M=600, K=3072, N=768, outlier_count=31, factor=30.0)
+    return li, P.prepare_svdq(li.w, li.x_cal, li.bias, rank=32)
+
+
+@pytest.mark.parametrize("mode", ["plain", "gelu", "qkv"])
+def test_linear_with_tail_split(split_layer, mode):
+    """Split tiles: pieces store fp32 partials, a second kernel adds them in piece order
+    and runs the epilogue; against the oracle, and against the same call with a
+    workspace too small for the split (every tile whole, one GEMM kernel)."""
+    from oracle import attention as AT
+    li, layer = split_layer
+    dev = _layer_dev(layer)
+    x = dev_bf16(li.x)
+    M = li.x.shape[0]
+    nq, nk = I.qk_norm_weights()
+    rng = np.random.default_rng(5)
+    ang = rng.uniform(-3, 3, (M, 64))
+    rope_np = np.stack([np.cos(ang), np.sin(ang)], axis=2).astype(np.float32)
+    rope = torch.from_numpy(rope_np).cuda()
+
+    def run(ws):
+        if mode == "qkv":
+            return dev.qkv_norm_rope(x, dev_bf16(nq), dev_bf16(nk), I.QK_NORM_EPS, rope, workspace=ws)
+        return dev(x, workspace=ws, gelu=(mode == "gelu"))
+
+    full_ws = torch.empty(dev.workspace_bytes(M), dtype=torch.uint8, device="cuda")
+    split_area = 256 * 256 * 192 * 4
+    small_ws = torch.empty(dev.workspace_bytes(M) - split_area, dtype=torch.uint8, device="cuda")
+    svdq.timing_start(1)
+    y_split = host_bits(run(full_ws))
+    assert len(svdq.timing_stop()[1]) == 3      # quantizer, GEMM, tail kernel
+    svdq.timing_start(1)
+    y_whole = host_bits(run(small_ws))
+    assert len(svdq.timing_stop()[1]) == 2      # quantizer, GEMM
+    r = OL.w4a4_linear("int4", li.x, layer)["r"]
+    ref = {"plain": r, "gelu": A.gelu_f64(r),
+           "qkv": AT.qkv_norm_rope_f64(r, nq, nk, I.QK_NORM_EPS, rope_np)}[mode]
+    check_y(y_split, ref)
+    check_y(y_whole, ref)

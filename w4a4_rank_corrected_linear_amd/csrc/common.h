@@ -108,4 +108,20 @@ __host__ __device__ __forceinline__ size_t u_frag_index(int split, int row, int 
              256 + lane * 4 + (e & 3);
 }
 
+// u = h + m + l + e with h, m, l bf16 and |e| <= 2^-27 |u| (each step's remainder is
+// exact in fp32 and keeps 8 more bits): the low-rank term's fp32 U fed to bf16 MFMAs
+// as three products whose sum is U L2 to fp32 accuracy (two terms leave 2^-18 |u|,
+// which is visible next to large |U|).
+struct Bf16x3 {
+  __bf16 h, m, l;
+};
+__device__ __forceinline__ Bf16x3 split3_bf16(float u) {
+  Bf16x3 r;
+  r.h = (__bf16)u;
+  const float r1 = u - (float)r.h;
+  r.m = (__bf16)r1;
+  r.l = (__bf16)(r1 - (float)r.m);
+  return r;
+}
+
 }  // namespace svdq

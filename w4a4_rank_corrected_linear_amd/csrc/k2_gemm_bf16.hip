@@ -113,7 +113,7 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
   }
   sync_all();
 
-  // Epilogue: acc * g, + U @ L2t^T (U split into bf16 hi + lo), + bias, then (QKV
+  // Epilogue: acc * g, + U @ L2t^T (U split into three bf16 terms), + bias, then (QKV
   // mode) the per-head norm and rotation, and bf16 stores through a per-wave LDS tile
   // (rows of 80 B).
   const int lr = lane & 31, lh = lane >> 5;
@@ -137,14 +137,17 @@ k2_gemm_bf16(const uint16_t* __restrict__ A, const float* __restrict__ U, int ns
           uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w;
           uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z; uf[7] += u1.w;
         }
-        v8bf hi, lo;
+        v8bf hi, mid, lo;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          hi[t] = (__bf16)uf[t];
-          lo[t] = (__bf16)(uf[t] - (float)hi[t]);
+          const Bf16x3 s3 = split3_bf16(uf[t]);
+          hi[t] = s3.h;
+          mid[t] = s3.m;
+          lo[t] = s3.l;
         }
         const uint4 lb = *reinterpret_cast<const uint4*>(L2t + (size_t)(colb + lr) * rank + kk + 8 * lh);
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), hi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), mid, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), lo, c, 0, 0, 0);
       }
       if (bias) {

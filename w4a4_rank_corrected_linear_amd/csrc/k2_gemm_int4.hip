@@ -16,7 +16,7 @@
 //                                                    < 32) and k = 4 or 5 (lanes >= 32),
 //                                                    the exact product 2 sw[n] sx[m]
 //   acc = fma(S, D, acc)                             one VALU op per element and group
-// The low-rank term U L2t^T (U split into bf16 hi + lo, four bf16 MFMAs per 16 ranks)
+// The low-rank term U L2t^T (U split into three bf16 terms, split3_bf16 in common.h)
 // either seeds the accumulator before the main loop (all of its global loads issued
 // before the first is used) or, when K has at most two k-splits, is added in the
 // epilogue from copies of U and lora_up that the last two stages DMA into the ring
@@ -51,6 +51,8 @@
 // The tile order is XCD-aware: workgroup i runs on XCD i % 8, and the eight XCDs
 // take disjoint (tiles_m/4) x (tiles_n/2) sub-grids, so each XCD's L2 holds a quarter
 // of the activation rows and half of the weight columns.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -83,6 +85,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
 }
 
+// Tile (tm, tn) of tile id t: XCD-aware when the grid allows (t % 8 is the XCD that
+// workgroup t runs on; XCD x takes a (tiles_m / 4) x (tiles_n / 2) sub-grid), else
+// row-major.
+// Partial tile of tail tile t, piece p in the split area.
+__device__ __forceinline__ float* part_tile(float* part, int t, int p, int ks, int tile_floats) {
+  return part + (size_t)(t * ks + p) * tile_floats;
+}
+
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
+    const int x = t & 7, loc = t >> 3;
+    const int sm = tiles_m >> 2, sn = tiles_n >> 1;
+    tm = (x >> 1) * sm + loc / sn;
+    tn = (x & 1) * sn + loc % sn;
+  } else {
+    tn = t % tiles_n;
+    tm = t / tiles_n;
+  }
+}
+
 }  // namespace
 
 template <int BN, int EPI>
@@ -91,7 +113,8 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
              const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
              const uint2* __restrict__ sB, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-             int M, int N, int K, int M_pad, int rank, QkEpi qk) {
+             int M, int N, int K, int M_pad, int rank, QkEpi qk, int full_tiles, int ks,
+             float* __restrict__ part) {
   constexpr int BM = 256;
   constexpr int WN = BN / 64;              // 32-column blocks per wave
   constexpr int CB = BN / 32;              // 32-column blocks per tile
@@ -112,20 +135,24 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = N / BN, tiles_m = M_pad / BM;
-  int tm, tn;
-  if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
-    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
-    const int sm = tiles_m >> 2, sn = tiles_n >> 1;
-    tm = (x >> 1) * sm + loc / sn;
-    tn = (x & 1) * sn + loc % sn;
-  } else {
-    tn = blockIdx.x % tiles_n;
-    tm = blockIdx.x / tiles_n;
+  // Workgroups below full_tiles own tile blockIdx.x and all of K.  The tiles of the
+  // last, partial round (ids full_tiles and up) are split along K into ks pieces of
+  // consecutive stages, one workgroup each (piece >= 0), which store their fp32
+  // partial tiles for the tail kernel below to add up and finish.
+  int tile_id = blockIdx.x, piece = -1;
+  if ((int)blockIdx.x >= full_tiles) {
+    const int q = (int)blockIdx.x - full_tiles;
+    tile_id = full_tiles + q / ks;
+    piece = q % ks;
   }
+  int tm, tn;
+  tile_coords(tile_id, tiles_m, tiles_n, tm, tn);
   const int col0 = tn * BN, row0 = tm * BM;
   const int rb0 = row0 >> 5, cb0 = col0 >> 5;
   const int G = K >> 6;
-  const int S = G >> 1;
+  const int S_all = G >> 1;
+  const int sbase = piece < 0 ? 0 : piece * S_all / ks;                 // first stage
+  const int S = piece < 0 ? S_all : (piece + 1) * S_all / ks - sbase;   // stages here
 
   auto slotA = [&](int sl) { return ring + sl * SLOT; };
   auto slotB = [&](int sl) { return ring + sl * SLOT + ASZ; };
@@ -139,13 +166,13 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   const uint32_t voff = lane * 16;
   auto dma = [&](int s, int sl) {
     {
-      const uint8_t* src = A + ((size_t)(rb0 + wave) * G + 2 * s) * 1536;
+      const uint8_t* src = A + ((size_t)(rb0 + wave) * G + 2 * (sbase + s)) * 1536;
       const uint32_t dst = lds_addr(slotA(sl) + wave * 768);
 #pragma unroll
       for (int t = 0; t < 3; ++t) dma16(voff, src + t * 1024, dst + t * 1024);
     }
     if (wave < CB) {
-      const uint8_t* src = B + ((size_t)(cb0 + wave) * G + 2 * s) * 1536;
+      const uint8_t* src = B + ((size_t)(cb0 + wave) * G + 2 * (sbase + s)) * 1536;
       const uint32_t dst = lds_addr(slotB(sl) + wave * 768);
 #pragma unroll
       for (int t = 0; t < 3; ++t) dma16(voff, src + t * 1024, dst + t * 1024);
@@ -153,11 +180,11 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int gl = t >> 1, part = t & 1;
-        dma16(voff, sA + (size_t)(2 * s + gl) * M_pad + row0 + 128 * part,
+        dma16(voff, sA + (size_t)(2 * (sbase + s) + gl) * M_pad + row0 + 128 * part,
               lds_addr(slotSA(sl) + gl * BM + 128 * part));
       }
     } else if (wave == CB + 1) {
-      const uint2* src = sB + (size_t)s * N + col0;
+      const uint2* src = sB + (size_t)(sbase + s) * N + col0;
       const uint32_t dst = lds_addr(slotSB(sl));
       dma16(voff, src, dst);
       if (BN > 128 && lane < (BN - 128) / 2) dma16(voff, src + 128, dst + 1024);
@@ -191,13 +218,14 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // Low-rank term acc^T += L2t U^T.  U (fp32, the sum of the quantizer's k-split
-  // partials in split order) is split into bf16 hi + lo; u - hi is exact in fp32 and
-  // what lo drops is below 2^-17 |u|.  rank <= 32: at most two 16-rank slices.  With at
+  // partials in split order) is split into three bf16 terms (split3_bf16), which
+  // leave less than 2^-27 |u|.  rank <= 32: at most two 16-rank slices.  With at
   // most two k-splits and three stages or more, U and lora_up are copied into the ring
   // slots that the last two stages leave free and the term is added in the epilogue;
   // otherwise it seeds the accumulator here, from global memory.
-  const bool late_seed = rank > 0 && nsplit <= 2 && S >= 3;
-  if (rank > 0 && !late_seed) {
+  // (A split tile takes the term in piece 0, before its loop.)
+  const bool late_seed = rank > 0 && nsplit <= 2 && S >= 3 && piece < 0;
+  if (rank > 0 && !late_seed && piece <= 0) {
     uint4 lbv[2][WN];
     float uf[2][2][8];
 #pragma unroll
@@ -245,13 +273,15 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if (16 * kk < rank) {
-        v8bf uh[2], ul[2];
+        v8bf uh[2], um[2], ul[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            uh[i][q] = (__bf16)uf[kk][i][q];
-            ul[i][q] = (__bf16)(uf[kk][i][q] - (float)uh[i][q]);
+            const Bf16x3 t = split3_bf16(uf[kk][i][q]);
+            uh[i][q] = t.h;
+            um[i][q] = t.m;
+            ul[i][q] = t.l;
           }
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
@@ -259,6 +289,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, uh[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, um[i], acc[i][j], 0, 0, 0);
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, ul[i], acc[i][j], 0, 0, 0);
           }
         }
@@ -395,6 +426,25 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
       for (int j = 0; j < WN; ++j) asm volatile("" : "+v"(acc[i][j]));
   }
 
+  if (piece >= 0) {
+    // Partial tile of this piece: block (wave, i, j) is 4 KiB, float4 q of lane l at
+    // 16 (64 q + l) bytes, so each store instruction of a wave writes 1 KiB in a row.
+    // The bias copy of the last stage lands before the wave exits.
+    wait_vm0();
+    float* dst = part_tile(part, tile_id - full_tiles, piece, ks, BM * BN);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        float4* d4 = reinterpret_cast<float4*>(dst + ((wave * 2 + i) * WN + j) * 1024) + lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          d4[64 * q] = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                   acc[i][j][4 * q + 3]);
+      }
+    return;
+  }
+
   // Epilogue: + bias, round to bf16.  Each wave stages its 64 x BN/2 tile in LDS (the
   // ring is free once every wave has passed the barrier) and writes Y in 16-byte
   // pieces, BN/16 consecutive lanes per row, so every row segment of the tile is one
@@ -433,7 +483,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if (16 * kk < rank) {
-        v8bf uh[2], ul[2];
+        v8bf uh[2], um[2], ul[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const uint32_t o = ((wm * 2 + i) * (rank >> 4) + kk) * 2048 + lane * 16;
@@ -445,8 +495,10 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
           const float uf[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            uh[i][q] = (__bf16)uf[q];
-            ul[i][q] = (__bf16)(uf[q] - (float)uh[i][q]);
+            const Bf16x3 t = split3_bf16(uf[q]);
+            uh[i][q] = t.h;
+            um[i][q] = t.m;
+            ul[i][q] = t.l;
           }
         }
         v8bf lv[WN];
@@ -455,13 +507,18 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
           const uint32_t lo = s0 + rank * 1024 + ((wn * WN + j) * 32 + lr) * rank * 2 + kk * 32 + lh * 16;
           lv[j] = __builtin_bit_cast(v8bf, *(lds_v4i*)(uintptr_t)lo);
         }
-        // the hi products of all blocks, then the lo ones: an accumulator's two MFMAs
-        // are 2 WN apart instead of back to back
+        // the hi products of all blocks, then the mid and lo ones: an accumulator's
+        // MFMAs are 2 WN apart instead of back to back
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < WN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv[j], uh[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv[j], um[i], acc[i][j], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -588,38 +645,177 @@ int cu_count() {
   return cached[dev];
 }
 
-// Fraction of the workgroup slots the tiles fill over their waves (one workgroup per CU).
-double fill(int64_t tiles, int cus) {
-  const int64_t waves = (tiles + cus - 1) / cus;
-  return (double)tiles / (double)(waves * cus);
-}
-
 }  // namespace
 
-// Tile width: 192 when N allows, unless 128-wide tiles fill the CUs' waves clearly better
-// (a 128-wide tile costs about 0.7 of a 192-wide one, so it must win by more than 10 %).
-// At M = 4608, N = 3072 the 192-wide grid is 288 tiles on 256 CUs: the second wave is
-// nearly empty, and 128-wide tiles (432) are about 20 % faster.
-hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
-                          const uint8_t* B, const uint2* sB, const uint16_t* L2t,
-                          const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, int epi, const QkEpi& qk, hipStream_t st, hipEvent_t ev0,
-                          hipEvent_t ev1) {
-  if (M_pad % 256 != 0 || N % 128 != 0 || K % 128 != 0) return hipErrorInvalidValue;
-  if (epi == kEpiQkNormRope && (N % 384 != 0 || !qk.norm_q || !qk.norm_k || !qk.rope))
-    return hipErrorInvalidValue;
-  bool wide = N % 192 == 0 && epi != kEpiQkNormRope;
-  if (wide) {
-    const int cus = cu_count();
-    const int64_t t192 = (int64_t)(N / 192) * (M_pad / 256), t128 = (int64_t)(N / 128) * (M_pad / 256);
-    if (fill(t128, cus) > 1.1 * fill(t192, cus)) wide = false;
+// Plan by a cost model in units of one 192-wide stage (about 1.3 us on MI355X): a
+// tile costs S u + 4 (u = 1 for 192-wide tiles, 0.76 for 128-wide; 4 for the fill,
+// drain and epilogue), a round of tiles costs one tile, and a split tail costs one
+// piece plus 8 (its partial stores, the second kernel and its launch).  Pieces have at
+// least 4 stages; the split is taken when it is 3 % cheaper than the best whole-tile
+// plan.  The constants are fitted to the DiT shapes at 4096 and 4608 tokens.
+K2Plan plan_k2_int4(int M_pad, int N, int K, int epi, int max_pieces) {
+  const int cus = cu_count();
+  const int S = K / 128;
+  K2Plan best, best_split;
+  double best_whole = 1e30;
+  double split_cost = 1e30;
+  for (int bn : {192, 128}) {
+    if (N % bn != 0 || (bn == 192 && epi == kEpiQkNormRope)) continue;
+    const double u = bn == 192 ? 1.0 : 0.76;
+    const double tile = S * u + 4.0;
+    const int tiles = (N / bn) * (M_pad / 256);
+    const double whole = (double)((tiles + cus - 1) / cus) * tile;
+    if (whole < best_whole) {
+      best_whole = whole;
+      best.bn = bn;
+      best.tiles = best.full = tiles;
+      best.ks = 1;
+    }
+    const int rem = tiles % cus;
+    if (max_pieces > 0 && rem > 0) {
+      const int ks = std::min({cus / rem, S / 4, max_pieces / rem, 16});
+      if (ks >= 2) {
+        const double c = (double)(tiles / cus) * tile + (double)S / ks * u + 4.0 + 8.0;
+        if (c < split_cost) {
+          split_cost = c;
+          best_split.bn = bn;
+          best_split.tiles = tiles;
+          best_split.full = tiles - rem;
+          best_split.ks = ks;
+        }
+      }
+    }
   }
-  const unsigned g = (unsigned)((N / (wide ? 192 : 128)) * (M_pad / 256));
+  return split_cost < 0.97 * best_whole ? best_split : best;
+}
+
+// Finishes the split tiles: workgroup (tail tile t, row block rb = 32 rows) adds the
+// ks partial tiles in piece order, then runs the epilogue (bias, GELU or the Q/K norm
+// and rotation) and stores the 32 rows.  Phase 1 reads the partials in their stored
+// order (a wave's float4 loads are 1 KiB in a row) and puts the sums into an LDS tile
+// of 32 rows x BN; phase 2 gives each row to 8 consecutive threads.
+template <int BN, int EPI>
+__global__ void __launch_bounds__(256)
+k2_tail_int4(const float* __restrict__ part, int ks, int full_tiles, int tiles_m, int tiles_n,
+             const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N,
+             QkEpi qk) {
+  constexpr int BM = 256, WN = BN / 64, C4 = BN / 4, LD = BN + 4;
+  __shared__ __attribute__((aligned(16))) float T[32 * LD];
+  const int t = blockIdx.x >> 3, rb = blockIdx.x & 7;  // rb = 2 wm + i of the GEMM
+  const int wm = rb >> 1, i = rb & 1;
+  const int tid = threadIdx.x;
+  int tm, tn;
+  tile_coords(full_tiles + t, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * BM + 32 * rb, col0 = tn * BN;
+  {
+    // thread (q, lane) of every block (wn, j) of this row block: row lane % 32,
+    // columns 32 (wn WN + j) + 8 q + 4 (lane / 32) + [0, 4)
+    const int q = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int wn = 0; wn < 2; ++wn)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const size_t off = (size_t)(((wm * 2 + wn) * 2 + i) * WN + j) * 1024 + (64 * q + lane) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+        for (int p = 0; p < ks; ++p) {
+          const float4 x = *reinterpret_cast<const float4*>(part + (size_t)(t * ks + p) * (BM * BN) + off);
+          v.x += x.x;
+          v.y += x.y;
+          v.z += x.z;
+          v.w += x.w;
+        }
+        *reinterpret_cast<float4*>(&T[(lane & 31) * LD + 32 * (wn * WN + j) + 8 * q + 4 * (lane >> 5)]) = v;
+      }
+  }
+  __syncthreads();
+  // row r = tid / 8 of the block; float4 columns sub + 8 k
+  const int r = tid >> 3, sub = tid & 7;
+  const int row = row0 + r;
+  constexpr int NK = C4 / 8;
+  float v[NK][4];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int c = 4 * (sub + 8 * k);
+    const float4 x = *reinterpret_cast<const float4*>(&T[r * LD + c]);
+    v[k][0] = x.x;
+    v[k][1] = x.y;
+    v[k][2] = x.z;
+    v[k][3] = x.w;
+    if (bias) {
+      const uint2 b2 = *reinterpret_cast<const uint2*>(bias + col0 + c);
+      v[k][0] += __uint_as_float(b2.x << 16);
+      v[k][1] += __uint_as_float(b2.x & 0xFFFF0000u);
+      v[k][2] += __uint_as_float(b2.y << 16);
+      v[k][3] += __uint_as_float(b2.y & 0xFFFF0000u);
+    }
+  }
+  if constexpr (EPI == kEpiQkNormRope) {
+    if (col0 < 2 * (N / 3)) {  // a Q or K head (workgroup-uniform); BN = 128
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(v[k][e], v[k][e], ss);
+#pragma unroll
+      for (int d = 1; d < 8; d <<= 1) ss += __shfl_xor(ss, d, 8);
+      const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + qk.eps);
+      const uint16_t* nw = col0 < N / 3 ? qk.norm_q : qk.norm_k;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int c = 4 * (sub + 8 * k);
+        const uint2 w2 = *reinterpret_cast<const uint2*>(nw + c);
+        const float w[4] = {__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xFFFF0000u),
+                            __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xFFFF0000u)};
+        const float4 cs = *reinterpret_cast<const float4*>(qk.rope + (size_t)min(row, M - 1) * 128 + c);
+        float n[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) n[e] = v[k][e] * inv * w[e];
+        v[k][0] = n[0] * cs.x - n[1] * cs.y;
+        v[k][1] = n[1] * cs.x + n[0] * cs.y;
+        v[k][2] = n[2] * cs.z - n[3] * cs.w;
+        v[k][3] = n[3] * cs.z + n[2] * cs.w;
+      }
+    }
+  }
+  if (row < M) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(EPI == kEpiGelu ? gelu_f32(v[k][e]) : v[k][e]);
+      *reinterpret_cast<uint2*>(Y + (size_t)row * N + col0 + 4 * (sub + 8 * k)) =
+          make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  }
+}
+
+hipError_t launch_k2_int4(const K2Plan& plan, const uint8_t* A, const uint2* sA, const float* U,
+                          int nsplit, const uint8_t* B, const uint2* sB, const uint16_t* L2t,
+                          const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
+                          int rank, int epi, const QkEpi& qk, float* part, hipStream_t st,
+                          hipEvent_t ev0, hipEvent_t ev1, hipEvent_t ev2, hipEvent_t ev3) {
+  if (M_pad % 256 != 0 || N % 128 != 0 || K % 128 != 0 || N % plan.bn != 0) return hipErrorInvalidValue;
+  if (epi == kEpiQkNormRope && (N % 384 != 0 || plan.bn != 128 || !qk.norm_q || !qk.norm_k || !qk.rope))
+    return hipErrorInvalidValue;
+  const bool split = plan.ks > 1;
+  if (split && (!part || (int64_t)(plan.tiles - plan.full) * plan.ks > kSplitMaxPieces))
+    return hipErrorInvalidValue;
+  const bool wide = plan.bn == 192;
+  const unsigned g = (unsigned)(plan.full + (plan.tiles - plan.full) * plan.ks);
   auto k = epi == kEpiQkNormRope ? k2_gemm_int4<128, kEpiQkNormRope>
            : wide ? (epi == kEpiGelu ? k2_gemm_int4<192, kEpiGelu> : k2_gemm_int4<192, kEpiPlain>)
                   : (epi == kEpiGelu ? k2_gemm_int4<128, kEpiGelu> : k2_gemm_int4<128, kEpiPlain>);
   hipExtLaunchKernelGGL(k, dim3(g), dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB, L2t,
-                        bias, Y, M, N, K, M_pad, rank, qk);
+                        bias, Y, M, N, K, M_pad, rank, qk, plan.full, plan.ks, part);
+  if (split) {
+    const unsigned gt = (unsigned)((plan.tiles - plan.full) * 8);
+    auto kt = epi == kEpiQkNormRope ? k2_tail_int4<128, kEpiQkNormRope>
+              : wide ? (epi == kEpiGelu ? k2_tail_int4<192, kEpiGelu> : k2_tail_int4<192, kEpiPlain>)
+                     : (epi == kEpiGelu ? k2_tail_int4<128, kEpiGelu> : k2_tail_int4<128, kEpiPlain>);
+    hipExtLaunchKernelGGL(kt, dim3(gt), dim3(256), 0, st, ev2, ev3, 0, part, plan.ks, plan.full,
+                          M_pad / 256, N / plan.bn, bias, Y, M, N, qk);
+  }
   return hipGetLastError();
 }
 

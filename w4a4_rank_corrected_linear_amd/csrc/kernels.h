@@ -34,11 +34,26 @@ struct QkEpi {
   float eps;
 };
 
-hipError_t launch_k2_int4(const uint8_t* A, const uint2* sA, const float* U, int nsplit,
-                          const uint8_t* B, const uint2* sB, const uint16_t* L2t,
+// Launch plan of the int4 GEMM: tile width, tile count, and the K-split of the tiles
+// of a last, partial round on the CUs (tiles [full, tiles) split into ks pieces each,
+// whose fp32 partial tiles a second, small kernel adds up and finishes).  max_pieces
+// is the number of 256 x 192 fp32 partial tiles the caller has room for (0: no split).
+struct K2Plan {
+  int bn = 192;
+  int tiles = 0, full = 0, ks = 1;
+  int kernels() const { return ks > 1 ? 2 : 1; }
+};
+K2Plan plan_k2_int4(int M_pad, int N, int K, int epi, int max_pieces);
+constexpr int kSplitMaxPieces = 256;
+constexpr size_t kSplitTileBytes = (size_t)256 * 192 * 4;
+
+// ev0/ev1 time the GEMM, ev2/ev3 the tail kernel (when the plan splits).
+hipError_t launch_k2_int4(const K2Plan& plan, const uint8_t* A, const uint2* sA, const float* U,
+                          int nsplit, const uint8_t* B, const uint2* sB, const uint16_t* L2t,
                           const uint16_t* bias, uint16_t* Y, int M, int N, int K, int M_pad,
-                          int rank, int epi, const QkEpi& qk, hipStream_t st,
-                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                          int rank, int epi, const QkEpi& qk, float* part, hipStream_t st,
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
+                          hipEvent_t ev2 = nullptr, hipEvent_t ev3 = nullptr);
 
 hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,

@@ -115,7 +115,7 @@ svdq_status check_global(float g, const char* what) {
 
 struct WsLayout {
   int64_t M_pad = 0;
-  size_t codes = 0, scales = 0, lora = 0, total = 0;
+  size_t codes = 0, scales = 0, lora = 0, split = 0, total = 0;
 };
 
 WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
@@ -135,6 +135,12 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   L.scales = (size_t)round_up((int64_t)codes, 256);
   L.lora = L.scales + (size_t)round_up((int64_t)scales, 256);
   L.total = L.lora + (size_t)round_up((int64_t)lora, 256);
+  if (!nv) {
+    // int4: fp32 partial tiles of the GEMM's K-split of its last, partial round of
+    // tiles; a workspace that stops short of this area runs without the split
+    L.split = L.total;
+    L.total = L.split + svdq::kSplitMaxPieces * svdq::kSplitTileBytes;
+  }
   return L;
 }
 
@@ -345,9 +351,11 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
       (cfg->rank > 0 && (!aligned16(w->lora_down) || !aligned16(w->lora_up))))
     return fail(SVDQ_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   const WsLayout L = ws_layout(cfg, M, w->K);
-  if (workspace_bytes < L.total)
+  const size_t need = L.split ? L.split : L.total;  // the split area is optional
+  if (workspace_bytes < need)
     return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                workspace_bytes, L.total);
+                workspace_bytes, need);
+  const bool split_room = L.split && workspace_bytes >= L.total;
   if (M == 0) return ok();
   SVDQ_TRY(check_current_device());
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -379,12 +387,18 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                                            a_scales, cfg->rank ? a_lora : nullptr, (int)L.M_pad,
                                            stream, e1.start, e1.end),
                      "quantize kernel launch"));
+  const svdq::K2Plan plan = svdq::plan_k2_int4((int)L.M_pad, (int)w->N, (int)w->K, epi,
+                                               split_room ? svdq::kSplitMaxPieces : 0);
   const EvPair e2 = timer_kernel();
-  SVDQ_TRY(hip_check(svdq::launch_k2_int4(a_codes, a_scales, a_lora, svdq::k1_splits((int)w->K),
-                                           w->qweight,
+  const EvPair e3 = plan.kernels() > 1 ? timer_kernel() : EvPair{};
+  SVDQ_TRY(hip_check(svdq::launch_k2_int4(plan, a_codes, a_scales, a_lora,
+                                           svdq::k1_splits((int)w->K), w->qweight,
                                            static_cast<const uint2*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
-                                           cfg->rank, epi, qk, stream, e2.start, e2.end),
+                                           cfg->rank, epi, qk,
+                                           split_room ? reinterpret_cast<float*>(ws + L.split)
+                                                      : nullptr,
+                                           stream, e2.start, e2.end, e3.start, e3.end),
                      "gemm kernel launch"));
   return ok();
 }
