@@ -7,8 +7,9 @@
 // clamped to [-7, 7], U = xhat @ lora_down^T (fp32 accumulation, not rounded).
 //
 // Two kernels share the quantizer below:
-//  * k1_int4_fused (the layer's own path) uses the row-pair skeleton of k1_rows32.h
-//    and writes the GEMM operand layout, scales [K/64][M_pad] (8-byte records by
+//  * k1_int4_fused / k1_int4_fused16 (the layer's own path) use the row-pair skeleton
+//    of k1_rows32.h or the 16-row batch skeleton of k1_batch.h and write the GEMM
+//    operand layout, scales [K/64][M_pad] (8-byte records by
 //    group parity, see common.h) and partial U per k-split in the fragment layout;
 //  * k1_int4_interchange (svdq_quantize_act) streams whole rows with register
 //    prefetch and writes codes [M][K/2], scales [M][K/64] and U [M][r].
@@ -98,7 +99,12 @@ struct QuantInt4Fused {
   }
 };
 
+// Two skeletons of the same computation (identical codes and scales; U summed over the
+// waves in a different order): 32 rows and twelve waves per workgroup, one workgroup
+// per CU, when all workgroups fit in one round on the CUs; else 16 rows and four waves,
+// two workgroups per CU, whose smaller workgroups leave a finer last round.
 __global__ void __launch_bounds__(768, 1) k1_int4_fused(K1Args a) { k1_rows32<QuantInt4Fused>(a); }
+__global__ void __launch_bounds__(256, 2) k1_int4_fused16(K1Args a) { k1_batch<QuantInt4Fused>(a); }
 
 // Interchange kernel: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide
 // k-blocks kb = w, w+8, ... and prefetches the next block's X, smoothing and
@@ -243,8 +249,14 @@ hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uin
                           hipEvent_t ev1) {
   if (fused) {
     K1Args a{x, M, K, smooth, ldown, rank, codes, scales, uact, M_pad, 1.0f};
-    dim3 grid(M_pad / 32, k1_splits(K));
-    hipExtLaunchKernelGGL(k1_int4_fused, grid, dim3(64 * kK1RowsWaves), 0, st, ev0, ev1, 0, a);
+    const int splits = k1_splits(K);
+    if ((int64_t)(M_pad / 32) * splits <= device_cu_count()) {
+      hipExtLaunchKernelGGL(k1_int4_fused, dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0, st,
+                            ev0, ev1, 0, a);
+    } else {
+      hipExtLaunchKernelGGL(k1_int4_fused16, dim3(M_pad / 16, splits), dim3(256), 0, st, ev0, ev1, 0,
+                            a);
+    }
   } else {
     dim3 grid((M + 15) / 16);
     hipExtLaunchKernelGGL(k1_int4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,

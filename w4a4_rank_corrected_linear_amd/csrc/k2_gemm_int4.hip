@@ -630,9 +630,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   }
 }
 
-namespace {
-
-int cu_count() {
+int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -645,8 +643,6 @@ int cu_count() {
   return cached[dev];
 }
 
-}  // namespace
-
 // Plan by a cost model in units of one 192-wide stage (about 1.3 us on MI355X): a
 // tile costs S u + 4 (u = 1 for 192-wide tiles, 0.76 for 128-wide; 4 for the fill,
 // drain and epilogue), a round of tiles costs one tile, and a split tail costs one
@@ -654,7 +650,7 @@ int cu_count() {
 // least 4 stages; the split is taken when it is 3 % cheaper than the best whole-tile
 // plan.  The constants are fitted to the DiT shapes at 4096 and 4608 tokens.
 K2Plan plan_k2_int4(int M_pad, int N, int K, int epi, int max_pieces) {
-  const int cus = cu_count();
+  const int cus = device_cu_count();
   const int S = K / 128;
   K2Plan best, best_split;
   double best_whole = 1e30;

@@ -34,6 +34,9 @@ struct QkEpi {
   float eps;
 };
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
 // Launch plan of the int4 GEMM: tile width, tile count, and the K-split of the tiles
 // of a last, partial round on the CUs (tiles [full, tiles) split into ks pieces each,
 // whose fp32 partial tiles a second, small kernel adds up and finishes).  max_pieces
