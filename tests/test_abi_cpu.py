@@ -101,7 +101,7 @@ def test_workspace_size_and_check():
     assert linear(cfg(), weight(), M=100, ws_bytes=base - 1) == L.ERR_WORKSPACE
     assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 16384 + split
     nv = lib.svdq_workspace_bytes(ctypes.byref(cfg(precision=L.NVFP4, group=16)), 100, 512)
-    assert nv == 128 * 512 * 2 + 128 * 32 * 4   # exact bf16 operand [M_pad][K] and U
+    assert nv == 256 * 512 * 2 + 256 * 32 * 4   # exact bf16 operand [M_pad][K] and U
 
 
 def test_packed_weight_bytes():
@@ -150,8 +150,9 @@ def test_timing_start_without_device_is_a_clear_error():
 def test_nvfp4_sizes_and_global_scale_check():
     lib = L.lib()
     c = cfg(precision=L.NVFP4, group=16)
-    # bf16 operand 128 x 512 x 2, no scales, U 128 x 32 x 4
-    assert lib.svdq_workspace_bytes(ctypes.byref(c), 100, 512) == 131072 + 16384
+    # rows padded to the GEMM's 256-row tile: bf16 operand 256 x 512 x 2, no scales,
+    # U 256 x 32 x 4
+    assert lib.svdq_workspace_bytes(ctypes.byref(c), 100, 512) == 262144 + 32768
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     tot = lib.svdq_packed_weight_bytes(ctypes.byref(c), 512, 256, ctypes.byref(cb), ctypes.byref(sb))
     assert (cb.value, sb.value, tot) == (256 * 512 * 2, 256, 256 * 512 * 2 + 256)

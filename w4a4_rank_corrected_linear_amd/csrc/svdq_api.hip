@@ -121,8 +121,8 @@ struct WsLayout {
 WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   WsLayout L;
   const bool nv = c->precision == SVDQ_NVFP4;
-  // row padding to the GEMM's row tile: 256 (int4), 128 (nvfp4)
-  L.M_pad = round_up(M, nv ? 128 : 256);
+  // row padding to the GEMMs' row tile (256)
+  L.M_pad = round_up(M, 256);
   const int64_t G = K / c->group_size;
   // int4: GEMM A operand as E2M3 lane slots, 6 bits per value (3/4 byte), scale
   // records [G][M_pad] (8 bytes); nvfp4: the exact dequantized operand in bf16
