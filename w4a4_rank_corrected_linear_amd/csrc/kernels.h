@@ -2,8 +2,8 @@
 // enqueues on `st` and returns hipGetLastError() of its launches.  Shapes were
 // validated by the C ABI before any of these is called.  `ev0` / `ev1` (may be
 // null) are HIP events that receive the kernel's start and end timestamps
-// (hipExtLaunchKernelGGL), used by the per-kernel timing hook.  `gelu` selects the GEMM
-// epilogue that applies the exact GELU to the fp32 result before the bf16 rounding.
+// (hipExtLaunchKernelGGL), used by the per-kernel timing hook.  `epi` selects the GEMM
+// epilogue (Epilogue below).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
