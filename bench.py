@@ -102,6 +102,15 @@ def make_inputs(workload: str):
                 seeds=dict(x=sd.x, w=sd.w, bias=sd.bias, outliers=sd.outliers))
 
 
+def _threads() -> int:
+    """BLAS threads the oracle runs with (the CPU baseline's core count)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return int(os.cpu_count() or 1)
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 8):
     """The oracle on the same inputs, timed on the host (test infrastructure)."""
     from oracle import linear as OL
@@ -126,12 +135,7 @@ def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 8):
         run()
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    return {"value": round(2.0 * M * N * K / t / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+    return {"value": round(2.0 * M * N * K / t / 1e12, 6), "unit": "TOPS", "cores": _threads(),
             "kind": "oracle",
             "sample": f"full {M}x{K}x{N} call on the same inputs, {len(times)} runs, median "
                       f"{t:.3f} s (float64 numpy/BLAS)"}
@@ -295,6 +299,93 @@ def run_chain(args) -> int:
     return 0
 
 
+def run_prep(args) -> int:
+    """Offline int4 weight preparation on the GPU (svdq_prepare_int4) of the attention
+    projection's weight (K = N = 3072, rank 32, 16 oversampling columns, 8 power
+    iterations, 4096 calibration rows), timed per call; with the CPU baseline, the
+    oracle's preparation (exact float64 SVD) on the same inputs, and the ratio of the
+    two residual norms."""
+    import ctypes
+    import numpy as np
+    import torch
+    import w4a4_rank_corrected_linear_amd as svdq
+    from synth import inputs as I
+
+    K = N = 3072
+    rank, over, iters = 32, 16, 8
+    li = I.layer_inputs(config_id=2, M=16, K=K, N=N, cal_rows=4096)
+    dev = torch.device("cuda:0")
+    L = svdq.lib()
+    w = torch.from_numpy(np.ascontiguousarray(li.w, np.float32)).to(dev)
+    xc = torch.from_numpy(li.x_cal.view(np.int16)).view(torch.bfloat16).to(dev)
+    om = torch.from_numpy(I.gaussian_test_matrix(N, rank + over, 7)).to(dev)
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev)
+    sm = torch.empty((K,), dtype=torch.bfloat16, device=dev)
+    ld = torch.empty((rank, K), dtype=torch.bfloat16, device=dev)
+    lu = torch.empty((N, rank), dtype=torch.bfloat16, device=dev)
+    res = torch.empty((K, N), dtype=torch.float32, device=dev)
+    nbytes = L.svdq_prepare_workspace_bytes(K, N, rank, over)
+    work = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call():
+        svdq._lib.check(L.svdq_prepare_int4(K, N, rank, w.data_ptr(), xc.data_ptr(), 4096,
+                                            om.data_ptr(), over, iters, qw.data_ptr(),
+                                            sc.data_ptr(), sm.data_ptr(), ld.data_ptr(),
+                                            lu.data_ptr(), res.data_ptr(), work.data_ptr(), nbytes,
+                                            stream), "svdq_prepare_int4")
+
+    steps, warmup = min(args.steps, 20), min(args.warmup, 3)
+    print(f"[bench] workload prep: K=N={K}, rank {rank}, oversample {over}, {iters} power "
+          f"iterations; warmup {warmup}, steps {steps}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ell = rank + over
+    # float64 work of the factorization: 2 K N l per product with What, (2 iters + 2) of them
+    flops = 2.0 * K * N * ell * (2 * iters + 2)
+    out = {
+        "metric": f"GPU int4 weight preparation (smoothing, rank-{rank} factorization, residual "
+                  f"quantization) time at K=N={K}",
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"prep: W [{K}, {N}] ~ N(0, 0.02), X_cal [4096, {K}] with 1 % "
+                               f"outlier channels x30, rank {rank}, l = {ell}, {iters} power "
+                               "iterations", "K": K, "N": N, "rank": rank, "oversample": over,
+                   "power_iters": iters},
+        "factorization_f64_GFLOPs": round(flops / (ms * 1e-3) / 1e9, 1),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import prep as P
+        t0 = time.perf_counter()
+        ref = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=rank)
+        cpu_s = time.perf_counter() - t0
+        ratio = float(np.linalg.norm(res.cpu().numpy()) / np.linalg.norm(ref.residual))
+        out["residual_norm_ratio_vs_exact_svd"] = round(ratio, 6)
+        out["cpu_baseline"] = {"value": round(cpu_s * 1e3, 1), "unit": "ms", "cores": _threads(),
+                               "kind": "oracle",
+                               "sample": "one oracle preparation (float64 numpy SVD) of the same "
+                                         "weight"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 PROFILE_CMDS = {
     "stats": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_stats "
              "-o run --output-format csv -- python3 <repo>/bench.py --no-cpu-baseline",
@@ -383,7 +474,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS) + ["chain"])
+    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS) + ["chain", "prep"])
     ap.add_argument("--batch", type=int, default=1, choices=[1, 4],
                     help="chain workload: images per step (M = 4608 per image)")
     ap.add_argument("--fuse-gelu", action="store_true",
@@ -422,6 +513,8 @@ def main() -> int:
     svdq.check_device(0)
     if args.workload == "chain":
         return run_chain(args)
+    if args.workload == "prep":
+        return run_prep(args)
     if args.qkv_norm_rope and args.workload != "qkv":
         print("--qkv-norm-rope applies to the qkv and chain workloads only", file=sys.stderr)
         return 2

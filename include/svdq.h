@@ -219,6 +219,35 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
  * recorded by the timing hook below.  Enqueued on `stream`. */
 svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 
+/* Offline weight preparation of an int4 svdq_w4a4 layer on the GPU (the tutorial's
+ * calibrate -> SVDQuant -> package step; Diffusers docs "Nunchaku Lite" introduction).
+ * From W [K][N] fp32 (Y = X W) and calibration activations x_cal [Mc][K] bf16:
+ *   smooth[k] = bf16(fl32(1 / sqrt(max(amax_m |x_cal[m][k]|, 1e-5))))
+ *   What = W / smooth (float64, per input row)
+ *   What ~ L1 L2, L1 [K][r], L2 [r][N]: a randomized top-r factorization (Halko,
+ *     Martinsson, Tropp 2011: range finder with power_iters power iterations on
+ *     l = rank + oversample columns, CholeskyQR2, Jacobi eigen-decomposition of the
+ *     projected l x l problem), each column of L1 signed so that its largest-magnitude
+ *     entry is positive; lora_down [r][K] = bf16(L1^T), lora_up [N][r] = bf16(L2^T)
+ *   R = What - L1_bf16 L2_bf16 (float64, stored as float32; residual [K][N] if not NULL)
+ *   qweight [N][K/2] int4 two's complement nibbles, wscales [N][K/64] bf16: R per output
+ *     column in groups of 64, s = bf16(fl32(amax / 7)), q = round-half-even(R / s).
+ * omega [N][l] float64 is the Gaussian test matrix (drawn by the caller).  The outputs
+ * are the interchange layout of svdq_pack_weight / svdq_pack_lora_down.  rank 0, 16 or
+ * 32 (rank 0: no factorization, R = What, omega / lora pointers may be NULL);
+ * rank + oversample <= min(64, K, N); K and N multiples of 128.  Device pointers,
+ * 16-byte aligned; the workspace (svdq_prepare_workspace_bytes) is the caller's.  Runs
+ * on `stream` and synchronizes it.  Errors: SVDQ_ERR_NULL, SVDQ_ERR_CONFIG,
+ * SVDQ_ERR_SHAPE, SVDQ_ERR_ALIGN, SVDQ_ERR_WORKSPACE, SVDQ_ERR_DEVICE, SVDQ_ERR_HIP,
+ * SVDQ_ERR_RANGE (the factorization broke down: What has rank below l). */
+size_t svdq_prepare_workspace_bytes(int64_t K, int64_t N, int32_t rank, int32_t oversample);
+svdq_status svdq_prepare_int4(int64_t K, int64_t N, int32_t rank, const float* w,
+                              const uint16_t* x_cal, int64_t Mc, const double* omega,
+                              int32_t oversample, int32_t power_iters, uint8_t* qweight,
+                              uint16_t* wscales, uint16_t* smooth, uint16_t* lora_down,
+                              uint16_t* lora_up, float* residual, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Graph capture of a sequence of calls (Diffusers docs "Nunchaku Lite", "Fused kernels"
  * and the tutorial's torch.compile section: once the kernels are fused, what is left of
  * a denoise step's latency is launch overhead, which compiling the model recovers).

@@ -97,6 +97,20 @@ def low_rank(w_hat: np.ndarray, rank: int):
     return L1, L2
 
 
+def residual(w_hat: np.ndarray, l1_bits, l2_bits) -> np.ndarray:
+    """R = What - L1_bf16 @ L2_bf16 in float64, stored as float32 [K, N]."""
+    R = np.asarray(w_hat, np.float64) - F.bf16_to_f64(l1_bits) @ F.bf16_to_f64(l2_bits)
+    return R.astype(np.float32)
+
+
+def residual_int4(r32: np.ndarray):
+    """int4 weight quantization of the residual per output column (rows of R^T) in
+    groups of 64 along K: (packed codes [N, K/2], bf16 scale bits [N, K/64])."""
+    q, s_bits = Q.int4_scales_codes(np.ascontiguousarray(np.asarray(r32, np.float32).T),
+                                    Q.INT4_GROUP)
+    return F.pack_nibbles(F.int4_encode(q)), s_bits
+
+
 def nvfp4_global(amax: float) -> float:
     """Per-tensor NVFP4 scale fl32(amax / (6 * 448))."""
     return float(np.float32(np.float32(amax) / np.float32(6.0 * 448.0)))
@@ -113,12 +127,11 @@ def prepare_svdq(w_f32, x_cal_bits, bias_bits, rank: int = 32, precision: str = 
     L1, L2 = low_rank(w_hat, rank)
     l1_bits = F.bf16_rne(L1.astype(np.float32))          # [K, r]
     l2_bits = F.bf16_rne(L2.astype(np.float32))          # [r, N]
-    R = w_hat - F.bf16_to_f64(l1_bits) @ F.bf16_to_f64(l2_bits)
-    R32 = R.astype(np.float32)
+    R32 = residual(w_hat, l1_bits, l2_bits)
     Rt = np.ascontiguousarray(R32.T)                      # [N, K]: per output column
     if precision == "int4":
-        q, s_bits = Q.int4_scales_codes(Rt, Q.INT4_GROUP)
-        qweight, wscales, gw, gx = F.pack_nibbles(F.int4_encode(q)), s_bits, 1.0, 1.0
+        qweight, wscales = residual_int4(R32)
+        gw, gx = 1.0, 1.0
     elif precision == "nvfp4":
         gw = nvfp4_global(float(np.max(np.abs(R32))))
         xhat = Q.smooth(x_cal_bits, m_bits)

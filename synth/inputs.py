@@ -298,3 +298,9 @@ def qk_norm_weights(config_id: int = 3, head_dim: int = 128):
     rng = np.random.default_rng(seeds(config_id).w + 900)
     w = 1.0 + 0.1 * rng.standard_normal((2, head_dim))
     return to_bf16_bits(w[0].astype(np.float32)), to_bf16_bits(w[1].astype(np.float32))
+
+
+def gaussian_test_matrix(N: int, cols: int, seed: int) -> np.ndarray:
+    """Omega [N, cols] float64 ~ N(0, 1): the random test matrix of the randomized
+    low-rank factorization in the GPU weight preparation (drawn here, passed in)."""
+    return np.random.default_rng(seed).standard_normal((N, cols))

@@ -245,3 +245,23 @@ def test_separate_qk_norm_rope_validation():
     assert call(eps=0.0) == L.ERR_RANGE
     assert call(rope=FAKE_MISALIGNED) == L.ERR_ALIGN
     assert call(M=0) == L.OK
+
+
+def test_prepare_entry_validation():
+    lib = L.lib()
+
+    def call(K=512, N=512, rank=32, over=16, iters=4, Mc=8, w=FAKE, om=FAKE, nbytes=1 << 40):
+        return lib.svdq_prepare_int4(K, N, rank, w, FAKE, Mc, om, over, iters, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, None, FAKE, nbytes, None)
+
+    assert call(w=None) == L.ERR_NULL
+    assert call(om=None) == L.ERR_NULL
+    assert call(om=None, rank=0) != L.ERR_NULL        # rank 0 needs no test matrix
+    assert call(rank=8) == L.ERR_CONFIG
+    assert call(K=500) == L.ERR_SHAPE
+    assert call(over=40) == L.ERR_SHAPE              # rank + oversample > 64
+    assert call(Mc=0) == L.ERR_SHAPE
+    assert call(nbytes=16) == L.ERR_WORKSPACE
+    assert call(w=FAKE_MISALIGNED) == L.ERR_ALIGN
+    need = lib.svdq_prepare_workspace_bytes(512, 512, 32, 16)
+    assert need >= 512 * 512 * 12                      # float64 What and float32 residual

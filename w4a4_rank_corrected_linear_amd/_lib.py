@@ -86,6 +86,11 @@ def lib() -> ctypes.CDLL:
     L.awq_w4a16_linear.restype = st
     L.svdq_gelu_bf16.argtypes = [vp, vp, i64, vp]
     L.svdq_gelu_bf16.restype = st
+    L.svdq_prepare_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
+    L.svdq_prepare_workspace_bytes.restype = ctypes.c_size_t
+    L.svdq_prepare_int4.argtypes = [i64, i64, ctypes.c_int32, vp, vp, i64, vp, ctypes.c_int32,
+                                    ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.svdq_prepare_int4.restype = st
     L.svdq_capture_begin.argtypes = [vp]
     L.svdq_capture_begin.restype = st
     L.svdq_capture_end.argtypes = [vp, ctypes.POINTER(vp)]

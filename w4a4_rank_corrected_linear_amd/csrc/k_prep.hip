@@ -1,0 +1,427 @@
+// Offline weight preparation of an int4 svdq_w4a4 layer on the GPU: the step before
+// the layer runs (infolabhq tutorial, section on quantizing your own model; Diffusers
+// docs "Nunchaku Lite" introduction: calibrate, SVDQuant, package).  The pages give
+// no formulas; the readings, as in the CPU reference of this repository:
+//
+//   m_k   = bf16(fl32(1 / sqrt(max(amax_k(X_cal), 1e-5))))      smoothing, per channel
+//   What  = W / m  (float64, per input row k)
+//   What ~ L1 L2, L1 = U_r S_r [K, r], L2 = V_r^T [r, N]: a top-r factorization, each
+//          column of L1 signed so its largest-magnitude entry is positive, then bf16
+//   R     = What - L1_bf16 L2_bf16  (float64, stored as float32)
+//   R quantized per output column in groups of 64 along K: s = bf16(fl32(amax / 7)),
+//   q = round-half-even(R / s) in [-7, 7].
+//
+// The factorization is a randomized subspace iteration (Halko, Martinsson and Tropp,
+// "Finding structure with randomness", 2011: the randomized range finder with power
+// iterations, Algorithms 4.3/4.4, and the direct SVD of the projected matrix,
+// Algorithm 5.1), all in float64:
+//   Y = What Omega (Omega [N, l] Gaussian, an input), Q = orth(Y);
+//   repeat p times: Q = orth(What orth(What^T Q));
+//   B = Q^T What [l, N];  B B^T = Ub diag(S^2) Ub^T (Jacobi, one workgroup);
+//   L1 = Q Ub_r diag(S_r),  L2 = diag(1 / S_r) Ub_r^T B.
+// orth() is CholeskyQR2: G = Y^T Y = R^T R (Cholesky, one workgroup), Y = Y R^-1,
+// twice.  It is not the exact SVD: L1 L2 is the projection of What on an l-dimensional
+// subspace found by p power iterations, whose residual approaches the optimal one
+// (Eckart-Young) as p grows.
+#include <algorithm>
+#include <cmath>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kMaxL = 64;  // l = rank + oversampling
+
+// m_k from the calibration activations, one thread per channel (coalesced over k).
+__global__ void __launch_bounds__(256)
+k_prep_smooth(const uint16_t* __restrict__ xc, int64_t Mc, int K, uint16_t* __restrict__ m) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  float a = 0.f;
+  for (int64_t i = 0; i < Mc; ++i) a = fmaxf(a, fabsf(bf16_to_f32(xc[i * K + k])));
+  const double lam = sqrt(fmax((double)a, 1e-5));
+  m[k] = (uint16_t)f32_to_bf16_rne((float)(1.0 / lam));
+}
+
+// What[k][n] = W[k][n] / m_k in float64.
+__global__ void __launch_bounds__(256)
+k_prep_what(const float* __restrict__ w, const uint16_t* __restrict__ m, double* __restrict__ wh,
+            int K, int N) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)K * N) return;
+  wh[i] = (double)w[i] / (double)bf16_to_f32(m[i / N]);
+}
+
+// C[i][j] = sum_k A(i, k) B(k, j), float64, A(i, k) = A[i * as0 + k * as1],
+// B(k, j) = B[k * bs0 + j * bs1], C row-major with leading dimension ldc.  64 x 64
+// tiles, 16 values of k per step through LDS, 4 x 4 outputs per thread, k summed in
+// ascending order.
+__global__ void __launch_bounds__(256)
+k_gemm_f64(const double* __restrict__ A, int64_t as0, int64_t as1, const double* __restrict__ B,
+           int64_t bs0, int64_t bs1, double* __restrict__ C, int64_t ldc, int M, int N, int K) {
+  __shared__ double As[16][65], Bs[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  double c[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int kk = e >> 6, ii = e & 63;
+      const int gi = i0 + ii, gk = k0 + kk;
+      As[kk][ii] = (gi < M && gk < K) ? A[gi * as0 + gk * as1] : 0.0;
+      const int gj = j0 + ii;
+      Bs[kk][ii] = (gj < N && gk < K) ? B[gk * bs0 + gj * bs1] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) c[a][b] = fma(As[kk][ty + 16 * a], Bs[kk][tx + 16 * b], c[a][b]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int gi = i0 + ty + 16 * a, gj = j0 + tx + 16 * b;
+      if (gi < M && gj < N) C[gi * ldc + gj] = c[a][b];
+    }
+}
+
+// Cholesky G = R^T R of an l x l Gram matrix (one workgroup), then Rinv = R^-1 (upper
+// triangular).  A non-positive pivot sets *fail and leaves Rinv = I.
+__global__ void __launch_bounds__(256)
+k_chol_inv(const double* __restrict__ G, int l, double* __restrict__ Rinv, int* __restrict__ fail) {
+  __shared__ double R[kMaxL][kMaxL + 1], X[kMaxL][kMaxL + 1];
+  __shared__ int bad;
+  const int t = threadIdx.x;
+  if (t == 0) bad = 0;
+  for (int e = t; e < l * l; e += 256) {
+    R[e / l][e % l] = G[e];
+    X[e / l][e % l] = (e / l == e % l) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  // right-looking: row j of R from the trailing matrix
+  for (int j = 0; j < l; ++j) {
+    if (t == 0) {
+      const double d = R[j][j];
+      if (!(d > 0.0)) bad = 1;
+      R[j][j] = d > 0.0 ? sqrt(d) : 1.0;
+    }
+    __syncthreads();
+    const double piv = R[j][j];
+    for (int c = j + 1 + t; c < l; c += 256) R[j][c] /= piv;
+    __syncthreads();
+    for (int e = t; e < (l - j - 1) * (l - j - 1); e += 256) {
+      const int a = j + 1 + e / (l - j - 1), b = j + 1 + e % (l - j - 1);
+      if (b >= a) R[a][b] -= R[j][a] * R[j][b];
+    }
+    __syncthreads();
+  }
+  // X = R^-1 by back substitution, one column of X per thread
+  for (int c = t; c < l; c += 256) {
+    for (int i = c; i >= 0; --i) {
+      double v = (i == c) ? 1.0 : 0.0;
+      for (int k = i + 1; k <= c; ++k) v -= R[i][k] * X[k][c];
+      X[i][c] = v / R[i][i];
+    }
+    for (int i = c + 1; i < l; ++i) X[i][c] = 0.0;
+  }
+  __syncthreads();
+  for (int e = t; e < l * l; e += 256) Rinv[e] = X[e / l][e % l];
+  if (t == 0 && bad) atomicOr(fail, 1);
+}
+
+// Eigen-decomposition of a symmetric l x l matrix C (one workgroup) by cyclic Jacobi
+// rotations (Golub and Van Loan, Matrix Computations, the cyclic Jacobi method), pairs
+// (p, q) taken in row order, until the off-diagonal mass is below 1e-30 of the total.
+// Output: eigenvalues descending in ev[l], eigenvectors in the columns of V [l][l].
+__global__ void __launch_bounds__(64)
+k_jacobi(const double* __restrict__ C, int l, double* __restrict__ ev, double* __restrict__ V) {
+  __shared__ double A[kMaxL][kMaxL + 1], Q[kMaxL][kMaxL + 1];
+  __shared__ double cs[2];
+  const int t = threadIdx.x;
+  for (int e = t; e < l * l; e += 64) {
+    A[e / l][e % l] = C[e];
+    Q[e / l][e % l] = (e / l == e % l) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    __shared__ double off, tot;
+    if (t == 0) {
+      double o = 0.0, s = 0.0;
+      for (int a = 0; a < l; ++a)
+        for (int b = 0; b < l; ++b) {
+          const double v = A[a][b] * A[a][b];
+          s += v;
+          if (a != b) o += v;
+        }
+      off = o;
+      tot = s;
+    }
+    __syncthreads();
+    if (!(off > 1e-30 * tot)) break;
+    for (int p = 0; p < l - 1; ++p)
+      for (int q = p + 1; q < l; ++q) {
+        if (t == 0) {
+          const double apq = A[p][q];
+          double c = 1.0, s = 0.0;
+          if (apq != 0.0) {
+            const double theta = (A[q][q] - A[p][p]) / (2.0 * apq);
+            const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(tt * tt + 1.0);
+            s = tt * c;
+          }
+          cs[0] = c;
+          cs[1] = s;
+        }
+        __syncthreads();
+        const double c = cs[0], s = cs[1];
+        if (s != 0.0) {
+          // A = J^T A J, J the rotation in the (p, q) plane; Q = Q J
+          for (int k = t; k < l; k += 64) {
+            const double akp = A[k][p], akq = A[k][q];
+            A[k][p] = c * akp - s * akq;
+            A[k][q] = s * akp + c * akq;
+          }
+          __syncthreads();
+          for (int k = t; k < l; k += 64) {
+            const double apk = A[p][k], aqk = A[q][k];
+            A[p][k] = c * apk - s * aqk;
+            A[q][k] = s * apk + c * aqk;
+            const double qkp = Q[k][p], qkq = Q[k][q];
+            Q[k][p] = c * qkp - s * qkq;
+            Q[k][q] = s * qkp + c * qkq;
+          }
+        }
+        __syncthreads();
+      }
+  }
+  // sort descending (selection, one thread), move vectors along
+  if (t == 0) {
+    int idx[kMaxL];
+    for (int a = 0; a < l; ++a) idx[a] = a;
+    for (int a = 0; a < l; ++a) {
+      int best = a;
+      for (int b = a + 1; b < l; ++b)
+        if (A[idx[b]][idx[b]] > A[idx[best]][idx[best]]) best = b;
+      const int tmp = idx[a];
+      idx[a] = idx[best];
+      idx[best] = tmp;
+    }
+    for (int a = 0; a < l; ++a) {
+      ev[a] = A[idx[a]][idx[a]];
+      for (int k = 0; k < l; ++k) V[k * l + a] = Q[k][idx[a]];
+    }
+  }
+}
+
+// M1 = Ub_r diag(S_r) [l][r] and M2 = diag(1 / S_r) Ub_r^T [r][l] from the eigenpairs
+// of B B^T (S = sqrt of the eigenvalue).  A non-positive eigenvalue among the top r
+// sets *fail.
+__global__ void k_prep_small(const double* __restrict__ ev, const double* __restrict__ V, int l,
+                             int r, double* __restrict__ M1, double* __restrict__ M2,
+                             int* __restrict__ fail) {
+  const int t = threadIdx.x;
+  for (int e = t; e < l * r; e += blockDim.x) {
+    const int a = e / r, j = e % r;
+    const double lam = ev[j];
+    const double s = lam > 0.0 ? sqrt(lam) : 0.0;
+    M1[a * r + j] = V[a * l + j] * s;
+    M2[j * l + a] = s > 0.0 ? V[a * l + j] / s : 0.0;
+  }
+  if (t == 0)
+    for (int j = 0; j < r; ++j)
+      if (!(ev[j] > 0.0)) atomicOr(fail, 2);
+}
+
+// Sign of column j of L1 [K][r]: the entry of largest magnitude (first one on ties)
+// made positive; the bf16 factors lora_down [r][K] = L1^T and lora_up [N][r] = L2^T.
+__global__ void __launch_bounds__(256)
+k_prep_sign(const double* __restrict__ L1, int K, int r, int* __restrict__ sgn) {
+  __shared__ double bv[256];
+  __shared__ int bi[256];
+  const int j = blockIdx.x, t = threadIdx.x;
+  double best = -1.0;
+  int bidx = K;
+  for (int k = t; k < K; k += 256) {
+    const double v = fabs(L1[(size_t)k * r + j]);
+    if (v > best) {
+      best = v;
+      bidx = k;
+    }
+  }
+  bv[t] = best;
+  bi[t] = bidx;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (t < h) {
+      const double o = bv[t + h];
+      const int oi = bi[t + h];
+      if (o > bv[t] || (o == bv[t] && oi < bi[t])) {
+        bv[t] = o;
+        bi[t] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  if (t == 0) sgn[j] = L1[(size_t)bi[0] * r + j] < 0.0 ? -1 : 1;
+}
+
+__global__ void __launch_bounds__(256)
+k_prep_factors(const double* __restrict__ L1, const double* __restrict__ L2,
+               const int* __restrict__ sgn, int K, int N, int r, uint16_t* __restrict__ ldown,
+               uint16_t* __restrict__ lup) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)K * r) {  // lora_down[j][k] = sign_j L1[k][j]
+    const int j = (int)(i / K), k = (int)(i % K);
+    ldown[i] = (uint16_t)f32_to_bf16_rne((float)(sgn[j] * L1[(size_t)k * r + j]));
+  }
+  if (i < (int64_t)N * r) {  // lora_up[n][j] = sign_j L2[j][n]
+    const int n = (int)(i / r), j = (int)(i % r);
+    lup[i] = (uint16_t)f32_to_bf16_rne((float)(sgn[j] * L2[(size_t)j * N + n]));
+  }
+}
+
+// R[k][n] = What[k][n] - sum_j L1_bf16[k][j] L2_bf16[j][n] (float64, j ascending),
+// stored as float32.
+__global__ void __launch_bounds__(256)
+k_prep_residual(const double* __restrict__ wh, const uint16_t* __restrict__ ldown,
+                const uint16_t* __restrict__ lup, int K, int N, int r, float* __restrict__ R) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)K * N) return;
+  const int k = (int)(i / N), n = (int)(i % N);
+  double acc = 0.0;
+  for (int j = 0; j < r; ++j)
+    acc = fma((double)bf16_to_f32(ldown[(size_t)j * K + k]), (double)bf16_to_f32(lup[(size_t)n * r + j]),
+              acc);
+  R[i] = (float)(wh[i] - acc);
+}
+
+// int4 quantization of R per output column n and group g of 64 values of k: one
+// workgroup per (64 columns, group); the 64 x 64 block goes through LDS so that the
+// reads of R rows and the writes of column codes are both contiguous.
+__global__ void __launch_bounds__(256)
+k_prep_quant(const float* __restrict__ R, int K, int N, uint8_t* __restrict__ qweight,
+             uint16_t* __restrict__ wscales) {
+  __shared__ float T[64][65];
+  const int n0 = blockIdx.x * 64, g = blockIdx.y, t = threadIdx.x;
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int kk = e >> 6, nn = e & 63;
+    T[nn][kk] = (n0 + nn < N) ? R[(size_t)(64 * g + kk) * N + n0 + nn] : 0.f;
+  }
+  __syncthreads();
+  if (t < 64 && n0 + t < N) {
+    const int n = n0 + t;
+    float amax = 0.f;
+    for (int kk = 0; kk < 64; ++kk) amax = fmaxf(amax, fabsf(T[t][kk]));
+    const uint32_t sb = f32_to_bf16_rne(amax / 7.0f);
+    const double s = (double)__uint_as_float(sb << 16);
+    wscales[(size_t)n * (K / 64) + g] = (uint16_t)sb;
+    uint8_t* dst = qweight + (size_t)n * (K / 2) + 32 * g;
+    for (int kk = 0; kk < 64; kk += 2) {
+      int q[2];
+      for (int u = 0; u < 2; ++u) {
+        // the quotient in float64 decides the round-half-even exactly
+        const double v = s > 0.0 ? rint((double)T[t][kk + u] / s) : 0.0;
+        q[u] = (int)fmin(fmax(v, -7.0), 7.0);
+      }
+      dst[kk / 2] = (uint8_t)((q[0] & 15) | ((q[1] & 15) << 4));
+    }
+  }
+}
+
+size_t al(size_t b) { return (b + 255) & ~size_t(255); }
+
+// eigenvalues (kMaxL), then M1 [l][r] and M2 [r][l] with r <= 32
+constexpr size_t kSmallBytes = (kMaxL + 2 * kMaxL * 32) * 8;
+
+}  // namespace
+
+size_t prep_workspace_bytes(int64_t K, int64_t N, int rank, int l) {
+  return al(K * N * 8) + al(K * l * 8) * 2 + al(N * l * 8) + al(l * N * 8) + 3 * al(64 * 64 * 8) +
+         al(kSmallBytes) + al(K * rank * 8) + al(rank * N * 8) + al(K * N * 4) + al(256);
+}
+
+hipError_t launch_prep_int4(int K, int N, int rank, int l, int iters, const float* w,
+                            const uint16_t* xc, int64_t Mc, const double* omega, uint8_t* qweight,
+                            uint16_t* wscales, uint16_t* smooth, uint16_t* ldown, uint16_t* lup,
+                            float* residual, void* ws, int* fail_host, hipStream_t st) {
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  auto take = [&](size_t b) { uint8_t* q = p; p += al(b); return q; };
+  double* wh = reinterpret_cast<double*>(take((size_t)K * N * 8));
+  double* Y = reinterpret_cast<double*>(take((size_t)K * l * 8));
+  double* Y2 = reinterpret_cast<double*>(take((size_t)K * l * 8));
+  double* Z = reinterpret_cast<double*>(take((size_t)N * l * 8));
+  double* Bm = reinterpret_cast<double*>(take((size_t)l * N * 8));
+  double* G = reinterpret_cast<double*>(take(64 * 64 * 8));
+  double* Rinv = reinterpret_cast<double*>(take(64 * 64 * 8));
+  double* Vv = reinterpret_cast<double*>(take(64 * 64 * 8));
+  double* small = reinterpret_cast<double*>(take(kSmallBytes));
+  double* L1 = reinterpret_cast<double*>(take((size_t)K * rank * 8));
+  double* L2 = reinterpret_cast<double*>(take((size_t)rank * N * 8));
+  float* R = residual ? residual : reinterpret_cast<float*>(take((size_t)K * N * 4));
+  if (residual) take((size_t)K * N * 4);
+  int* flags = reinterpret_cast<int*>(take(256));  // fail flag, signs
+  int* sgn = flags + 1;
+
+  auto gemm = [&](const double* A, int64_t as0, int64_t as1, const double* B, int64_t bs0,
+                  int64_t bs1, double* C, int64_t ldc, int M, int Nn, int Kk) {
+    dim3 grid((Nn + 63) / 64, (M + 63) / 64);
+    hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, st, A, as0, as1, B, bs0, bs1, C, ldc, M, Nn, Kk);
+  };
+  // orth(Y [n][l]) in place by CholeskyQR2
+  auto orth = [&](double* Yp, int n) {
+    for (int pass = 0; pass < 2; ++pass) {
+      gemm(Yp, 1, l, Yp, l, 1, G, l, l, l, n);                       // G = Y^T Y
+      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(256), 0, st, G, l, Rinv, flags);
+      gemm(Yp, l, 1, Rinv, l, 1, Y2, l, n, l, l);                    // Y2 = Y R^-1
+      hipMemcpyAsync(Yp, Y2, (size_t)n * l * 8, hipMemcpyDeviceToDevice, st);
+    }
+  };
+
+  hipError_t e = hipMemsetAsync(flags, 0, 256, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prep_smooth, dim3((K + 255) / 256), dim3(256), 0, st, xc, Mc, K, smooth);
+  const int64_t KN = (int64_t)K * N;
+  hipLaunchKernelGGL(k_prep_what, dim3((unsigned)((KN + 255) / 256)), dim3(256), 0, st, w, smooth,
+                     wh, K, N);
+  if (rank > 0) {
+    gemm(wh, N, 1, omega, l, 1, Y, l, K, l, N);                      // Y = What Omega
+    orth(Y, K);
+    for (int it = 0; it < iters; ++it) {
+      gemm(wh, 1, N, Y, l, 1, Z, l, N, l, K);                        // Z = What^T Q
+      orth(Z, N);
+      gemm(wh, N, 1, Z, l, 1, Y, l, K, l, N);                        // Y = What Z
+      orth(Y, K);
+    }
+    gemm(Y, 1, l, wh, N, 1, Bm, N, l, N, K);                         // B = Q^T What [l][N]
+    gemm(Bm, N, 1, Bm, 1, N, G, l, l, l, N);                         // C = B B^T
+    double* ev = small;
+    double* M1 = small + kMaxL;
+    double* M2 = small + kMaxL + kMaxL * 32;
+    hipLaunchKernelGGL(k_jacobi, dim3(1), dim3(64), 0, st, G, l, ev, Vv);
+    hipLaunchKernelGGL(k_prep_small, dim3(1), dim3(256), 0, st, ev, Vv, l, rank, M1, M2, flags);
+    gemm(Y, l, 1, M1, rank, 1, L1, rank, K, rank, l);                // L1 = Q Ub_r S_r
+    gemm(M2, l, 1, Bm, N, 1, L2, N, rank, N, l);                     // L2 = S_r^-1 Ub_r^T B
+    hipLaunchKernelGGL(k_prep_sign, dim3(rank), dim3(256), 0, st, L1, K, rank, sgn);
+    const int64_t nf = std::max<int64_t>((int64_t)K * rank, (int64_t)N * rank);
+    hipLaunchKernelGGL(k_prep_factors, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, st, L1,
+                       L2, sgn, K, N, rank, ldown, lup);
+  }
+  hipLaunchKernelGGL(k_prep_residual, dim3((unsigned)((KN + 255) / 256)), dim3(256), 0, st, wh,
+                     ldown, lup, K, N, rank, R);
+  hipLaunchKernelGGL(k_prep_quant, dim3((N + 63) / 64, K / 64), dim3(256), 0, st, R, K, N, qweight,
+                     wscales);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(fail_host, flags, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(st);
+}
+
+}  // namespace svdq

@@ -82,6 +82,17 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
 
 hipError_t launch_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t st);
 
+// Offline int4 weight preparation on the GPU (k_prep.hip): smoothing factors, the
+// randomized top-rank factorization of the smoothed weight (l = rank + oversampling
+// columns, iters power iterations), the bf16 factors and the int4 residual.  Runs on
+// `st` and synchronizes it; *fail_host gets 0, or a nonzero code when the
+// orthonormalization or the small eigenproblem broke down.
+size_t prep_workspace_bytes(int64_t K, int64_t N, int rank, int l);
+hipError_t launch_prep_int4(int K, int N, int rank, int l, int iters, const float* w,
+                            const uint16_t* xc, int64_t Mc, const double* omega, uint8_t* qweight,
+                            uint16_t* wscales, uint16_t* smooth, uint16_t* ldown, uint16_t* lup,
+                            float* residual, void* ws, int* fail_host, hipStream_t st);
+
 // Per-head Q/K RMSNorm + rotary embedding on a bf16 [M][N] QKV output (N = 3 H 128);
 // the V third is copied when y != x.
 hipError_t launch_qk_norm_rope_bf16(const uint16_t* x, uint16_t* y, int64_t M, int N,

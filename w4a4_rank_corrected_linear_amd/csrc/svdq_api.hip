@@ -3,6 +3,7 @@
 // workspace layout and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -463,6 +464,53 @@ svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_
   if (n == 0) return ok();
   SVDQ_TRY(check_current_device());
   SVDQ_TRY(hip_check(svdq::launch_gelu_bf16(x, y, n, stream), "gelu kernel launch"));
+  return ok();
+}
+
+size_t svdq_prepare_workspace_bytes(int64_t K, int64_t N, int32_t rank, int32_t oversample) {
+  if (K <= 0 || N <= 0 || rank < 0 || oversample < 0) return 0;
+  return svdq::prep_workspace_bytes(K, N, rank, rank + oversample);
+}
+
+svdq_status svdq_prepare_int4(int64_t K, int64_t N, int32_t rank, const float* w,
+                              const uint16_t* x_cal, int64_t Mc, const double* omega,
+                              int32_t oversample, int32_t power_iters, uint8_t* qweight,
+                              uint16_t* wscales, uint16_t* smooth, uint16_t* lora_down,
+                              uint16_t* lora_up, float* residual, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !x_cal || !qweight || !wscales || !smooth || !workspace)
+    return fail(SVDQ_ERR_NULL, "svdq_prepare_int4: NULL argument");
+  if (rank != 0 && rank != 16 && rank != 32)
+    return fail(SVDQ_ERR_CONFIG, "svdq_prepare_int4: rank %d unsupported (0, 16 or 32)", rank);
+  if (rank > 0 && (!omega || !lora_down || !lora_up))
+    return fail(SVDQ_ERR_NULL, "svdq_prepare_int4: rank %d needs omega, lora_down and lora_up",
+                rank);
+  SVDQ_TRY(check_k(K));
+  SVDQ_TRY(check_n(N));
+  const int64_t l = rank + (int64_t)oversample;
+  if (oversample < 0 || power_iters < 0 || power_iters > 64 || Mc < 1 || Mc > (int64_t(1) << 24) ||
+      (rank > 0 && (l > 64 || l > std::min(K, N))))
+    return fail(SVDQ_ERR_SHAPE, "svdq_prepare_int4: need Mc >= 1, 0 <= power_iters <= 64 and "
+                "rank + oversample <= min(64, K, N)");
+  if (!aligned16(w) || !aligned16(x_cal) || !aligned16(qweight) || !aligned16(wscales) ||
+      !aligned16(smooth) || !aligned16(workspace) || (omega && !aligned16(omega)) ||
+      (lora_down && !aligned16(lora_down)) || (lora_up && !aligned16(lora_up)) ||
+      (residual && !aligned16(residual)))
+    return fail(SVDQ_ERR_ALIGN, "svdq_prepare_int4: pointers must be 16-byte aligned");
+  const size_t need = svdq::prep_workspace_bytes(K, N, rank, (int)l);
+  if (workspace_bytes < need)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need);
+  SVDQ_TRY(check_current_device());
+  int failed = 0;
+  SVDQ_TRY(hip_check(svdq::launch_prep_int4((int)K, (int)N, rank, (int)l, power_iters, w, x_cal,
+                                             Mc, omega, qweight, wscales, smooth, lora_down,
+                                             lora_up, residual, workspace, &failed, stream),
+                     "weight preparation"));
+  if (failed)
+    return fail(SVDQ_ERR_RANGE, "svdq_prepare_int4: the factorization broke down (%s); the "
+                "smoothed weight may have rank below rank + oversample",
+                failed & 1 ? "Cholesky of a Gram matrix" : "non-positive singular value");
   return ok();
 }
 
