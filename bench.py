@@ -300,7 +300,7 @@ def run_chain(args) -> int:
 
 
 def run_prep(args) -> int:
-    """Offline int4 weight preparation on the GPU (svdq_prepare_int4) of the attention
+    """Offline int4 weight preparation on the GPU (svdq_prepare_weight) of the attention
     projection's weight (K = N = 3072, rank 32, 16 oversampling columns, 8 power
     iterations, 4096 calibration rows), timed per call; with the CPU baseline, the
     oracle's preparation (exact float64 SVD) on the same inputs, and the ratio of the
@@ -329,12 +329,15 @@ def run_prep(args) -> int:
     work = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
+    cfg = svdq._lib.config("int4", rank)
+
     def call():
-        svdq._lib.check(L.svdq_prepare_int4(K, N, rank, w.data_ptr(), xc.data_ptr(), 4096,
-                                            om.data_ptr(), over, iters, qw.data_ptr(),
-                                            sc.data_ptr(), sm.data_ptr(), ld.data_ptr(),
-                                            lu.data_ptr(), res.data_ptr(), work.data_ptr(), nbytes,
-                                            stream), "svdq_prepare_int4")
+        svdq._lib.check(L.svdq_prepare_weight(ctypes.byref(cfg), K, N, w.data_ptr(), xc.data_ptr(),
+                                              4096, om.data_ptr(), over, iters, qw.data_ptr(),
+                                              sc.data_ptr(), sm.data_ptr(), ld.data_ptr(),
+                                              lu.data_ptr(), res.data_ptr(), None, None,
+                                              work.data_ptr(), nbytes, stream),
+                        "svdq_prepare_weight")
 
     steps, warmup = min(args.steps, 20), min(args.warmup, 3)
     print(f"[bench] workload prep: K=N={K}, rank {rank}, oversample {over}, {iters} power "

@@ -219,9 +219,10 @@ svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
  * recorded by the timing hook below.  Enqueued on `stream`. */
 svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 
-/* Offline weight preparation of an int4 svdq_w4a4 layer on the GPU (the tutorial's
- * calibrate -> SVDQuant -> package step; Diffusers docs "Nunchaku Lite" introduction).
- * From W [K][N] fp32 (Y = X W) and calibration activations x_cal [Mc][K] bf16:
+/* Offline weight preparation on the GPU (the tutorial's calibrate -> SVDQuant ->
+ * package step; Diffusers docs "Nunchaku Lite" introduction).  svdq_prepare_weight
+ * prepares an svdq_w4a4 layer of cfg (int4 or nvfp4, rank cfg->rank) from W [K][N]
+ * fp32 (Y = X W) and calibration activations x_cal [Mc][K] bf16:
  *   smooth[k] = bf16(fl32(1 / sqrt(max(amax_m |x_cal[m][k]|, 1e-5))))
  *   What = W / smooth (float64, per input row)
  *   What ~ L1 L2, L1 [K][r], L2 [r][N]: a randomized top-r factorization (Halko,
@@ -230,23 +231,37 @@ svdq_status svdq_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_
  *     projected l x l problem), each column of L1 signed so that its largest-magnitude
  *     entry is positive; lora_down [r][K] = bf16(L1^T), lora_up [N][r] = bf16(L2^T)
  *   R = What - L1_bf16 L2_bf16 (float64, stored as float32; residual [K][N] if not NULL)
- *   qweight [N][K/2] int4 two's complement nibbles, wscales [N][K/64] bf16: R per output
- *     column in groups of 64, s = bf16(fl32(amax / 7)), q = round-half-even(R / s).
+ *   int4:  qweight [N][K/2] two's complement nibbles, wscales [N][K/64] bf16: R per
+ *          output column in groups of 64, s = bf16(fl32(amax / 7)), q = rne(R / s)
+ *   nvfp4: *w_global = fl32(amax|R| / 2688), qweight [N][K/2] E2M1 nibbles, wscales
+ *          [N][K/16] E4M3 codes (the activation quantizer's rule on R per column), and
+ *          *act_global = fl32(amax|bf16(x_cal smooth)| / 2688); w_global and
+ *          act_global are host pointers (ignored for int4).
  * omega [N][l] float64 is the Gaussian test matrix (drawn by the caller).  The outputs
- * are the interchange layout of svdq_pack_weight / svdq_pack_lora_down.  rank 0, 16 or
- * 32 (rank 0: no factorization, R = What, omega / lora pointers may be NULL);
- * rank + oversample <= min(64, K, N); K and N multiples of 128.  Device pointers,
- * 16-byte aligned; the workspace (svdq_prepare_workspace_bytes) is the caller's.  Runs
- * on `stream` and synchronizes it.  Errors: SVDQ_ERR_NULL, SVDQ_ERR_CONFIG,
- * SVDQ_ERR_SHAPE, SVDQ_ERR_ALIGN, SVDQ_ERR_WORKSPACE, SVDQ_ERR_DEVICE, SVDQ_ERR_HIP,
- * SVDQ_ERR_RANGE (the factorization broke down: What has rank below l). */
+ * are the interchange layout of svdq_pack_weight / svdq_pack_lora_down.  rank 0: no
+ * factorization, R = What, omega / lora pointers may be NULL.  rank + oversample <=
+ * min(64, K, N); K and N multiples of 128.  Device pointers (except w_global and
+ * act_global), 16-byte aligned; the workspace (svdq_prepare_workspace_bytes) is the
+ * caller's.  Runs on `stream` and synchronizes it.  Errors: SVDQ_ERR_NULL,
+ * SVDQ_ERR_CONFIG, SVDQ_ERR_SHAPE, SVDQ_ERR_ALIGN, SVDQ_ERR_WORKSPACE, SVDQ_ERR_DEVICE,
+ * SVDQ_ERR_HIP, SVDQ_ERR_RANGE (the factorization broke down, What having rank below
+ * l, or a zero NVFP4 tensor scale).
+ *
+ * awq_prepare_weight: the AWQ W4A16 layer's weights from W [K][N] fp32 (no smoothing,
+ * no factorization): per output column and group of 64, s = bf16(fl32((max - min) /
+ * 15)), z = clamp(rne(-min / s), 0, 15), q = clamp(rne(w / s) + z, 0, 15) (s = 0: all
+ * zero); qweight [N][K/2], scales [N][K/64] bf16, zeros [N][K/64] u8.  Asynchronous on
+ * `stream`; errors as above without SVDQ_ERR_WORKSPACE and SVDQ_ERR_RANGE. */
 size_t svdq_prepare_workspace_bytes(int64_t K, int64_t N, int32_t rank, int32_t oversample);
-svdq_status svdq_prepare_int4(int64_t K, int64_t N, int32_t rank, const float* w,
-                              const uint16_t* x_cal, int64_t Mc, const double* omega,
-                              int32_t oversample, int32_t power_iters, uint8_t* qweight,
-                              uint16_t* wscales, uint16_t* smooth, uint16_t* lora_down,
-                              uint16_t* lora_up, float* residual, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream);
+svdq_status svdq_prepare_weight(const svdq_config* cfg, int64_t K, int64_t N, const float* w,
+                                const uint16_t* x_cal, int64_t Mc, const double* omega,
+                                int32_t oversample, int32_t power_iters, uint8_t* qweight,
+                                void* wscales, uint16_t* smooth, uint16_t* lora_down,
+                                uint16_t* lora_up, float* residual, float* w_global,
+                                float* act_global, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+svdq_status awq_prepare_weight(int64_t K, int64_t N, const float* w, uint8_t* qweight,
+                               uint16_t* scales, uint8_t* zeros, hipStream_t stream);
 
 /* Graph capture of a sequence of calls (Diffusers docs "Nunchaku Lite", "Fused kernels"
  * and the tutorial's torch.compile section: once the kernels are fused, what is left of

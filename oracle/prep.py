@@ -116,6 +116,21 @@ def nvfp4_global(amax: float) -> float:
     return float(np.float32(np.float32(amax) / np.float32(6.0 * 448.0)))
 
 
+def residual_nvfp4(r32: np.ndarray):
+    """NVFP4 weight quantization of the residual per output column in blocks of 16:
+    (g_w, packed E2M1 codes [N, K/2], E4M3 scale codes [N, K/16])."""
+    r32 = np.asarray(r32, np.float32)
+    gw = nvfp4_global(float(np.max(np.abs(r32))))
+    c, s_codes = Q.nvfp4_scales_codes(np.ascontiguousarray(r32.T), gw, Q.NVFP4_GROUP)
+    return gw, F.pack_nibbles(c), s_codes
+
+
+def nvfp4_act_global(x_cal_bits, m_bits) -> float:
+    """Static NVFP4 activation scale g_x from the smoothed calibration activations."""
+    xhat = Q.smooth(x_cal_bits, m_bits)
+    return nvfp4_global(float(np.max(np.abs(F.bf16_to_f32(xhat)))))
+
+
 def prepare_svdq(w_f32, x_cal_bits, bias_bits, rank: int = 32, precision: str = "int4",
                  smooth: bool = True) -> SvdqLayer:
     """Full offline preparation of one svdq_w4a4 layer from W [K, N] and X_cal."""
@@ -128,16 +143,12 @@ def prepare_svdq(w_f32, x_cal_bits, bias_bits, rank: int = 32, precision: str = 
     l1_bits = F.bf16_rne(L1.astype(np.float32))          # [K, r]
     l2_bits = F.bf16_rne(L2.astype(np.float32))          # [r, N]
     R32 = residual(w_hat, l1_bits, l2_bits)
-    Rt = np.ascontiguousarray(R32.T)                      # [N, K]: per output column
     if precision == "int4":
         qweight, wscales = residual_int4(R32)
         gw, gx = 1.0, 1.0
     elif precision == "nvfp4":
-        gw = nvfp4_global(float(np.max(np.abs(R32))))
-        xhat = Q.smooth(x_cal_bits, m_bits)
-        gx = nvfp4_global(float(np.max(np.abs(F.bf16_to_f32(xhat)))))
-        c, s_codes = Q.nvfp4_scales_codes(Rt, gw, Q.NVFP4_GROUP)
-        qweight, wscales = F.pack_nibbles(c), s_codes
+        gw, qweight, wscales = residual_nvfp4(R32)
+        gx = nvfp4_act_global(x_cal_bits, m_bits)
     else:
         raise ValueError(precision)
     return SvdqLayer(precision=precision, K=K, N=N, rank=rank, qweight=qweight,

@@ -250,13 +250,20 @@ def test_separate_qk_norm_rope_validation():
 def test_prepare_entry_validation():
     lib = L.lib()
 
-    def call(K=512, N=512, rank=32, over=16, iters=4, Mc=8, w=FAKE, om=FAKE, nbytes=1 << 40):
-        return lib.svdq_prepare_int4(K, N, rank, w, FAKE, Mc, om, over, iters, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, None, FAKE, nbytes, None)
+    g1, g2 = ctypes.c_float(), ctypes.c_float()
+
+    def call(K=512, N=512, rank=32, over=16, iters=4, Mc=8, w=FAKE, om=FAKE, nbytes=1 << 40,
+             precision=L.INT4, glob=True):
+        c = cfg(precision=precision, group=64 if precision == L.INT4 else 16, rank=rank)
+        return lib.svdq_prepare_weight(ctypes.byref(c), K, N, w, FAKE, Mc, om, over, iters, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, None,
+                                       ctypes.byref(g1) if glob else None,
+                                       ctypes.byref(g2) if glob else None, FAKE, nbytes, None)
 
     assert call(w=None) == L.ERR_NULL
     assert call(om=None) == L.ERR_NULL
     assert call(om=None, rank=0) != L.ERR_NULL        # rank 0 needs no test matrix
+    assert call(precision=L.NVFP4, glob=False) == L.ERR_NULL
     assert call(rank=8) == L.ERR_CONFIG
     assert call(K=500) == L.ERR_SHAPE
     assert call(over=40) == L.ERR_SHAPE              # rank + oversample > 64
@@ -265,3 +272,7 @@ def test_prepare_entry_validation():
     assert call(w=FAKE_MISALIGNED) == L.ERR_ALIGN
     need = lib.svdq_prepare_workspace_bytes(512, 512, 32, 16)
     assert need >= 512 * 512 * 12                      # float64 What and float32 residual
+
+    assert lib.awq_prepare_weight(512, 512, None, FAKE, FAKE, FAKE, None) == L.ERR_NULL
+    assert lib.awq_prepare_weight(500, 512, FAKE, FAKE, FAKE, FAKE, None) == L.ERR_SHAPE
+    assert lib.awq_prepare_weight(512, 512, FAKE_MISALIGNED, FAKE, FAKE, FAKE, None) == L.ERR_ALIGN

@@ -1,8 +1,9 @@
-"""GPU weight preparation (svdq_prepare_int4) against the oracle's preparation: the
-smoothing factors bit-exact, the residual within one float32 step of the oracle's
-formula on the GPU's own bf16 factors, the int4 codes and scales bit-exact on the
-GPU's residual, the factorization's residual norm within 1 % of the exact top-r SVD's
-(Eckart-Young), the sign convention, and the prepared layer end to end."""
+"""GPU weight preparation (svdq_prepare_weight, awq_prepare_weight) against the
+oracle's preparation: the smoothing factors bit-exact, the residual within one float32
+step of the oracle's formula on the GPU's own bf16 factors, the int4 or NVFP4 codes,
+scales and tensor scales bit-exact on the GPU's residual, the factorization's residual
+norm within 1 % of the exact top-r SVD's (Eckart-Young), the sign convention, the
+prepared layer end to end, and the AWQ weights bit-exact."""
 
 import ctypes
 
@@ -20,36 +21,41 @@ from synth import inputs as I
 pytestmark = pytest.mark.gpu
 
 
-def gpu_prepare(w, x_cal, rank=32, oversample=16, iters=8, seed=7):
+def gpu_prepare(w, x_cal, rank=32, oversample=16, iters=8, seed=7, precision="int4"):
     K, N = w.shape
+    nv = precision == "nvfp4"
     L = svdq.lib()
     dev = torch.device("cuda")
     w_d = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(dev)
     xc_d = dev_bf16(x_cal)
     om = torch.from_numpy(I.gaussian_test_matrix(N, rank + oversample, seed)).to(dev) if rank else None
     qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    ws_ = torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev)
+    ws_ = (torch.empty((N, K // 16), dtype=torch.uint8, device=dev) if nv else
+           torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev))
     sm = torch.empty((K,), dtype=torch.bfloat16, device=dev)
     ld = torch.empty((max(rank, 1), K), dtype=torch.bfloat16, device=dev)
     lu = torch.empty((N, max(rank, 1)), dtype=torch.bfloat16, device=dev)
     res = torch.empty((K, N), dtype=torch.float32, device=dev)
     nbytes = L.svdq_prepare_workspace_bytes(K, N, rank, oversample)
     work = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
-    st = L.svdq_prepare_int4(K, N, rank, w_d.data_ptr(), xc_d.data_ptr(), x_cal.shape[0],
-                             om.data_ptr() if rank else None, oversample, iters, qw.data_ptr(),
-                             ws_.data_ptr(), sm.data_ptr(), ld.data_ptr() if rank else None,
-                             lu.data_ptr() if rank else None, res.data_ptr(), work.data_ptr(),
-                             nbytes, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    svdq._lib.check(st, "svdq_prepare_int4")
+    gw, gx = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    cfg = svdq._lib.config(precision, rank)
+    st = L.svdq_prepare_weight(ctypes.byref(cfg), K, N, w_d.data_ptr(), xc_d.data_ptr(),
+                               x_cal.shape[0], om.data_ptr() if rank else None, oversample, iters,
+                               qw.data_ptr(), ws_.data_ptr(), sm.data_ptr(),
+                               ld.data_ptr() if rank else None, lu.data_ptr() if rank else None,
+                               res.data_ptr(), ctypes.byref(gw), ctypes.byref(gx), work.data_ptr(),
+                               nbytes, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    svdq._lib.check(st, "svdq_prepare_weight")
     out = dict(qweight=host_bits(qw), wscales=host_bits(ws_), smooth=host_bits(sm),
-               residual=res.cpu().numpy())
+               residual=res.cpu().numpy(), w_global=gw.value, act_global=gx.value)
     if rank:
         out["lora_down"] = host_bits(ld)
         out["lora_up"] = host_bits(lu)
     return out
 
 
-def check_prepared(w, x_cal, g, ref, rank):
+def check_prepared(w, x_cal, g, ref, rank, precision="int4"):
     # smoothing factors: bit-exact
     assert np.array_equal(g["smooth"], ref.smooth)
     m = F.bf16_to_f64(g["smooth"])
@@ -70,8 +76,13 @@ def check_prepared(w, x_cal, g, ref, rank):
     r = g["residual"]
     assert np.all(np.abs(r.astype(np.float64) - r_ref) <= np.spacing(np.abs(r_ref))), \
         float(np.max(np.abs(r.astype(np.float64) - r_ref)))
-    # the int4 quantization of the GPU's residual: bit-exact
-    qw, s = P.residual_int4(r)
+    # the quantization of the GPU's residual: bit-exact
+    if precision == "int4":
+        qw, s = P.residual_int4(r)
+    else:
+        gw, qw, s = P.residual_nvfp4(r)
+        assert np.float32(g["w_global"]) == np.float32(gw)
+        assert np.float32(g["act_global"]) == np.float32(P.nvfp4_act_global(x_cal, g["smooth"]))
     assert np.array_equal(g["qweight"], qw)
     assert np.array_equal(g["wscales"], s)
 
@@ -111,3 +122,33 @@ def test_prepared_layer_end_to_end():
     e_gpu = np.linalg.norm(F.bf16_to_f64(y) - exact)
     e_plain = np.linalg.norm(OL.w4a4_linear("int4", li.x, plain)["r"] - exact)
     assert e_gpu < e_plain, (e_gpu, e_plain)
+
+
+@pytest.mark.parametrize("rank", [0, 32])
+def test_prepare_nvfp4(rank):
+    li = I.layer_inputs(**I.TINY)
+    ref = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=rank, precision="nvfp4")
+    g = gpu_prepare(li.w, li.x_cal, rank=rank, precision="nvfp4")
+    check_prepared(li.w, li.x_cal, g, ref, rank, precision="nvfp4")
+
+
+@pytest.mark.parametrize("K,N", [(512, 512), (1024, 1536)])
+def test_prepare_awq(K, N):
+    """awq_prepare_weight bit-exact against the oracle, including a constant group
+    (s = 0) and a group with only non-negative values (z = 0)."""
+    w = I.weights(K, N, 11)
+    w[:64, 5] = 0.25                  # constant group: max - min = 0
+    w[64:128, 7] = np.abs(w[64:128, 7])
+    ref = P.prepare_awq(w, None)
+    L = svdq.lib()
+    dev = torch.device("cuda")
+    w_d = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(dev)
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev)
+    zs = torch.empty((N, K // 64), dtype=torch.uint8, device=dev)
+    st = L.awq_prepare_weight(K, N, w_d.data_ptr(), qw.data_ptr(), sc.data_ptr(), zs.data_ptr(),
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    svdq._lib.check(st, "awq_prepare_weight")
+    assert np.array_equal(host_bits(qw), ref.qweight)
+    assert np.array_equal(host_bits(sc), ref.scales)
+    assert np.array_equal(host_bits(zs), ref.zeros)

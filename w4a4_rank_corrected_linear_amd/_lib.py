@@ -88,9 +88,12 @@ def lib() -> ctypes.CDLL:
     L.svdq_gelu_bf16.restype = st
     L.svdq_prepare_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
     L.svdq_prepare_workspace_bytes.restype = ctypes.c_size_t
-    L.svdq_prepare_int4.argtypes = [i64, i64, ctypes.c_int32, vp, vp, i64, vp, ctypes.c_int32,
-                                    ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    L.svdq_prepare_int4.restype = st
+    fp = ctypes.POINTER(ctypes.c_float)
+    L.svdq_prepare_weight.argtypes = [cfgp, i64, i64, vp, vp, i64, vp, ctypes.c_int32, ctypes.c_int32,
+                                      vp, vp, vp, vp, vp, vp, fp, fp, vp, ctypes.c_size_t, vp]
+    L.svdq_prepare_weight.restype = st
+    L.awq_prepare_weight.argtypes = [i64, i64, vp, vp, vp, vp, vp]
+    L.awq_prepare_weight.restype = st
     L.svdq_capture_begin.argtypes = [vp]
     L.svdq_capture_begin.restype = st
     L.svdq_capture_end.argtypes = [vp, ctypes.POINTER(vp)]

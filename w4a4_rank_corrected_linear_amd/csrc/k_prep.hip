@@ -1,4 +1,5 @@
-// Offline weight preparation of an int4 svdq_w4a4 layer on the GPU: the step before
+// Offline weight preparation of svdq_w4a4 (int4, nvfp4) and awq_w4a16 layers on the
+// GPU: the step before
 // the layer runs (infolabhq tutorial, section on quantizing your own model; Diffusers
 // docs "Nunchaku Lite" introduction: calibrate, SVDQuant, package).  The pages give
 // no formulas; the readings, as in the CPU reference of this repository:
@@ -9,7 +10,10 @@
 //          column of L1 signed so its largest-magnitude entry is positive, then bf16
 //   R     = What - L1_bf16 L2_bf16  (float64, stored as float32)
 //   R quantized per output column in groups of 64 along K: s = bf16(fl32(amax / 7)),
-//   q = round-half-even(R / s) in [-7, 7].
+//   q = round-half-even(R / s) in [-7, 7]; or NVFP4: g_w = fl32(amax|R| / 2688), E4M3
+//   block scales and E2M1 codes per 16 (the activation quantizer's rule), and the
+//   static activation scale g_x = fl32(amax|bf16(x_cal m)| / 2688);
+//   AWQ (no smoothing, no factorization): asymmetric uint4 per column and group of 64.
 //
 // The factorization is a randomized subspace iteration (Halko, Martinsson and Tropp,
 // "Finding structure with randomness", 2011: the randomized range finder with power
@@ -28,6 +32,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "nvfp4_device.h"
 
 namespace svdq {
 
@@ -335,6 +340,98 @@ k_prep_quant(const float* __restrict__ R, int K, int N, uint8_t* __restrict__ qw
   }
 }
 
+// NVFP4: max |R| and max |bf16(x m)| over the calibration activations (float bits as
+// unsigned: the maximum of non-negative floats, in any order), then the per-tensor
+// scales g_w = fl32(amax_R / 2688) and g_x = fl32(amax_xhat / 2688).
+__global__ void __launch_bounds__(256)
+k_prep_absmax(const float* __restrict__ R, int64_t n, unsigned* __restrict__ out) {
+  float a = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    a = fmaxf(a, fabsf(R[i]));
+  for (int d = 32; d > 0; d >>= 1) a = fmaxf(a, __shfl_xor(a, d));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(a));
+}
+
+__global__ void __launch_bounds__(256)
+k_prep_absmax_xhat(const uint16_t* __restrict__ xc, int64_t n, int K, const uint16_t* __restrict__ m,
+                   unsigned* __restrict__ out) {
+  float a = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float xh = bf16_to_f32(f32_to_bf16_rne(bf16_to_f32(xc[i]) * bf16_to_f32(m[i % K])));
+    a = fmaxf(a, fabsf(xh));
+  }
+  for (int d = 32; d > 0; d >>= 1) a = fmaxf(a, __shfl_xor(a, d));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(a));
+}
+
+__global__ void k_prep_globals(const unsigned* __restrict__ amax, float* __restrict__ g) {
+  if (threadIdx.x < 2) g[threadIdx.x] = __uint_as_float(amax[threadIdx.x]) / 2688.0f;
+}
+
+// NVFP4 quantization of R per output column in blocks of 16 (nvfp4_quant32 on two
+// blocks at a time), 64 x 64 blocks of R transposed through LDS: codes [N][K/2]
+// (element 2j in bits 3:0), E4M3 scale codes [N][K/16].
+__global__ void __launch_bounds__(256)
+k_prep_quant_nvfp4(const float* __restrict__ R, int K, int N, const float* __restrict__ g,
+                   uint8_t* __restrict__ qweight, uint8_t* __restrict__ wscales) {
+  __shared__ float T[64][65];
+  const int n0 = blockIdx.x * 64, kb = blockIdx.y, t = threadIdx.x;
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int kk = e >> 6, nn = e & 63;
+    T[nn][kk] = (n0 + nn < N) ? R[(size_t)(64 * kb + kk) * N + n0 + nn] : 0.f;
+  }
+  __syncthreads();
+  if (t < 64 && n0 + t < N) {
+    const int n = n0 + t;
+    const float gw = g[0];
+    for (int c = 0; c < 2; ++c) {
+      float v[32], deq[32];
+      uint32_t codes[32], sc[2];
+      for (int i = 0; i < 32; ++i) v[i] = T[t][32 * c + i];
+      nvfp4_quant32(v, gw, codes, deq, sc);
+      uint8_t* dst = qweight + (size_t)n * (K / 2) + 32 * kb + 16 * c;
+      for (int i = 0; i < 16; ++i) dst[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+      wscales[(size_t)n * (K / 16) + 4 * kb + 2 * c] = (uint8_t)sc[0];
+      wscales[(size_t)n * (K / 16) + 4 * kb + 2 * c + 1] = (uint8_t)sc[1];
+    }
+  }
+}
+
+// AWQ W4A16 weights: per output column n and group of 64 along K, asymmetric uint4
+// with s = bf16(fl32((max - min) / 15)), z = clamp(rne(-min / s), 0, 15),
+// q = clamp(rne(w / s) + z, 0, 15) (the quotients in float64; s = 0 gives zeros).
+__global__ void __launch_bounds__(256)
+k_prep_awq(const float* __restrict__ W, int K, int N, uint8_t* __restrict__ qweight,
+           uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  __shared__ float T[64][65];
+  const int n0 = blockIdx.x * 64, g = blockIdx.y, t = threadIdx.x;
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int kk = e >> 6, nn = e & 63;
+    T[nn][kk] = (n0 + nn < N) ? W[(size_t)(64 * g + kk) * N + n0 + nn] : 0.f;
+  }
+  __syncthreads();
+  if (t < 64 && n0 + t < N) {
+    const int n = n0 + t;
+    float mx = T[t][0], mn = T[t][0];
+    for (int kk = 1; kk < 64; ++kk) {
+      mx = fmaxf(mx, T[t][kk]);
+      mn = fminf(mn, T[t][kk]);
+    }
+    const uint32_t sb = f32_to_bf16_rne((mx - mn) / 15.0f);
+    const double s = (double)__uint_as_float(sb << 16);
+    const double z = s > 0.0 ? fmin(fmax(rint(-(double)mn / s), 0.0), 15.0) : 0.0;
+    scales[(size_t)n * (K / 64) + g] = (uint16_t)sb;
+    zeros[(size_t)n * (K / 64) + g] = (uint8_t)z;
+    uint8_t* dst = qweight + (size_t)n * (K / 2) + 32 * g;
+    for (int kk = 0; kk < 64; kk += 2) {
+      int q[2];
+      for (int u = 0; u < 2; ++u)
+        q[u] = s > 0.0 ? (int)fmin(fmax(rint((double)T[t][kk + u] / s) + z, 0.0), 15.0) : 0;
+      dst[kk / 2] = (uint8_t)(q[0] | (q[1] << 4));
+    }
+  }
+}
+
 size_t al(size_t b) { return (b + 255) & ~size_t(255); }
 
 // eigenvalues (kMaxL), then M1 [l][r] and M2 [r][l] with r <= 32
@@ -347,10 +444,11 @@ size_t prep_workspace_bytes(int64_t K, int64_t N, int rank, int l) {
          al(kSmallBytes) + al(K * rank * 8) + al(rank * N * 8) + al(K * N * 4) + al(256);
 }
 
-hipError_t launch_prep_int4(int K, int N, int rank, int l, int iters, const float* w,
-                            const uint16_t* xc, int64_t Mc, const double* omega, uint8_t* qweight,
-                            uint16_t* wscales, uint16_t* smooth, uint16_t* ldown, uint16_t* lup,
-                            float* residual, void* ws, int* fail_host, hipStream_t st) {
+hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, const float* w,
+                       const uint16_t* xc, int64_t Mc, const double* omega, uint8_t* qweight,
+                       void* wscales, uint16_t* smooth, uint16_t* ldown, uint16_t* lup,
+                       float* residual, void* ws, int* fail_host, float* globals_host,
+                       hipStream_t st) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   auto take = [&](size_t b) { uint8_t* q = p; p += al(b); return q; };
   double* wh = reinterpret_cast<double*>(take((size_t)K * N * 8));
@@ -366,8 +464,10 @@ hipError_t launch_prep_int4(int K, int N, int rank, int l, int iters, const floa
   double* L2 = reinterpret_cast<double*>(take((size_t)rank * N * 8));
   float* R = residual ? residual : reinterpret_cast<float*>(take((size_t)K * N * 4));
   if (residual) take((size_t)K * N * 4);
-  int* flags = reinterpret_cast<int*>(take(256));  // fail flag, signs
+  int* flags = reinterpret_cast<int*>(take(256));  // fail flag, signs, amax bits, globals
   int* sgn = flags + 1;
+  unsigned* amax = reinterpret_cast<unsigned*>(flags + 40);
+  float* globals = reinterpret_cast<float*>(flags + 42);
 
   auto gemm = [&](const double* A, int64_t as0, int64_t as1, const double* B, int64_t bs0,
                   int64_t bs1, double* C, int64_t ldc, int M, int Nn, int Kk) {
@@ -415,13 +515,35 @@ hipError_t launch_prep_int4(int K, int N, int rank, int l, int iters, const floa
   }
   hipLaunchKernelGGL(k_prep_residual, dim3((unsigned)((KN + 255) / 256)), dim3(256), 0, st, wh,
                      ldown, lup, K, N, rank, R);
-  hipLaunchKernelGGL(k_prep_quant, dim3((N + 63) / 64, K / 64), dim3(256), 0, st, R, K, N, qweight,
-                     wscales);
+  if (nvfp4) {
+    const unsigned gb = (unsigned)std::min<int64_t>((KN + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_prep_absmax, dim3(gb), dim3(256), 0, st, R, KN, amax);
+    const int64_t xn = Mc * K;
+    const unsigned gx = (unsigned)std::min<int64_t>((xn + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_prep_absmax_xhat, dim3(gx), dim3(256), 0, st, xc, xn, K, smooth, amax + 1);
+    hipLaunchKernelGGL(k_prep_globals, dim3(1), dim3(64), 0, st, amax, globals);
+    hipLaunchKernelGGL(k_prep_quant_nvfp4, dim3((N + 63) / 64, K / 64), dim3(256), 0, st, R, K, N,
+                       globals, qweight, static_cast<uint8_t*>(wscales));
+  } else {
+    hipLaunchKernelGGL(k_prep_quant, dim3((N + 63) / 64, K / 64), dim3(256), 0, st, R, K, N,
+                       qweight, static_cast<uint16_t*>(wscales));
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(fail_host, flags, sizeof(int), hipMemcpyDeviceToHost, st);
   if (e != hipSuccess) return e;
+  if (nvfp4) {
+    e = hipMemcpyAsync(globals_host, globals, 2 * sizeof(float), hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return e;
+  }
   return hipStreamSynchronize(st);
+}
+
+hipError_t launch_prep_awq(int K, int N, const float* w, uint8_t* qweight, uint16_t* scales,
+                           uint8_t* zeros, hipStream_t st) {
+  hipLaunchKernelGGL(k_prep_awq, dim3((N + 63) / 64, K / 64), dim3(256), 0, st, w, K, N, qweight,
+                     scales, zeros);
+  return hipGetLastError();
 }
 
 }  // namespace svdq

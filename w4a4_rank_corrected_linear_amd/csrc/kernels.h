@@ -82,16 +82,20 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
 
 hipError_t launch_gelu_bf16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t st);
 
-// Offline int4 weight preparation on the GPU (k_prep.hip): smoothing factors, the
+// Offline weight preparation on the GPU (k_prep.hip): smoothing factors, the
 // randomized top-rank factorization of the smoothed weight (l = rank + oversampling
-// columns, iters power iterations), the bf16 factors and the int4 residual.  Runs on
-// `st` and synchronizes it; *fail_host gets 0, or a nonzero code when the
-// orthonormalization or the small eigenproblem broke down.
+// columns, iters power iterations), the bf16 factors and the int4 or NVFP4 residual
+// (NVFP4: globals_host[0..1] = g_w, g_x).  Runs on `st` and synchronizes it;
+// *fail_host gets 0, or a nonzero code when the orthonormalization or the small
+// eigenproblem broke down.  launch_prep_awq: the AWQ W4A16 weights (asynchronous).
 size_t prep_workspace_bytes(int64_t K, int64_t N, int rank, int l);
-hipError_t launch_prep_int4(int K, int N, int rank, int l, int iters, const float* w,
-                            const uint16_t* xc, int64_t Mc, const double* omega, uint8_t* qweight,
-                            uint16_t* wscales, uint16_t* smooth, uint16_t* ldown, uint16_t* lup,
-                            float* residual, void* ws, int* fail_host, hipStream_t st);
+hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, const float* w,
+                       const uint16_t* xc, int64_t Mc, const double* omega, uint8_t* qweight,
+                       void* wscales, uint16_t* smooth, uint16_t* ldown, uint16_t* lup,
+                       float* residual, void* ws, int* fail_host, float* globals_host,
+                       hipStream_t st);
+hipError_t launch_prep_awq(int K, int N, const float* w, uint8_t* qweight, uint16_t* scales,
+                           uint8_t* zeros, hipStream_t st);
 
 // Per-head Q/K RMSNorm + rotary embedding on a bf16 [M][N] QKV output (N = 3 H 128);
 // the V third is copied when y != x.

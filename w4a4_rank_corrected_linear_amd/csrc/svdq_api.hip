@@ -472,46 +472,71 @@ size_t svdq_prepare_workspace_bytes(int64_t K, int64_t N, int32_t rank, int32_t 
   return svdq::prep_workspace_bytes(K, N, rank, rank + oversample);
 }
 
-svdq_status svdq_prepare_int4(int64_t K, int64_t N, int32_t rank, const float* w,
-                              const uint16_t* x_cal, int64_t Mc, const double* omega,
-                              int32_t oversample, int32_t power_iters, uint8_t* qweight,
-                              uint16_t* wscales, uint16_t* smooth, uint16_t* lora_down,
-                              uint16_t* lora_up, float* residual, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
-  if (!w || !x_cal || !qweight || !wscales || !smooth || !workspace)
-    return fail(SVDQ_ERR_NULL, "svdq_prepare_int4: NULL argument");
-  if (rank != 0 && rank != 16 && rank != 32)
-    return fail(SVDQ_ERR_CONFIG, "svdq_prepare_int4: rank %d unsupported (0, 16 or 32)", rank);
+svdq_status svdq_prepare_weight(const svdq_config* cfg, int64_t K, int64_t N, const float* w,
+                                const uint16_t* x_cal, int64_t Mc, const double* omega,
+                                int32_t oversample, int32_t power_iters, uint8_t* qweight,
+                                void* wscales, uint16_t* smooth, uint16_t* lora_down,
+                                uint16_t* lora_up, float* residual, float* w_global,
+                                float* act_global, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (!cfg || !w || !x_cal || !qweight || !wscales || !smooth || !workspace)
+    return fail(SVDQ_ERR_NULL, "svdq_prepare_weight: NULL argument");
+  SVDQ_TRY(check_svdq_config(cfg));
+  const bool nv = cfg->precision == SVDQ_NVFP4;
+  const int rank = cfg->rank;
+  if (nv && (!w_global || !act_global))
+    return fail(SVDQ_ERR_NULL, "svdq_prepare_weight: nvfp4 needs w_global and act_global");
   if (rank > 0 && (!omega || !lora_down || !lora_up))
-    return fail(SVDQ_ERR_NULL, "svdq_prepare_int4: rank %d needs omega, lora_down and lora_up",
+    return fail(SVDQ_ERR_NULL, "svdq_prepare_weight: rank %d needs omega, lora_down and lora_up",
                 rank);
   SVDQ_TRY(check_k(K));
   SVDQ_TRY(check_n(N));
   const int64_t l = rank + (int64_t)oversample;
   if (oversample < 0 || power_iters < 0 || power_iters > 64 || Mc < 1 || Mc > (int64_t(1) << 24) ||
       (rank > 0 && (l > 64 || l > std::min(K, N))))
-    return fail(SVDQ_ERR_SHAPE, "svdq_prepare_int4: need Mc >= 1, 0 <= power_iters <= 64 and "
+    return fail(SVDQ_ERR_SHAPE, "svdq_prepare_weight: need Mc >= 1, 0 <= power_iters <= 64 and "
                 "rank + oversample <= min(64, K, N)");
   if (!aligned16(w) || !aligned16(x_cal) || !aligned16(qweight) || !aligned16(wscales) ||
       !aligned16(smooth) || !aligned16(workspace) || (omega && !aligned16(omega)) ||
       (lora_down && !aligned16(lora_down)) || (lora_up && !aligned16(lora_up)) ||
       (residual && !aligned16(residual)))
-    return fail(SVDQ_ERR_ALIGN, "svdq_prepare_int4: pointers must be 16-byte aligned");
+    return fail(SVDQ_ERR_ALIGN, "svdq_prepare_weight: pointers must be 16-byte aligned");
   const size_t need = svdq::prep_workspace_bytes(K, N, rank, (int)l);
   if (workspace_bytes < need)
     return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 workspace_bytes, need);
   SVDQ_TRY(check_current_device());
   int failed = 0;
-  SVDQ_TRY(hip_check(svdq::launch_prep_int4((int)K, (int)N, rank, (int)l, power_iters, w, x_cal,
-                                             Mc, omega, qweight, wscales, smooth, lora_down,
-                                             lora_up, residual, workspace, &failed, stream),
+  float globals[2] = {1.0f, 1.0f};
+  SVDQ_TRY(hip_check(svdq::launch_prep(nv, (int)K, (int)N, rank, (int)l, power_iters, w, x_cal, Mc,
+                                        omega, qweight, wscales, smooth, lora_down, lora_up,
+                                        residual, workspace, &failed, globals, stream),
                      "weight preparation"));
   if (failed)
-    return fail(SVDQ_ERR_RANGE, "svdq_prepare_int4: the factorization broke down (%s); the "
+    return fail(SVDQ_ERR_RANGE, "svdq_prepare_weight: the factorization broke down (%s); the "
                 "smoothed weight may have rank below rank + oversample",
                 failed & 1 ? "Cholesky of a Gram matrix" : "non-positive singular value");
+  if (nv) {
+    if (!(globals[0] > 0.f) || !(globals[1] > 0.f))
+      return fail(SVDQ_ERR_RANGE, "svdq_prepare_weight: an all-zero residual or calibration "
+                  "set gives a zero NVFP4 tensor scale");
+    *w_global = globals[0];
+    *act_global = globals[1];
+  }
   return ok();
+}
+
+svdq_status awq_prepare_weight(int64_t K, int64_t N, const float* w, uint8_t* qweight,
+                               uint16_t* scales, uint8_t* zeros, hipStream_t stream) {
+  if (!w || !qweight || !scales || !zeros)
+    return fail(SVDQ_ERR_NULL, "awq_prepare_weight: NULL argument");
+  SVDQ_TRY(check_k(K));
+  SVDQ_TRY(check_n(N));
+  if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros))
+    return fail(SVDQ_ERR_ALIGN, "awq_prepare_weight: pointers must be 16-byte aligned");
+  SVDQ_TRY(check_current_device());
+  return hip_check(svdq::launch_prep_awq((int)K, (int)N, w, qweight, scales, zeros, stream),
+                   "awq weight preparation");
 }
 
 struct svdq_graph {
