@@ -152,3 +152,21 @@ def test_prepare_awq(K, N):
     assert np.array_equal(host_bits(qw), ref.qweight)
     assert np.array_equal(host_bits(sc), ref.scales)
     assert np.array_equal(host_bits(zs), ref.zeros)
+
+
+@pytest.mark.parametrize("precision", ["int4", "nvfp4"])
+def test_prepare_layer_wrapper(precision):
+    """svdq.prepare_layer: prepared and packed on the GPU, its output closer to the exact
+    X W than plain W4A4 (no smoothing, rank 0); svdq.prepare_awq_layer within the
+    tolerance of the oracle's AWQ linear on the oracle's AWQ weights (bit-exact weights)."""
+    li = I.layer_inputs(**I.TINY)
+    w = torch.from_numpy(np.ascontiguousarray(li.w, np.float32)).cuda()
+    layer = svdq.prepare_layer(w, dev_bf16(li.x_cal), dev_bf16(li.bias), precision=precision)
+    y = F.bf16_to_f64(host_bits(layer(dev_bf16(li.x))))
+    exact = F.bf16_to_f64(li.x) @ np.asarray(li.w, np.float64) + F.bf16_to_f64(li.bias)[None, :]
+    plain = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=0, precision=precision, smooth=False)
+    e_plain = np.linalg.norm(OL.w4a4_linear(precision, li.x, plain)["r"] - exact)
+    assert np.linalg.norm(y - exact) < e_plain
+    awq = svdq.prepare_awq_layer(w, dev_bf16(li.bias))
+    ref = P.prepare_awq(li.w, li.bias)
+    check_y(host_bits(awq(dev_bf16(li.x))), OL.awq_w4a16_linear(li.x, ref)["r"])

@@ -20,6 +20,8 @@ from .api import (  # noqa: F401
     gelu,
     pack_lora_down,
     pack_weight,
+    prepare_awq_layer,
+    prepare_layer,
     qk_norm_rope,
     quantize_act,
     timing_start,

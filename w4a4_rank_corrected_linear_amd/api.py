@@ -188,6 +188,53 @@ class SvdqLinear:
         return y
 
 
+def prepare_layer(w: torch.Tensor, x_cal: torch.Tensor, bias: torch.Tensor | None = None,
+                  precision: str = "int4", rank: int = 32, oversample: int = 16,
+                  power_iters: int = 8, seed: int = 0) -> "SvdqLinear":
+    """Prepare an svdq_w4a4 layer on the GPU (svdq_prepare_weight) from W [K, N] float32
+    (Y = X W) and calibration activations x_cal [Mc, K] bf16, then pack it: smoothing,
+    a randomized rank-r factorization (the Gaussian test matrix is drawn here with
+    torch's generator from ``seed``) and the quantized residual."""
+    _want(w, torch.float32, "w")
+    _want(x_cal, torch.bfloat16, "x_cal")
+    K, N = w.shape
+    dev = w.device
+    ell = rank + oversample
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    omega = torch.randn((N, ell), generator=gen, dtype=torch.float64).to(dev) if rank else None
+    nv = precision == "nvfp4"
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = (torch.empty((N, K // 16), dtype=torch.uint8, device=dev) if nv else
+              torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev))
+    smooth = torch.empty((K,), dtype=torch.bfloat16, device=dev)
+    ldown = torch.empty((rank, K), dtype=torch.bfloat16, device=dev) if rank else None
+    lup = torch.empty((N, rank), dtype=torch.bfloat16, device=dev) if rank else None
+    nbytes = int(L.lib().svdq_prepare_workspace_bytes(K, N, rank, oversample))
+    work = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    gw, gx = ctypes.c_float(1.0), ctypes.c_float(1.0)
+    cfg = L.config(precision, rank)
+    L.check(L.lib().svdq_prepare_weight(ctypes.byref(cfg), K, N, _p(w), _p(x_cal), x_cal.shape[0],
+                                        _p(omega), oversample, power_iters, _p(codes), _p(scales),
+                                        _p(smooth), _p(ldown), _p(lup), None, ctypes.byref(gw),
+                                        ctypes.byref(gx), _p(work), nbytes, _stream()),
+            "svdq_prepare_weight")
+    return SvdqLinear.from_interchange(codes, scales, smooth, ldown, lup, bias, precision,
+                                       w_global=gw.value, act_global=gx.value)
+
+
+def prepare_awq_layer(w: torch.Tensor, bias: torch.Tensor | None = None) -> "AwqLinear":
+    """AWQ W4A16 weights prepared on the GPU (awq_prepare_weight) from W [K, N] float32."""
+    _want(w, torch.float32, "w")
+    K, N = w.shape
+    dev = w.device
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((N, K // 64), dtype=torch.uint8, device=dev)
+    L.check(L.lib().awq_prepare_weight(K, N, _p(w), _p(q), _p(s), _p(z), _stream()),
+            "awq_prepare_weight")
+    return AwqLinear(q, s, z, bias)
+
+
 class AwqLinear:
     """An awq_w4a16 layer: qweight [N, K/2] u8, scales [N, K/64] bf16, zeros [N, K/64] u8."""
 
