@@ -474,13 +474,15 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
     dim3 grid((Nn + 63) / 64, (M + 63) / 64);
     hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, st, A, as0, as1, B, bs0, bs1, C, ldc, M, Nn, Kk);
   };
-  // orth(Y [n][l]) in place by CholeskyQR2
+  // orth(Y [n][l]) in place by CholeskyQR2; the first failed copy is kept in copy_err
+  hipError_t copy_err = hipSuccess;
   auto orth = [&](double* Yp, int n) {
     for (int pass = 0; pass < 2; ++pass) {
       gemm(Yp, 1, l, Yp, l, 1, G, l, l, l, n);                       // G = Y^T Y
       hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(256), 0, st, G, l, Rinv, flags);
       gemm(Yp, l, 1, Rinv, l, 1, Y2, l, n, l, l);                    // Y2 = Y R^-1
-      hipMemcpyAsync(Yp, Y2, (size_t)n * l * 8, hipMemcpyDeviceToDevice, st);
+      const hipError_t ce = hipMemcpyAsync(Yp, Y2, (size_t)n * l * 8, hipMemcpyDeviceToDevice, st);
+      if (copy_err == hipSuccess) copy_err = ce;
     }
   };
 
@@ -530,6 +532,7 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (copy_err != hipSuccess) return copy_err;
   e = hipMemcpyAsync(fail_host, flags, sizeof(int), hipMemcpyDeviceToHost, st);
   if (e != hipSuccess) return e;
   if (nvfp4) {
