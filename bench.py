@@ -401,6 +401,30 @@ PROFILE_CMDS = {
 }
 
 
+def summarize_stats(csv_dir: str, name: str, command: str, what: str) -> None:
+    """One rocprofv3 --kernel-trace --stats run (CSV under csv_dir) as a text summary
+    profiles/<name>_kernel_stats.txt: the kernel table with the command that made it
+    (host only, no GPU)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(os.path.join(csv_dir, "**/*kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics: {what}",
+             f"# command: {command}",
+             "# kernel                                        calls     avg_us     min_us     max_us   share_%"]
+    for r in csv.DictReader(open(files[0])):
+        nm = r["Name"].replace("(anonymous namespace)::", "")
+        nm = nm[: nm.index("(")] if "(" in nm else nm
+        lines.append(f"{nm[:46]:46s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} "
+                     f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
+                     f"{float(r['Percentage']):8.2f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{name}_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     """Turn the CSV output of the three rocprofv3 runs in PROFILE_CMDS (under
     out_dir) into the text summaries kept under profiles/ (host only, no GPU)."""
@@ -472,6 +496,9 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
 def main() -> int:
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
         summarize_profiles(sys.argv[2])
+        return 0
+    if len(sys.argv) == 6 and sys.argv[1] == "--summarize-stats":
+        summarize_stats(*sys.argv[2:6])
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
