@@ -21,6 +21,7 @@
 // bytes [M][K/16] and U [M][r].
 #include "common.h"
 #include "k1_batch.h"
+#include "k1_rows32.h"
 #include "nvfp4_device.h"
 #include "kernels.h"
 
@@ -42,7 +43,9 @@ struct QuantNvfp4Fused {
   }
 };
 
+// The two skeletons of the int4 quantizer, chosen the same way (k1_quant_int4.hip).
 __global__ void __launch_bounds__(256, 2) k1_nvfp4_fused(K1Args a) { k1_batch<QuantNvfp4Fused>(a); }
+__global__ void __launch_bounds__(768, 1) k1_nvfp4_fused32(K1Args a) { k1_rows32<QuantNvfp4Fused>(a); }
 
 struct K1Load {
   uint4 x[4];
@@ -177,8 +180,14 @@ hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const ui
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (fused) {
     K1Args a{x, M, K, smooth, ldown, rank, out, scales, uact, M_pad, g};
-    dim3 grid(M_pad / 16, k1_splits(K));
-    hipExtLaunchKernelGGL(k1_nvfp4_fused, grid, dim3(256), 0, st, ev0, ev1, 0, a);
+    const int splits = k1_splits(K);
+    if ((int64_t)(M_pad / 32) * splits <= device_cu_count()) {
+      hipExtLaunchKernelGGL(k1_nvfp4_fused32, dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0,
+                            st, ev0, ev1, 0, a);
+    } else {
+      hipExtLaunchKernelGGL(k1_nvfp4_fused, dim3(M_pad / 16, splits), dim3(256), 0, st, ev0, ev1, 0,
+                            a);
+    }
   } else {
     dim3 grid((M + 15) / 16);
     hipExtLaunchKernelGGL(k1_nvfp4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,
