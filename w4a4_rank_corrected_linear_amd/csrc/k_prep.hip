@@ -63,21 +63,25 @@ k_prep_what(const float* __restrict__ w, const uint16_t* __restrict__ m, double*
 // C[i][j] = sum_k A(i, k) B(k, j), float64, A(i, k) = A[i * as0 + k * as1],
 // B(k, j) = B[k * bs0 + j * bs1], C row-major with leading dimension ldc.  64 x 64
 // tiles, 16 values of k per step through LDS, 4 x 4 outputs per thread, k summed in
-// ascending order.
+// ascending order.  Workgroup z takes k in [z kc, (z + 1) kc) and writes its partial
+// product to C + z cz (one chunk: cz = 0, kc >= K).
 __global__ void __launch_bounds__(256)
 k_gemm_f64(const double* __restrict__ A, int64_t as0, int64_t as1, const double* __restrict__ B,
-           int64_t bs0, int64_t bs1, double* __restrict__ C, int64_t ldc, int M, int N, int K) {
+           int64_t bs0, int64_t bs1, double* __restrict__ C, int64_t ldc, int M, int N, int K,
+           int kc, int64_t cz) {
   __shared__ double As[16][65], Bs[16][65];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int kbeg = blockIdx.z * kc, kend = min(K, kbeg + kc);
+  C += blockIdx.z * cz;
   double c[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     for (int e = threadIdx.x; e < 16 * 64; e += 256) {
       const int kk = e >> 6, ii = e & 63;
       const int gi = i0 + ii, gk = k0 + kk;
-      As[kk][ii] = (gi < M && gk < K) ? A[gi * as0 + gk * as1] : 0.0;
+      As[kk][ii] = (gi < M && gk < kend) ? A[gi * as0 + gk * as1] : 0.0;
       const int gj = j0 + ii;
-      Bs[kk][ii] = (gj < N && gk < K) ? B[gk * bs0 + gj * bs1] : 0.0;
+      Bs[kk][ii] = (gj < N && gk < kend) ? B[gk * bs0 + gj * bs1] : 0.0;
     }
     __syncthreads();
 #pragma unroll
@@ -95,6 +99,16 @@ k_gemm_f64(const double* __restrict__ A, int64_t as0, int64_t as1, const double*
       const int gi = i0 + ty + 16 * a, gj = j0 + tx + 16 * b;
       if (gi < M && gj < N) C[gi * ldc + gj] = c[a][b];
     }
+}
+
+// C[i][j] = sum_z P[z][i][j] over nz partial products [M][N], z ascending.
+__global__ void __launch_bounds__(256)
+k_sum_parts(const double* __restrict__ P, int nz, int M, int N, double* __restrict__ C, int64_t ldc) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)M * N) return;
+  double v = 0.0;
+  for (int z = 0; z < nz; ++z) v += P[z * (int64_t)M * N + e];
+  C[(e / N) * ldc + e % N] = v;
 }
 
 // Cholesky G = R^T R of an l x l Gram matrix (one workgroup), then Rinv = R^-1 (upper
@@ -141,70 +155,94 @@ k_chol_inv(const double* __restrict__ G, int l, double* __restrict__ Rinv, int* 
   if (t == 0 && bad) atomicOr(fail, 1);
 }
 
-// Eigen-decomposition of a symmetric l x l matrix C (one workgroup) by cyclic Jacobi
-// rotations (Golub and Van Loan, Matrix Computations, the cyclic Jacobi method), pairs
-// (p, q) taken in row order, until the off-diagonal mass is below 1e-30 of the total.
-// Output: eigenvalues descending in ev[l], eigenvectors in the columns of V [l][l].
-__global__ void __launch_bounds__(64)
+// Eigen-decomposition of a symmetric l x l matrix C (one workgroup) by Jacobi
+// rotations in the parallel round-robin ordering (Brent and Luk, "The solution of
+// singular-value and symmetric eigenvalue problems on multiprocessor arrays", 1985;
+// Golub and Van Loan, Matrix Computations, parallel Jacobi): each sweep has n - 1
+// rounds of n / 2 disjoint pairs (n = l rounded up to even; pairs with the padding
+// index are skipped), whose rotations are computed from the same matrix and applied
+// together, columns then rows.  Sweeps stop once the off-diagonal mass is below 1e-30
+// of the total.  Output: eigenvalues descending in ev[l], eigenvectors in the columns
+// of V [l][l].
+__global__ void __launch_bounds__(256)
 k_jacobi(const double* __restrict__ C, int l, double* __restrict__ ev, double* __restrict__ V) {
   __shared__ double A[kMaxL][kMaxL + 1], Q[kMaxL][kMaxL + 1];
-  __shared__ double cs[2];
+  __shared__ double rc[kMaxL / 2], rs[kMaxL / 2];
+  __shared__ int rp[kMaxL / 2], rq[kMaxL / 2];
+  __shared__ double off, tot;
   const int t = threadIdx.x;
-  for (int e = t; e < l * l; e += 64) {
+  const int n = l + (l & 1), np = n / 2;
+  for (int e = t; e < l * l; e += 256) {
     A[e / l][e % l] = C[e];
     Q[e / l][e % l] = (e / l == e % l) ? 1.0 : 0.0;
   }
   __syncthreads();
   for (int sweep = 0; sweep < 40; ++sweep) {
-    __shared__ double off, tot;
     if (t == 0) {
-      double o = 0.0, s = 0.0;
+      double o = 0.0, sum = 0.0;
       for (int a = 0; a < l; ++a)
         for (int b = 0; b < l; ++b) {
           const double v = A[a][b] * A[a][b];
-          s += v;
+          sum += v;
           if (a != b) o += v;
         }
       off = o;
-      tot = s;
+      tot = sum;
     }
     __syncthreads();
     if (!(off > 1e-30 * tot)) break;
-    for (int p = 0; p < l - 1; ++p)
-      for (int q = p + 1; q < l; ++q) {
-        if (t == 0) {
+    for (int round = 0; round < n - 1; ++round) {
+      if (t < np) {
+        // players: position 0 fixed, positions 1 .. n-1 rotate; pair t = (pos t, pos n-1-t)
+        auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + round) % (n - 1); };
+        int p = player(t), q = player(n - 1 - t);
+        if (p > q) {
+          const int x = p;
+          p = q;
+          q = x;
+        }
+        double c = 1.0, sn = 0.0;
+        if (q < l && A[p][q] != 0.0) {
           const double apq = A[p][q];
-          double c = 1.0, s = 0.0;
-          if (apq != 0.0) {
-            const double theta = (A[q][q] - A[p][p]) / (2.0 * apq);
-            const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-            c = 1.0 / sqrt(tt * tt + 1.0);
-            s = tt * c;
-          }
-          cs[0] = c;
-          cs[1] = s;
+          const double theta = (A[q][q] - A[p][p]) / (2.0 * apq);
+          const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+          c = 1.0 / sqrt(tt * tt + 1.0);
+          sn = tt * c;
         }
-        __syncthreads();
-        const double c = cs[0], s = cs[1];
-        if (s != 0.0) {
-          // A = J^T A J, J the rotation in the (p, q) plane; Q = Q J
-          for (int k = t; k < l; k += 64) {
-            const double akp = A[k][p], akq = A[k][q];
-            A[k][p] = c * akp - s * akq;
-            A[k][q] = s * akp + c * akq;
-          }
-          __syncthreads();
-          for (int k = t; k < l; k += 64) {
-            const double apk = A[p][k], aqk = A[q][k];
-            A[p][k] = c * apk - s * aqk;
-            A[q][k] = s * apk + c * aqk;
-            const double qkp = Q[k][p], qkq = Q[k][q];
-            Q[k][p] = c * qkp - s * qkq;
-            Q[k][q] = s * qkp + c * qkq;
-          }
-        }
-        __syncthreads();
+        rp[t] = p;
+        rq[t] = q < l ? q : p;  // a skipped pair rotates nothing
+        rc[t] = c;
+        rs[t] = q < l ? sn : 0.0;
       }
+      __syncthreads();
+      // columns: A = A J, Q = Q J
+      for (int e = t; e < np * l; e += 256) {
+        const int i = e / l, k = e % l;
+        const double c = rc[i], sn = rs[i];
+        if (sn != 0.0) {
+          const int p = rp[i], q = rq[i];
+          const double akp = A[k][p], akq = A[k][q];
+          A[k][p] = c * akp - sn * akq;
+          A[k][q] = sn * akp + c * akq;
+          const double qkp = Q[k][p], qkq = Q[k][q];
+          Q[k][p] = c * qkp - sn * qkq;
+          Q[k][q] = sn * qkp + c * qkq;
+        }
+      }
+      __syncthreads();
+      // rows: A = J^T A
+      for (int e = t; e < np * l; e += 256) {
+        const int i = e / l, k = e % l;
+        const double c = rc[i], sn = rs[i];
+        if (sn != 0.0) {
+          const int p = rp[i], q = rq[i];
+          const double apk = A[p][k], aqk = A[q][k];
+          A[p][k] = c * apk - sn * aqk;
+          A[q][k] = sn * apk + c * aqk;
+        }
+      }
+      __syncthreads();
+    }
   }
   // sort descending (selection, one thread), move vectors along
   if (t == 0) {
@@ -436,12 +474,15 @@ size_t al(size_t b) { return (b + 255) & ~size_t(255); }
 
 // eigenvalues (kMaxL), then M1 [l][r] and M2 [r][l] with r <= 32
 constexpr size_t kSmallBytes = (kMaxL + 2 * kMaxL * 32) * 8;
+// partial products of the GEMMs that have few output tiles (split along k)
+constexpr size_t kPartBytes = size_t(8) << 20;
 
 }  // namespace
 
 size_t prep_workspace_bytes(int64_t K, int64_t N, int rank, int l) {
   return al(K * N * 8) + al(K * l * 8) * 2 + al(N * l * 8) + al(l * N * 8) + 3 * al(64 * 64 * 8) +
-         al(kSmallBytes) + al(K * rank * 8) + al(rank * N * 8) + al(K * N * 4) + al(256);
+         al(kSmallBytes) + al(K * rank * 8) + al(rank * N * 8) + al(K * N * 4) + al(256) +
+         al(kPartBytes);
 }
 
 hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, const float* w,
@@ -464,15 +505,34 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
   double* L2 = reinterpret_cast<double*>(take((size_t)rank * N * 8));
   float* R = residual ? residual : reinterpret_cast<float*>(take((size_t)K * N * 4));
   if (residual) take((size_t)K * N * 4);
+  double* parts = reinterpret_cast<double*>(take(kPartBytes));
   int* flags = reinterpret_cast<int*>(take(256));  // fail flag, signs, amax bits, globals
   int* sgn = flags + 1;
   unsigned* amax = reinterpret_cast<unsigned*>(flags + 40);
   float* globals = reinterpret_cast<float*>(flags + 42);
 
+  // a product with fewer than 128 output tiles is split along k into nz chunks (at most
+  // 64, at least 64 values of k each, partials within kPartBytes), summed in order
   auto gemm = [&](const double* A, int64_t as0, int64_t as1, const double* B, int64_t bs0,
                   int64_t bs1, double* C, int64_t ldc, int M, int Nn, int Kk) {
-    dim3 grid((Nn + 63) / 64, (M + 63) / 64);
-    hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, st, A, as0, as1, B, bs0, bs1, C, ldc, M, Nn, Kk);
+    const int tiles = ((Nn + 63) / 64) * ((M + 63) / 64);
+    int nz = 1;
+    if (tiles < 128)
+      nz = (int)std::max<int64_t>(1, std::min<int64_t>({64, Kk / 64, (int64_t)(kPartBytes / 8) / ((int64_t)M * Nn)}));
+    if (nz <= 1) {
+      dim3 grid((Nn + 63) / 64, (M + 63) / 64);
+      hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, st, A, as0, as1, B, bs0, bs1, C, ldc, M, Nn,
+                         Kk, Kk, (int64_t)0);
+      return;
+    }
+    const int kc = ((Kk + nz - 1) / nz + 15) / 16 * 16;
+    nz = (Kk + kc - 1) / kc;
+    dim3 grid((Nn + 63) / 64, (M + 63) / 64, nz);
+    hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, st, A, as0, as1, B, bs0, bs1, parts,
+                       (int64_t)Nn, M, Nn, Kk, kc, (int64_t)M * Nn);
+    const int64_t mn = (int64_t)M * Nn;
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st, parts, nz,
+                       M, Nn, C, ldc);
   };
   // orth(Y [n][l]) in place by CholeskyQR2; the first failed copy is kept in copy_err
   hipError_t copy_err = hipSuccess;
@@ -506,7 +566,7 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
     double* ev = small;
     double* M1 = small + kMaxL;
     double* M2 = small + kMaxL + kMaxL * 32;
-    hipLaunchKernelGGL(k_jacobi, dim3(1), dim3(64), 0, st, G, l, ev, Vv);
+    hipLaunchKernelGGL(k_jacobi, dim3(1), dim3(256), 0, st, G, l, ev, Vv);
     hipLaunchKernelGGL(k_prep_small, dim3(1), dim3(256), 0, st, ev, Vv, l, rank, M1, M2, flags);
     gemm(Y, l, 1, M1, rank, 1, L1, rank, K, rank, l);                // L1 = Q Ub_r S_r
     gemm(M2, l, 1, Bm, N, 1, L2, N, rank, N, l);                     // L2 = S_r^-1 Ub_r^T B
