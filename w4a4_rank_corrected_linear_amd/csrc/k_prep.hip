@@ -40,13 +40,33 @@ namespace {
 
 constexpr int kMaxL = 64;  // l = rank + oversampling
 
-// m_k from the calibration activations, one thread per channel (coalesced over k).
+// Channel amax of the calibration activations over the rows [z rc, (z + 1) rc) of chunk
+// z = blockIdx.y: two channels per thread (32-bit loads, coalesced over k), written to
+// part[z][K].  K is even.
 __global__ void __launch_bounds__(256)
-k_prep_smooth(const uint16_t* __restrict__ xc, int64_t Mc, int K, uint16_t* __restrict__ m) {
+k_prep_amax_part(const uint16_t* __restrict__ xc, int64_t Mc, int K, int64_t rc,
+                 float* __restrict__ part) {
+  const int k = 2 * (blockIdx.x * 256 + threadIdx.x);
+  if (k >= K) return;
+  const int64_t r0 = blockIdx.y * rc, r1 = min(Mc, r0 + rc);
+  float a0 = 0.f, a1 = 0.f;
+  for (int64_t i = r0; i < r1; ++i) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(xc + i * K + k);
+    a0 = fmaxf(a0, fabsf(bf16_to_f32(v & 0xFFFFu)));
+    a1 = fmaxf(a1, fabsf(bf16_to_f32(v >> 16)));
+  }
+  part[(int64_t)blockIdx.y * K + k] = a0;
+  part[(int64_t)blockIdx.y * K + k + 1] = a1;
+}
+
+// m_k = bf16(1 / sqrt(max(amax_k, 1e-5))) from the nz chunk maxima (a maximum does not
+// depend on the order it is taken in).
+__global__ void __launch_bounds__(256)
+k_prep_smooth(const float* __restrict__ part, int nz, int K, uint16_t* __restrict__ m) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k >= K) return;
   float a = 0.f;
-  for (int64_t i = 0; i < Mc; ++i) a = fmaxf(a, fabsf(bf16_to_f32(xc[i * K + k])));
+  for (int z = 0; z < nz; ++z) a = fmaxf(a, part[(int64_t)z * K + k]);
   const double lam = sqrt(fmax((double)a, 1e-5));
   m[k] = (uint16_t)f32_to_bf16_rne((float)(1.0 / lam));
 }
@@ -111,48 +131,54 @@ k_sum_parts(const double* __restrict__ P, int nz, int M, int N, double* __restri
   C[(e / N) * ldc + e % N] = v;
 }
 
-// Cholesky G = R^T R of an l x l Gram matrix (one workgroup), then Rinv = R^-1 (upper
-// triangular).  A non-positive pivot sets *fail and leaves Rinv = I.
-__global__ void __launch_bounds__(256)
+// Lane `src` of v, broadcast to the wave (src a compile-time constant in the unrolled
+// loops below).
+__device__ __forceinline__ double lane_bcast(double v, int src) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Cholesky G = R^T R of an l x l Gram matrix, then Rinv = R^-1 (upper triangular), in
+// one wave with lane c holding column c in registers.  The matrix is padded to LP >= l
+// with an identity block, which factors to itself and leaves R and R^-1 of G unchanged.
+// Right-looking factorization: at step j the pivot comes from lane j, row j of R is each
+// lane's element j over the pivot, and the trailing matrix loses R[j][b] R[j][c]
+// (R[j][b] broadcast from lane b).  The inverse overwrites column c from the bottom:
+// X[i][c] = (delta_ic - sum_{k>i} R[i][k] X[k][c]) / R[i][i], R[i][k] broadcast from lane
+// k, which still holds row i of R at that point; entries below the diagonal come out
+// zero.  A non-positive pivot sets *fail (and is replaced by 1 so the kernel finishes).
+template <int LP>
+__global__ void __launch_bounds__(64)
 k_chol_inv(const double* __restrict__ G, int l, double* __restrict__ Rinv, int* __restrict__ fail) {
-  __shared__ double R[kMaxL][kMaxL + 1], X[kMaxL][kMaxL + 1];
-  __shared__ int bad;
-  const int t = threadIdx.x;
-  if (t == 0) bad = 0;
-  for (int e = t; e < l * l; e += 256) {
-    R[e / l][e % l] = G[e];
-    X[e / l][e % l] = (e / l == e % l) ? 1.0 : 0.0;
+  const int c = threadIdx.x;
+  double a[LP];
+#pragma unroll
+  for (int i = 0; i < LP; ++i) a[i] = (c < l && i < l) ? G[i * l + c] : (i == c ? 1.0 : 0.0);
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < LP; ++j) {
+    const double d = lane_bcast(a[j], j);
+    bad |= !(d > 0.0);
+    const double piv = d > 0.0 ? sqrt(d) : 1.0;
+    const double r = c == j ? piv : a[j] / piv;
+    a[j] = r;
+#pragma unroll
+    for (int b = j + 1; b < LP; ++b) a[b] = fma(-lane_bcast(r, b), r, a[b]);
   }
-  __syncthreads();
-  // right-looking: row j of R from the trailing matrix
-  for (int j = 0; j < l; ++j) {
-    if (t == 0) {
-      const double d = R[j][j];
-      if (!(d > 0.0)) bad = 1;
-      R[j][j] = d > 0.0 ? sqrt(d) : 1.0;
-    }
-    __syncthreads();
-    const double piv = R[j][j];
-    for (int c = j + 1 + t; c < l; c += 256) R[j][c] /= piv;
-    __syncthreads();
-    for (int e = t; e < (l - j - 1) * (l - j - 1); e += 256) {
-      const int a = j + 1 + e / (l - j - 1), b = j + 1 + e % (l - j - 1);
-      if (b >= a) R[a][b] -= R[j][a] * R[j][b];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int i = LP - 1; i >= 0; --i) {
+    double v = i == c ? 1.0 : 0.0;
+#pragma unroll
+    for (int k = i + 1; k < LP; ++k) v = fma(-lane_bcast(a[i], k), a[k], v);
+    a[i] = v / lane_bcast(a[i], i);
   }
-  // X = R^-1 by back substitution, one column of X per thread
-  for (int c = t; c < l; c += 256) {
-    for (int i = c; i >= 0; --i) {
-      double v = (i == c) ? 1.0 : 0.0;
-      for (int k = i + 1; k <= c; ++k) v -= R[i][k] * X[k][c];
-      X[i][c] = v / R[i][i];
-    }
-    for (int i = c + 1; i < l; ++i) X[i][c] = 0.0;
-  }
-  __syncthreads();
-  for (int e = t; e < l * l; e += 256) Rinv[e] = X[e / l][e % l];
-  if (t == 0 && bad) atomicOr(fail, 1);
+  if (c < l)
+#pragma unroll
+    for (int i = 0; i < LP; ++i)
+      if (i < l) Rinv[i * l + c] = a[i];
+  if (c == 0 && bad) atomicOr(fail, 1);
 }
 
 // Eigen-decomposition of a symmetric l x l matrix C (one workgroup) by Jacobi
@@ -539,7 +565,14 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
   auto orth = [&](double* Yp, int n) {
     for (int pass = 0; pass < 2; ++pass) {
       gemm(Yp, 1, l, Yp, l, 1, G, l, l, l, n);                       // G = Y^T Y
-      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(256), 0, st, G, l, Rinv, flags);
+      if (l <= 16)
+        hipLaunchKernelGGL(k_chol_inv<16>, dim3(1), dim3(64), 0, st, G, l, Rinv, flags);
+      else if (l <= 32)
+        hipLaunchKernelGGL(k_chol_inv<32>, dim3(1), dim3(64), 0, st, G, l, Rinv, flags);
+      else if (l <= 48)
+        hipLaunchKernelGGL(k_chol_inv<48>, dim3(1), dim3(64), 0, st, G, l, Rinv, flags);
+      else
+        hipLaunchKernelGGL(k_chol_inv<64>, dim3(1), dim3(64), 0, st, G, l, Rinv, flags);
       gemm(Yp, l, 1, Rinv, l, 1, Y2, l, n, l, l);                    // Y2 = Y R^-1
       const hipError_t ce = hipMemcpyAsync(Yp, Y2, (size_t)n * l * 8, hipMemcpyDeviceToDevice, st);
       if (copy_err == hipSuccess) copy_err = ce;
@@ -548,7 +581,16 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
 
   hipError_t e = hipMemsetAsync(flags, 0, 256, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_prep_smooth, dim3((K + 255) / 256), dim3(256), 0, st, xc, Mc, K, smooth);
+  {  // channel amax in row chunks of at least 64 (at most 128 chunks, within kPartBytes)
+    float* part = reinterpret_cast<float*>(parts);
+    const int64_t nzmax = std::max<int64_t>(1, std::min<int64_t>(128, (int64_t)(kPartBytes / 4) / K));
+    const int64_t nz0 = std::max<int64_t>(1, std::min<int64_t>(nzmax, (Mc + 63) / 64));
+    const int64_t rc = std::max<int64_t>(1, (Mc + nz0 - 1) / nz0);
+    const int nz = (int)std::max<int64_t>(1, (Mc + rc - 1) / rc);
+    hipLaunchKernelGGL(k_prep_amax_part, dim3((K / 2 + 255) / 256, nz), dim3(256), 0, st, xc, Mc, K,
+                       rc, part);
+    hipLaunchKernelGGL(k_prep_smooth, dim3((K + 255) / 256), dim3(256), 0, st, part, nz, K, smooth);
+  }
   const int64_t KN = (int64_t)K * N;
   hipLaunchKernelGGL(k_prep_what, dim3((unsigned)((KN + 255) / 256)), dim3(256), 0, st, w, smooth,
                      wh, K, N);
