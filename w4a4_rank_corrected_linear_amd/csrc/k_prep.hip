@@ -145,13 +145,14 @@ __device__ __forceinline__ double lane_bcast(double v, int src) {
 // with an identity block, which factors to itself and leaves R and R^-1 of G unchanged.
 // Right-looking factorization: at step j the pivot comes from lane j, row j of R is each
 // lane's element j over the pivot, and the trailing matrix loses R[j][b] R[j][c]
-// (R[j][b] broadcast from lane b).  The inverse overwrites column c from the bottom:
-// X[i][c] = (delta_ic - sum_{k>i} R[i][k] X[k][c]) / R[i][i], R[i][k] broadcast from lane
-// k, which still holds row i of R at that point; entries below the diagonal come out
-// zero.  A non-positive pivot sets *fail (and is replaced by 1 so the kernel finishes).
+// (row j of R staged in LDS and read back as broadcasts).  The inverse overwrites column
+// c from the bottom: X[i][c] = (delta_ic - sum_{k>i} R[i][k] X[k][c]) / R[i][i], row i of
+// R staged in LDS the same way before column c's element i is replaced; entries below the
+// diagonal come out zero.  A non-positive pivot sets *fail (and is replaced by 1 so the kernel finishes).
 template <int LP>
 __global__ void __launch_bounds__(64)
 k_chol_inv(const double* __restrict__ G, int l, double* __restrict__ Rinv, int* __restrict__ fail) {
+  __shared__ double row[LP];
   const int c = threadIdx.x;
   double a[LP];
 #pragma unroll
@@ -164,15 +165,21 @@ k_chol_inv(const double* __restrict__ G, int l, double* __restrict__ Rinv, int* 
     const double piv = d > 0.0 ? sqrt(d) : 1.0;
     const double r = c == j ? piv : a[j] / piv;
     a[j] = r;
+    if (c < LP) row[c] = r;
+    __syncthreads();
 #pragma unroll
-    for (int b = j + 1; b < LP; ++b) a[b] = fma(-lane_bcast(r, b), r, a[b]);
+    for (int b = j + 1; b < LP; ++b) a[b] = fma(-row[b], r, a[b]);
+    __syncthreads();
   }
 #pragma unroll
   for (int i = LP - 1; i >= 0; --i) {
+    if (c < LP) row[c] = a[i];
+    __syncthreads();
     double v = i == c ? 1.0 : 0.0;
 #pragma unroll
-    for (int k = i + 1; k < LP; ++k) v = fma(-lane_bcast(a[i], k), a[k], v);
-    a[i] = v / lane_bcast(a[i], i);
+    for (int k = i + 1; k < LP; ++k) v = fma(-row[k], a[k], v);
+    a[i] = v / row[i];
+    __syncthreads();
   }
   if (c < l)
 #pragma unroll
@@ -195,7 +202,7 @@ k_jacobi(const double* __restrict__ C, int l, double* __restrict__ ev, double* _
   __shared__ double A[kMaxL][kMaxL + 1], Q[kMaxL][kMaxL + 1];
   __shared__ double rc[kMaxL / 2], rs[kMaxL / 2];
   __shared__ int rp[kMaxL / 2], rq[kMaxL / 2];
-  __shared__ double off, tot;
+  __shared__ double roff[256], rtot[256];
   const int t = threadIdx.x;
   const int n = l + (l & 1), np = n / 2;
   for (int e = t; e < l * l; e += 256) {
@@ -204,19 +211,28 @@ k_jacobi(const double* __restrict__ C, int l, double* __restrict__ ev, double* _
   }
   __syncthreads();
   for (int sweep = 0; sweep < 40; ++sweep) {
-    if (t == 0) {
+    {  // off-diagonal and total squared mass: strided partial sums, then a tree
       double o = 0.0, sum = 0.0;
-      for (int a = 0; a < l; ++a)
-        for (int b = 0; b < l; ++b) {
-          const double v = A[a][b] * A[a][b];
-          sum += v;
-          if (a != b) o += v;
+      for (int e = t; e < l * l; e += 256) {
+        const int a = e / l, b = e % l;
+        const double v = A[a][b] * A[a][b];
+        sum += v;
+        if (a != b) o += v;
+      }
+      roff[t] = o;
+      rtot[t] = sum;
+      __syncthreads();
+      for (int h = 128; h > 0; h >>= 1) {
+        if (t < h) {
+          roff[t] += roff[t + h];
+          rtot[t] += rtot[t + h];
         }
-      off = o;
-      tot = sum;
+        __syncthreads();
+      }
     }
+    const bool done = !(roff[0] > 1e-30 * rtot[0]);
     __syncthreads();
-    if (!(off > 1e-30 * tot)) break;
+    if (done) break;
     for (int round = 0; round < n - 1; ++round) {
       if (t < np) {
         // players: position 0 fixed, positions 1 .. n-1 rotate; pair t = (pos t, pos n-1-t)
@@ -242,8 +258,7 @@ k_jacobi(const double* __restrict__ C, int l, double* __restrict__ ev, double* _
       }
       __syncthreads();
       // columns: A = A J, Q = Q J
-      for (int e = t; e < np * l; e += 256) {
-        const int i = e / l, k = e % l;
+      for (int i = t >> 6, k = t & 63; i < np && k < l; i += 4) {
         const double c = rc[i], sn = rs[i];
         if (sn != 0.0) {
           const int p = rp[i], q = rq[i];
@@ -257,8 +272,7 @@ k_jacobi(const double* __restrict__ C, int l, double* __restrict__ ev, double* _
       }
       __syncthreads();
       // rows: A = J^T A
-      for (int e = t; e < np * l; e += 256) {
-        const int i = e / l, k = e % l;
+      for (int i = t >> 6, k = t & 63; i < np && k < l; i += 4) {
         const double c = rc[i], sn = rs[i];
         if (sn != 0.0) {
           const int p = rp[i], q = rq[i];
@@ -358,17 +372,39 @@ k_prep_factors(const double* __restrict__ L1, const double* __restrict__ L2,
 
 // R[k][n] = What[k][n] - sum_j L1_bf16[k][j] L2_bf16[j][n] (float64, j ascending),
 // stored as float32.
+// R[k][n] = fl32(What[k][n] - sum_j L1b[k][j] L2b[j][n]) with the bf16 factors (j
+// ascending), r <= 32.  One workgroup per 64 x 64 block of [K][N]: the factor slices go
+// through LDS as float64, thread t takes column nn = t % 64 and the rows t / 64 + 4 a.
 __global__ void __launch_bounds__(256)
 k_prep_residual(const double* __restrict__ wh, const uint16_t* __restrict__ ldown,
                 const uint16_t* __restrict__ lup, int K, int N, int r, float* __restrict__ R) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)K * N) return;
-  const int k = (int)(i / N), n = (int)(i % N);
-  double acc = 0.0;
-  for (int j = 0; j < r; ++j)
-    acc = fma((double)bf16_to_f32(ldown[(size_t)j * K + k]), (double)bf16_to_f32(lup[(size_t)n * r + j]),
-              acc);
-  R[i] = (float)(wh[i] - acc);
+  __shared__ double Ld[32][64], Lu[32][65];
+  const int t = threadIdx.x, n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  for (int e = t; e < r * 64; e += 256) {
+    const int j = e >> 6, x = e & 63;
+    Ld[j][x] = k0 + x < K ? (double)bf16_to_f32(ldown[(size_t)j * K + k0 + x]) : 0.0;
+  }
+  for (int e = t; e < r * 64; e += 256) {
+    const int x = e / r, j = e % r;
+    Lu[j][x] = n0 + x < N ? (double)bf16_to_f32(lup[(size_t)(n0 + x) * r + j]) : 0.0;
+  }
+  __syncthreads();
+  const int nn = t & 63, kq = t >> 6;
+  double acc[16] = {};
+  for (int j = 0; j < r; ++j) {
+    const double u = Lu[j][nn];
+#pragma unroll
+    for (int a = 0; a < 16; ++a) acc[a] = fma(Ld[j][kq + 4 * a], u, acc[a]);
+  }
+  if (n0 + nn >= N) return;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) {
+    const int k = k0 + kq + 4 * a;
+    if (k < K) {
+      const size_t i = (size_t)k * N + n0 + nn;
+      R[i] = (float)(wh[i] - acc[a]);
+    }
+  }
 }
 
 // int4 quantization of R per output column n and group g of 64 values of k: one
@@ -617,7 +653,7 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
     hipLaunchKernelGGL(k_prep_factors, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, st, L1,
                        L2, sgn, K, N, rank, ldown, lup);
   }
-  hipLaunchKernelGGL(k_prep_residual, dim3((unsigned)((KN + 255) / 256)), dim3(256), 0, st, wh,
+  hipLaunchKernelGGL(k_prep_residual, dim3((N + 63) / 64, (K + 63) / 64), dim3(256), 0, st, wh,
                      ldown, lup, K, N, rank, R);
   if (nvfp4) {
     const unsigned gb = (unsigned)std::min<int64_t>((KN + 255) / 256, 1024);
