@@ -127,6 +127,7 @@ k_sum_parts(const double* __restrict__ P, int nz, int M, int N, double* __restri
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (int64_t)M * N) return;
   double v = 0.0;
+#pragma unroll 8
   for (int z = 0; z < nz; ++z) v += P[z * (int64_t)M * N + e];
   C[(e / N) * ldc + e % N] = v;
 }
@@ -542,7 +543,7 @@ constexpr size_t kPartBytes = size_t(8) << 20;
 }  // namespace
 
 size_t prep_workspace_bytes(int64_t K, int64_t N, int rank, int l) {
-  return al(K * N * 8) + al(K * l * 8) * 2 + al(N * l * 8) + al(l * N * 8) + 3 * al(64 * 64 * 8) +
+  return al(K * N * 8) + al(K * l * 8) + al(std::max(K, N) * l * 8) + al(N * l * 8) + al(l * N * 8) + 3 * al(64 * 64 * 8) +
          al(kSmallBytes) + al(K * rank * 8) + al(rank * N * 8) + al(K * N * 4) + al(256) +
          al(kPartBytes);
 }
@@ -556,7 +557,8 @@ hipError_t launch_prep(bool nvfp4, int K, int N, int rank, int l, int iters, con
   auto take = [&](size_t b) { uint8_t* q = p; p += al(b); return q; };
   double* wh = reinterpret_cast<double*>(take((size_t)K * N * 8));
   double* Y = reinterpret_cast<double*>(take((size_t)K * l * 8));
-  double* Y2 = reinterpret_cast<double*>(take((size_t)K * l * 8));
+  // the CholeskyQR2 output, for Y [K][l] and Z [N][l]
+  double* Y2 = reinterpret_cast<double*>(take((size_t)std::max(K, N) * l * 8));
   double* Z = reinterpret_cast<double*>(take((size_t)N * l * 8));
   double* Bm = reinterpret_cast<double*>(take((size_t)l * N * 8));
   double* G = reinterpret_cast<double*>(take(64 * 64 * 8));
