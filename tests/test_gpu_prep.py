@@ -95,9 +95,11 @@ def test_prepare_tiny(rank):
     check_prepared(li.w, li.x_cal, g, ref, rank)
 
 
-def test_prepare_rectangular_with_outliers():
-    """K = 1024, N = 1536 with 1 % outlier channels x30 in the calibration data."""
-    li = I.layer_inputs(config_id=2, M=64, K=1024, N=1536, cal_rows=512)
+@pytest.mark.parametrize("K,N", [(1024, 1536), (1536, 1024)])
+def test_prepare_rectangular_with_outliers(K, N):
+    """Wide and tall weights (the orthogonalization runs on K and on N rows) with 1 %
+    outlier channels x30 in the calibration data."""
+    li = I.layer_inputs(config_id=2, M=64, K=K, N=N, cal_rows=512)
     ref = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=32)
     g = gpu_prepare(li.w, li.x_cal, rank=32)
     check_prepared(li.w, li.x_cal, g, ref, 32)
