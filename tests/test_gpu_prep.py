@@ -37,7 +37,9 @@ def gpu_prepare(w, x_cal, rank=32, oversample=16, iters=8, seed=7, precision="in
     lu = torch.empty((N, max(rank, 1)), dtype=torch.bfloat16, device=dev)
     res = torch.empty((K, N), dtype=torch.float32, device=dev)
     nbytes = L.svdq_prepare_workspace_bytes(K, N, rank, oversample)
-    work = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    # the workspace as sized, followed by a guard region the call must leave alone
+    guard = 1 << 20
+    work = torch.full((nbytes + guard,), 0xA5, dtype=torch.uint8, device=dev)
     gw, gx = ctypes.c_float(0.0), ctypes.c_float(0.0)
     cfg = svdq._lib.config(precision, rank)
     st = L.svdq_prepare_weight(ctypes.byref(cfg), K, N, w_d.data_ptr(), xc_d.data_ptr(),
@@ -47,6 +49,7 @@ def gpu_prepare(w, x_cal, rank=32, oversample=16, iters=8, seed=7, precision="in
                                res.data_ptr(), ctypes.byref(gw), ctypes.byref(gx), work.data_ptr(),
                                nbytes, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     svdq._lib.check(st, "svdq_prepare_weight")
+    assert bool((work[nbytes:] == 0xA5).all()), "svdq_prepare_weight wrote past its workspace"
     out = dict(qweight=host_bits(qw), wscales=host_bits(ws_), smooth=host_bits(sm),
                residual=res.cpu().numpy(), w_global=gw.value, act_global=gx.value)
     if rank:
