@@ -171,9 +171,13 @@ def test_workspace_holds_exact_dequantized_activations(tiny):
     li, layer = tiny
     M = 200
     dl = _layer_dev(layer)
-    ws = torch.zeros(dl.workspace(M, torch.device("cuda")).numel(), dtype=torch.uint8, device="cuda")
+    # the workspace as sized, followed by a guard region the call must leave alone
+    need = dl.workspace_bytes(M)
+    buf = torch.full((need + (1 << 20),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = buf[:need]
     dl(dev_bf16(li.x[:M]), workspace=ws)
     torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "the NVFP4 linear wrote past its workspace"
     ref = Q.quantize_act_nvfp4(li.x[:M], layer.smooth, layer.act_global, layer.lora_down)
     w = host_bits(ws)
     M_pad, K = 256, layer.K
