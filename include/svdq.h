@@ -102,7 +102,8 @@ svdq_status svdq_check_device(int hip_device);
  *          FP6 MFMA reads, chunks of 1536 bytes per 32 output columns and 64-group),
  *          scales round_up(K/128 * N * 8, 256) + 256 ([K/128][N] 8-byte records
  *          {scale of group 2p, scale of group 2p+1, 0, 0} in bf16: the rescale MFMA's
- *          operand as stored, one record per pair of groups; range flag)
+ *          operand as stored, one record per pair of groups; a 256-byte trailer the
+ *          pack clears)
  *   nvfp4: codes N*K*2 (exact dequantized bf16 [N][K]), scales 256 (range flag) */
 size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
                                 size_t* codes_bytes, size_t* scales_bytes);
@@ -112,8 +113,9 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
  *                          nvfp4: E2M1 nibbles, same order
  *   scales       [N][K/G]  int4: bf16; nvfp4: E4M3 bytes
  *   packed_codes, packed_scales: buffers of svdq_packed_weight_bytes()
- * int4 codes must lie in the symmetric range [-7, 7] (what the layer's
- * quantizer produces); a -8 code makes the call return SVDQ_ERR_RANGE.  This
+ * int4 codes may take every value of the 4-bit two's complement range [-8, 7]
+ * (each is an exact E2M3 operand value q/8 of the GEMM).  An nvfp4 scale byte that is
+ * an E4M3 NaN (0x7F or 0xFF) makes the call return SVDQ_ERR_RANGE.  This
  * is an offline step: it synchronizes `stream` before returning. */
 svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N,
                              const uint8_t* codes, const void* scales,
@@ -145,7 +147,8 @@ size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);
  *   scales     [M][K/G] out: bf16 (int4) or E4M3 bytes (nvfp4)
  *   lora_act   [M][r] out: U = xhat @ lora_down^T, fp32 (NULL iff r == 0); U is
  *              accumulated in fp32 and kept unrounded for the up projection
- * int4: s = bf16(amax/7) per 64-group, q = round-half-even(xhat/s) in [-7, 7].
+ * int4: s = bf16(amax/7) per 64-group, q = round-half-even(xhat/s) clamped to the
+ * int4 range [-8, 7] (only a subnormal bf16 s lets a quotient leave [-7.5, 7.5]).
  * nvfp4: s = E4M3(amax / (6 g_x)) per 16-block, code = E2M1(xhat / (s g_x)). */
 svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
                               const uint16_t* smooth, const uint16_t* lora_down, float act_global,

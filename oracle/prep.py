@@ -14,7 +14,7 @@ steps; the readings used here:
   its largest-magnitude entry is positive, then rounded to bf16;
 * residual R = What - L1_bf16 @ L2_bf16 (float64, stored as float32), quantized
   per output column in groups along K with the same rule as the activations
-  (int4: s = bf16(amax / 7), q = rne(R / s) in [-7, 7]; NVFP4: per-tensor
+  (int4: s = bf16(amax / 7), q = rne(R / s) in [-8, 7]; NVFP4: per-tensor
   g_w = fl32(amax|R| / (6 * 448)), E4M3 block scales, E2M1 codes);
 * NVFP4 activation scale g_x = fl32(amax|Xhat_cal| / (6 * 448)), static;
 * AWQ W4A16 (no smoothing, no low-rank): per (column, group of 64) asymmetric

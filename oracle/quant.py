@@ -11,9 +11,13 @@ The pages leave the steps open; the readings used (all recorded in the design doc):
 1. Smoothing.  The per-input-channel smoothing multiplier m (bf16) is folded into
    the activations: xhat = bf16(x * m).  The product of two bf16 numbers is exact in
    float32, so this is one rounding.
-2. Groups run along K, per token.  int4: amax over 64 values, scale
+2. Groups run along K, per token.  int4: amax over 64 values, symmetric scale
    s = bf16(fl32(amax / 7)), code q = round-half-even(xhat / s) clamped to the
-   symmetric range [-7, 7] (with s = 0 every code is 0).
+   4-bit two's complement range [-8, 7] (with s = 0 every code is 0).  While s is a
+   normal bf16 number it is within 2^-9 of amax / 7, so |xhat / s| < 7.02 and the
+   clamp never acts: codes stay in [-7, 7].  Only a subnormal bf16 scale (amax below
+   about 2^-123), whose few significant bits can round far below amax / 7, lets a
+   quotient reach -8 (kept) or +8 (clamped to 7).
 3. NVFP4: blocks of 16.  Per-tensor float32 scale g (calibrated offline, passed
    in).  Block scale s = E4M3(fl32(amax / fl32(6 g))) (saturating).  Element code =
    E2M1(fl32(xhat / fl32(s g))), sign taken from the quotient's sign bit; with s = 0
@@ -61,7 +65,7 @@ def lora_down(xhat_bits, lora_down_bits) -> np.ndarray:
 def int4_scales_codes(v_f32: np.ndarray, group: int = INT4_GROUP):
     """Symmetric int4 quantization of float32 rows [R, K] in groups along K.
 
-    Returns (codes int [-7, 7] of shape [R, K], scales as bf16 bits [R, K/group]).
+    Returns (codes int [-8, 7] of shape [R, K], scales as bf16 bits [R, K/group]).
     The code is the round-half-even of the exact quotient v / s.  The quotient is
     formed in float64, which decides that rounding exactly: with a float32
     numerator and a bf16 divisor, a quotient that is not a half-integer lies at
@@ -79,7 +83,7 @@ def int4_scales_codes(v_f32: np.ndarray, group: int = INT4_GROUP):
     with np.errstate(divide="ignore", invalid="ignore"):
         quot = vg.astype(np.float64) / s[:, :, None]
     q = np.where(s[:, :, None] > 0, np.rint(quot), 0.0)
-    q = np.clip(q, -7, 7).astype(np.int64)
+    q = np.clip(q, -8, 7).astype(np.int64)
     return q.reshape(R, K), s_bits
 
 

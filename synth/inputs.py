@@ -144,11 +144,10 @@ NVFP4_UP = dict(config_id=4, M=4096, K=3072, N=12288, outlier_count=None, factor
 
 
 def _nibble_bytes(rng: np.random.Generator, rows: int, half_k: int) -> np.ndarray:
-    """Bytes whose two 4-bit fields are drawn uniformly from the 15 two's complement
-    patterns of -7..7 (the pattern 0x8 of -8 is never drawn)."""
-    pats = np.array([0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15], dtype=np.uint8)
-    lo = pats[rng.integers(0, 15, size=(rows, half_k))]
-    hi = pats[rng.integers(0, 15, size=(rows, half_k))]
+    """Bytes whose two 4-bit fields are drawn uniformly from all 16 two's complement
+    patterns, the int4 values -8..7."""
+    lo = rng.integers(0, 16, size=(rows, half_k)).astype(np.uint8)
+    hi = rng.integers(0, 16, size=(rows, half_k)).astype(np.uint8)
     return (lo | (hi << 4)).astype(np.uint8)
 
 
@@ -157,7 +156,7 @@ class PreparedBytes:
     """Seeded bytes in the layout of a prepared int4 svdq_w4a4 layer (stand-ins for
     the output of the offline weight preparation, for timing the forward call).
 
-    qweight  uint8 [N, K/2]    codes uniform in -7..7
+    qweight  uint8 [N, K/2]    codes uniform in -8..7
     wscales  bf16  [N, K/64]   about 0.015 (log-normal spread)
     smooth   bf16  [K]         0.4..0.6, outlier channels 0.08..0.12
     lora_down bf16 [rank, K]   N(0, 0.05);  lora_up bf16 [N, rank]  N(0, 0.05)

@@ -105,8 +105,9 @@ def decode_fp6_operand(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
 
     Chunk (row // 32, g) of 1536 B: lane slot h*32 + row%32 holds dwords 0-3 at
     slot*16 and dwords 4-5 at 1024 + slot*8; field f (bits 6f..6f+5 of the six
-    dwords) is k = 64 g + 32 h + f, an E2M3 code with sign bit 5 and magnitude in
-    bits 2:0 (value q/8).
+    dwords) is k = 64 g + 32 h + f, an E2M3 code of value q/8 with sign bit 5: the
+    magnitude |q| <= 7 in bits 2:0 (subnormal), or 8 as the normal 1.0 (exponent
+    field 1, mantissa 0, i.e. bits 4:0 = 0b01000).
     """
     G = K // 64
     b = np.asarray(buf, dtype=np.uint8)[: rows_pad // 32 * G * 1536].reshape(rows_pad // 32, G, 1536)
@@ -119,9 +120,40 @@ def decode_fp6_operand(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
         for bit in range(6):
             p = 6 * f + bit
             code |= ((dw[..., p // 32] >> np.uint64(p % 32)) & np.uint64(1)) << np.uint64(bit)
-        assert np.all((code & np.uint64(0x18)) == 0), "exponent bits set in an int4 field"
-        mag = (code & np.uint64(7)).astype(np.int64)
+        mag = (code & np.uint64(0x1F)).astype(np.int64)
+        assert np.all(mag <= 8), "an E2M3 field outside the int4 values"
+        assert np.all((mag < 8) | ((code & np.uint64(0x20)) > 0)), "+8 is not an int4 code"
         out[..., f] = np.where(code & np.uint64(0x20), -mag, mag)
     # [rb, g, h*32 + r, f] -> row = 32 rb + r, k = 64 g + 32 h + f
     out = out.reshape(rows_pad // 32, G, 2, 32, 32).transpose(0, 3, 1, 2, 4)
     return out.reshape(rows_pad, K)
+
+
+def _round256(n: int) -> int:
+    return -(-n // 256) * 256
+
+
+def k1_splits(K: int) -> int:
+    """k-splits of the layer's quantizer (at most 1536 values each)."""
+    return -(-K // 1536)
+
+
+def int4_workspace(buf: np.ndarray, rows_pad: int, K: int, rank: int):
+    """The int4 linear's workspace -> (codes [rows_pad, K], scale bits [K/64, rows_pad],
+    partial U [splits, rows_pad, rank] or None): the E2M3 operand, then the scale
+    records, then the fp32 partial U, each area starting on a 256-byte boundary."""
+    G = K // 64
+    w = np.asarray(buf, dtype=np.uint8)
+    q = decode_fp6_operand(w, rows_pad, K)
+    off_s = _round256(rows_pad * K * 3 // 4)
+    s = scale_records(w[off_s:], G, rows_pad)
+    off_u = off_s + _round256(G * rows_pad * 8)
+    u = u_partials(w[off_u:], k1_splits(K), rows_pad, rank) if rank else None
+    return q, s, u
+
+
+def nvfp4_workspace_values(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
+    """The NVFP4 linear's staged activations -> float64 values [rows_pad, K]: the exact
+    dequantized bf16 operand e2m1 * s_b (without the tensor scale), [rows_pad][K]."""
+    a = np.asarray(buf, dtype=np.uint8)[: rows_pad * K * 2].view(np.uint16).reshape(rows_pad, K)
+    return F.bf16_to_f64(a)

@@ -90,13 +90,73 @@ def test_pack_weight_layout(tiny):
     assert np.array_equal(st, layer.wscales.T)
 
 
-def test_pack_weight_rejects_minus_eight(tiny):
+def test_pack_weight_holds_minus_eight(tiny):
+    """Every int4 code, -8 included, packs to the E2M3 operand value q/8."""
     _, layer = tiny
-    bad = layer.qweight.copy()
-    bad[5, 7] = (bad[5, 7] & 0x0F) | 0x80          # a -8 code
-    with pytest.raises(svdq.SvdqError) as ei:
-        svdq.pack_weight(dev_u8(bad), dev_bf16(layer.wscales))
-    assert ei.value.status == 8
+    rng = np.random.default_rng(83)
+    q = rng.integers(-8, 8, size=(layer.N, layer.K))
+    q[:, ::7] = -8
+    pc, _ = svdq.pack_weight(dev_u8(int4_interchange(q)), dev_bf16(layer.wscales))
+    assert np.array_equal(decode_fp6_operand(host_bits(pc), layer.N, layer.K), q)
+
+
+def _subnormal_golden_rows(M):
+    from golden_cases import int4_subnormal_scales
+    x, q, s = int4_subnormal_scales()
+    K = 512
+    assert x.shape[1] <= K
+    xb = np.zeros((M, K), np.uint16)
+    qq = np.zeros((M, K), np.int64)
+    for m in range(M):          # the golden groups, rotated by a group per row
+        sh = 64 * (m % 8)
+        xb[m, :x.shape[1]] = x[0]
+        qq[m, :x.shape[1]] = q[0]
+        xb[m] = np.roll(xb[m], sh)
+        qq[m] = np.roll(qq[m], sh)
+    return xb, qq, s
+
+
+def test_quantize_act_subnormal_scales_golden():
+    """The hand-worked groups with subnormal bf16 scales (their exact-division branch
+    and the clamp to [-8, 7]) through svdq_quantize_act: codes and scales equal the
+    golden values and the oracle's."""
+    from golden_cases import int4_subnormal_scales
+    xb, qq, s = _subnormal_golden_rows(24)
+    one = F.bf16_rne(np.ones(xb.shape[1], np.float32))
+    ref = Q.quantize_act_int4(xb, one, None)
+    assert np.array_equal(ref["q"], qq)
+    codes, scales, _ = svdq.quantize_act(dev_bf16(xb), dev_bf16(one), None)
+    torch.cuda.synchronize()
+    assert np.array_equal(F.int4_decode(F.unpack_nibbles(host_bits(codes))), qq)
+    assert np.array_equal(host_bits(scales), ref["scales"])
+    assert np.array_equal(host_bits(scales)[0, :s.shape[1]], s[0])
+
+
+def test_fused_quantizer_subnormal_scales_golden():
+    """The same groups through the layer's own quantizer (the GEMM operand layout in
+    the workspace): -8 codes become the E2M3 value -1.0."""
+    xb, qq, _ = _subnormal_golden_rows(40)
+    K, N = xb.shape[1], 128
+    rng = np.random.default_rng(84)
+    one = F.bf16_rne(np.ones(K, np.float32))
+    layer = P.SvdqLayer(precision="int4", K=K, N=N, rank=0,
+                        qweight=int4_interchange(rng.integers(-8, 8, size=(N, K))),
+                        wscales=F.bf16_rne(np.full((N, K // 64), 0.01, np.float32)), w_global=1.0,
+                        act_global=1.0, smooth=one, lora_down=np.zeros((0, K), np.uint16),
+                        lora_up=np.zeros((N, 0), np.uint16), bias=None)
+    dl = _layer_dev(layer)
+    need = dl.workspace_bytes(40)
+    buf = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    dl(dev_bf16(xb), workspace=buf)
+    torch.cuda.synchronize()
+    w = host_bits(buf)
+    q = decode_fp6_operand(w, 256, K)
+    assert np.array_equal(q[:40], qq)
+    assert np.all(q[40:] == 0)
+    ref = Q.quantize_act_int4(xb, one, None)
+    s = scale_records(w[256 * K * 3 // 4:], K // 64, 256)
+    assert np.array_equal(s[:, :40], ref["scales"].T)
+    assert np.all(s[:, 40:] == 0)
 
 
 @pytest.mark.parametrize("M", [256, 1, 17, 129, 255])
@@ -134,7 +194,8 @@ def test_linear_grid_exact_is_bit_exact():
     kx[:, ::64] = 7
     sx = 2.0 ** rng.integers(-3, 0, size=(M, K // 64))
     x = F.bf16_rne((kx * np.repeat(sx, 64, axis=1)).astype(np.float32))
-    kw = rng.integers(-7, 8, size=(N, K))
+    kw = rng.integers(-8, 8, size=(N, K))       # the whole int4 range, -8 included
+    kw[:, 1::9] = -8
     sw = 2.0 ** rng.integers(-7, -5, size=(N, K // 64))
     one = F.bf16_rne(np.ones(K, np.float32))
     layer = P.SvdqLayer(precision="int4", K=K, N=N, rank=0, qweight=int4_interchange(kw),
@@ -151,9 +212,14 @@ def test_workspace_matches_standalone_quantize(tiny):
     li, layer = tiny
     M = 200
     dl = _layer_dev(layer)
-    ws = torch.zeros(dl.workspace(M, torch.device("cuda")).numel(), dtype=torch.uint8, device="cuda")
+    # the workspace as sized, filled with a non-zero pattern (so the zero codes, scales
+    # and U of the padding rows must come from the kernel), then a guard region
+    need = dl.workspace_bytes(M)
+    buf = torch.full((need + (1 << 20),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = buf[:need]
     dl(dev_bf16(li.x[:M]), workspace=ws)
     torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "the linear wrote past its workspace"
     ref = Q.quantize_act_int4(li.x[:M], layer.smooth, layer.lora_down)
     w = host_bits(ws)
     M_pad, K, G = 256, layer.K, layer.K // 64

@@ -215,3 +215,40 @@ def test_linear_nvfp4_full_size_mlp_up_synthetic():
     y = host_bits(_layer_dev(layer)(dev_bf16(x)))
     rows = np.unique(np.concatenate([np.arange(7, 4096, 211), [4095]]))
     check_y(y[rows], OL.w4a4_linear_rows("nvfp4", x, layer, rows)["r"])
+
+
+def test_quantizers_non_dyadic_tensor_scale_golden():
+    """The hand-worked block with g = fl32(1/3) (tests/golden/nvfp4_tie_third.txt),
+    whose quotients sit on E2M1 midpoints only when the divisor is fl32(s g): through
+    svdq_quantize_act and through the layer's own quantizer (workspace values)."""
+    from golden_cases import nvfp4_tie_third
+    from helpers import nvfp4_workspace_values
+    xb, g, c, s = nvfp4_tie_third()
+    M, K, N = 40, 256, 128
+    rng = np.random.default_rng(93)
+    x = np.zeros((M, K), np.uint16)
+    for m in range(M):                      # the block, permuted, in every block slot
+        for b in range(K // 16):
+            x[m, 16 * b:16 * b + 16] = xb[0, rng.permutation(16)] if (m + b) % 3 else xb[0]
+    one = np.full(K, ONE, np.uint16)
+    ref = Q.quantize_act_nvfp4(x, one, float(g), None)
+    assert np.all(ref["scales"] == s[0, 0])
+    first = ref["e2m1"][0, :16]
+    assert np.array_equal(first, c[0])
+    codes, scales, _ = _quantize(x, one, None, float(g))
+    assert np.array_equal(host_bits(codes), ref["codes"])
+    assert np.array_equal(host_bits(scales), ref["scales"])
+    layer = P.SvdqLayer(precision="nvfp4", K=K, N=N, rank=0,
+                        qweight=F.pack_nibbles(rng.integers(0, 16, size=(N, K)).astype(np.uint8)),
+                        wscales=np.full((N, K // 16), 0x38, np.uint8), w_global=1.0,
+                        act_global=float(g), smooth=one, lora_down=np.zeros((0, K), np.uint16),
+                        lora_up=np.zeros((N, 0), np.uint16), bias=None)
+    dl = _layer_dev(layer)
+    need = dl.workspace_bytes(M)
+    buf = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    dl(dev_bf16(x), workspace=buf)
+    torch.cuda.synchronize()
+    a = nvfp4_workspace_values(host_bits(buf), 256, K)
+    expect = F.e2m1_decode(ref["e2m1"]) * np.repeat(F.e4m3_decode(ref["scales"]), 16, axis=1)
+    assert np.array_equal(a[:M], expect)
+    assert np.all(a[M:] == 0)

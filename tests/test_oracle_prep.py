@@ -89,3 +89,40 @@ def test_nvfp4_globals():
     assert 416 <= top <= 448
     assert layer.qweight.shape == (32, 32) and layer.wscales.shape == (32, 4)
     del rng
+
+
+def test_nvfp4_act_global_from_smoothed_calibration():
+    """g_x is the tensor scale of the smoothed, bf16-rounded calibration activations,
+    hand-worked: channel 0 holds the largest raw value (8) but, with multiplier 1/4,
+    only 2 after smoothing; channel 1 (multiplier 1) reaches 4; channel 2 holds
+    1 + 2^-7 with multiplier 1 + 2^-7, whose exact product 1 + 2^-6 + 2^-14 rounds to
+    the bf16 1 + 2^-6.  So amax |bf16(x m)| = 4 and g_x = fl32(4 / 2688) = fl32(1/672),
+    not 8/2688 (raw activations) nor a value from an unrounded product."""
+    x = np.array([[8.0, -4.0, 1.0078125],
+                  [-6.0, 3.0, 0.5]], np.float32)
+    m = np.array([0.25, 1.0, 1.0078125], np.float32)
+    gx = P.nvfp4_act_global(F.bf16_rne(x), F.bf16_rne(m))
+    assert gx == float(np.float32(1.0 / 672.0))
+    # the top value sits in the rounded channel when the others are small
+    x2 = np.array([[0.5, 0.25, 1.0078125]], np.float32)
+    gx2 = P.nvfp4_act_global(F.bf16_rne(x2), F.bf16_rne(m))
+    assert gx2 == float(np.float32(1.015625 / 2688.0))
+    assert gx2 != float(np.float32(np.float32(1.0078125 * 1.0078125) / np.float32(2688.0)))
+
+
+def test_prepare_nvfp4_act_global_uses_its_own_smoothing():
+    """Through prepare_svdq: the calibration set below has channel amax 16, 4 and 9, so
+    the multipliers are 1/4, 1/2 and bf16(1/3) = 0.333984375; the smoothed maxima are
+    4, 2 and bf16(9 * 0.333984375) = bf16(3.005859375) = 3.0, and g_x = fl32(4 / 2688)
+    (the raw maximum 16 would give four times that)."""
+    K = 64
+    x = np.zeros((2, K), np.float32)
+    x[:, 0] = [16.0, -3.0]
+    x[:, 1] = [-4.0, 1.0]
+    x[:, 2] = [2.0, 9.0]
+    rng = np.random.default_rng(25)
+    w = rng.standard_normal((K, 32)).astype(np.float32) * 0.02
+    layer = P.prepare_svdq(w, F.bf16_rne(x), None, rank=4, precision="nvfp4")
+    m = F.bf16_to_f64(layer.smooth)
+    assert m[0] == 0.25 and m[1] == 0.5 and m[2] == 0.333984375
+    assert layer.act_global == float(np.float32(1.0 / 672.0))

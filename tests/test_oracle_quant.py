@@ -185,3 +185,30 @@ def test_lora_down_is_not_rounded_to_bf16():
     one = np.full(128, ONE, np.uint16)
     u = Q.quantize_act_int4(x, one, l1t)["lora_act"]
     assert u[0, 0] == 1.0 + 2.0 ** -10 and u[1, 0] == 3 * 2.0 ** -12 + 2.0 ** -20
+
+
+def test_int4_subnormal_scales_golden():
+    """Hand-worked groups whose scale is a subnormal bf16 number
+    (tests/golden/int4_subnormal_scales.txt): the fl32 division and bf16 rounding of
+    amax / 7 on the subnormal grid, ties to even, the clamp to the int4 range [-8, 7]
+    (a -8 is kept, a +8 becomes 7) and the zero scale of a group whose amax / 7 rounds
+    to 0."""
+    from golden_cases import int4_subnormal_scales
+    x, q, s = int4_subnormal_scales()
+    out = Q.quantize_act_int4(x, np.full(x.shape[1], ONE, np.uint16))
+    assert np.array_equal(out["scales"], s)
+    assert np.array_equal(out["q"], q)
+    assert (q == -8).sum() >= 3
+    assert np.array_equal(F.int4_decode(F.unpack_nibbles(out["codes"])), q)
+
+
+def test_nvfp4_non_dyadic_tensor_scale_ties_golden():
+    """Hand-worked block with g = fl32(1/3) (tests/golden/nvfp4_tie_third.txt): the
+    divisor is fl32(s g), formed before the quotient, which puts every listed value on
+    or at an E2M1 point or midpoint; dividing by s and g one after the other misses the
+    midpoints and picks the odd neighbours."""
+    from golden_cases import nvfp4_tie_third
+    x, g, c, s = nvfp4_tie_third()
+    out = Q.quantize_act_nvfp4(x, np.full(16, ONE, np.uint16), float(g))
+    assert np.array_equal(out["scales"], s)
+    assert np.array_equal(out["e2m1"], c)

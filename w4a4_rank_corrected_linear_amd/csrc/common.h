@@ -3,8 +3,9 @@
 // Lane-slot layout of int4 GEMM operands
 // --------------------------------------
 // The int4 GEMM runs on the scaled FP6 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with
-// E2M3 operands).  An int4 code v in [-7, 7] is the E2M3 subnormal with sign bit 5
-// and the magnitude |v| in bits 2:0, whose value is v/8; E8M0 block scales make the
+// E2M3 operands).  An int4 code v in [-8, 7] is the E2M3 number v/8 with sign bit 5
+// and the magnitude |v| in bits 3:0 (|v| <= 7: a subnormal; |v| = 8: the normal 1.0,
+// exponent field 1 and mantissa 0); E8M0 block scales make the
 // MFMA return an exact multiple of the integer dot product of a 64-group in fp32.
 //
 // Both operands (activations written by the quantizer, weights written by the pack)
@@ -56,7 +57,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// E2M3 field of an int4 code in [-7, 7]: sign in bit 5, magnitude in bits 2:0.
+// E2M3 field of an int4 code in [-8, 7]: sign in bit 5, magnitude |q| in bits 3:0
+// (the value q/8: subnormal for |q| <= 7, the normal 1.0 for |q| = 8).
 __device__ __forceinline__ uint32_t e2m3_field(int q) {
   return (q < 0 ? 0x20u : 0u) | (uint32_t)(q < 0 ? -q : q);
 }

@@ -4,7 +4,8 @@
 // Layer definition: Diffusers docs "Nunchaku Lite", "Supported quantization types"
 // (svdq_w4a4, int4, group 64, SVDQ low-rank correction), with the readings stated
 // in svdq.h: xhat = bf16(x m), s = bf16(amax / 7), q = round-half-even(xhat / s)
-// clamped to [-7, 7], U = xhat @ lora_down^T (fp32 accumulation, not rounded).
+// clamped to the int4 range [-8, 7], U = xhat @ lora_down^T (fp32 accumulation, not
+// rounded).
 //
 // Two kernels share the quantizer below:
 //  * k1_int4_fused / k1_int4_fused16 (the layer's own path) use the row-pair skeleton
@@ -44,8 +45,9 @@ __device__ __forceinline__ uint32_t int4_quant32(const float (&xh)[32], float (&
   // 2^-9 relative of amax / 7, so |y| <= 7.014 and rounding to the nearest integer
   // already lands in [-7, 7]: the common path needs no clamp.  Scales below 2^-125
   // (subnormal bf16 scales lose precision, and 1/s may overflow) take the exact
-  // division and the clamp; that case is tested once per wave so the common path
-  // stays straight-line.
+  // division and the clamp to [-8, 7] (a subnormal scale can round far below amax / 7,
+  // so quotients reach beyond 8 in magnitude); that case is tested once per wave so
+  // the common path stays straight-line.
   const float rcp = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
   if (!__any(tiny)) {
 #pragma unroll
@@ -60,7 +62,7 @@ __device__ __forceinline__ uint32_t int4_quant32(const float (&xh)[32], float (&
       const float y1 = xh[i] * rcp;
       const float e = __builtin_fmaf(-y1, s, xh[i]);
       const float y = tiny ? __fdiv_rn(xh[i], s) : __builtin_fmaf(e, rcp, y1);
-      cq[i] = __builtin_amdgcn_fmed3f(y, -7.0f, 7.0f);
+      cq[i] = __builtin_amdgcn_fmed3f(y, -8.0f, 7.0f);
     }
   }
   return s_bits;
@@ -72,7 +74,9 @@ struct QuantInt4Fused {
     const uint32_t s_bits = int4_quant32(xh, cq);
     const int g = k0 >> 6, h = q & 1;
     // E2M3 fields of value q/8: the converter divides by the scale 8 and rounds to
-    // nearest even on the subnormal grid (step 1/8), i.e. to q/8.  Output field 2j
+    // nearest even on the E2M3 grid, whose step is 1/8 up to 1.0, i.e. to q/8 (q = -8
+    // is the normal -1.0; a clamped -7.5 sits midway between -0.875 and -1.0 and goes
+    // to the even -1.0, as round-half-even takes -7.5 to -8).  Output field 2j
     // comes from src0[j] and field 2j+1 from src1[j]: even k go to src0 and odd k
     // to src1, so field f holds k = f.
     v16f ev, od;
@@ -187,7 +191,7 @@ k1_int4_interchange(const uint16_t* __restrict__ x, int M, int K,
 
     {
       // Round to integer by adding 1.5 * 2^23: the low bits of the sum are the two's
-      // complement code (|q| <= 7); the add itself rounds half to even.
+      // complement code (-8 <= q <= 7); the add itself rounds half to even.
       uint32_t w[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {

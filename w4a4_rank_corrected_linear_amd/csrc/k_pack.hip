@@ -3,8 +3,9 @@
 // int4: codes [N][K/2] two's complement nibbles -> E2M3 lane slots of common.h
 //       (row-blocks of 32 output columns), scales [N][K/64] bf16 -> [K/64][N]
 //       8-byte records {s, 0, 0, 0} (common.h).
-//       A -8 code cannot be held by the sign-magnitude E2M3 field: it raises the
-//       range flag, which the host turns into SVDQ_ERR_RANGE.
+//       Every code of the int4 range [-8, 7] is an exact E2M3 value q/8: |q| <= 7
+//       are subnormals (magnitude in bits 2:0) and -8 is the normal -1.0 (exponent
+//       field 1, mantissa 0), i.e. the same sign-magnitude field with magnitude 8.
 // lora_down: [r][K] bf16 -> fragment order of the quantizer's low-rank MFMAs: for
 //       k-block kb (128 values), rank slice sl (16 ranks) and call c (0..3), lane
 //       l = 16 q + i holds lora_down[16 sl + i][128 kb + 32 q + 8 c .. + 8] (16 B), and
@@ -20,8 +21,7 @@ namespace svdq {
 // One thread per (row-block, group, lane slot h*32 + row % 32): reads the 16
 // interchange bytes of 32 codes and writes their six dwords of E2M3 fields.
 __global__ void __launch_bounds__(256)
-k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int N, int K,
-                  int* __restrict__ flag) {
+k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int N, int K) {
   const int G = K >> 6;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)N * G * 2;
@@ -35,13 +35,11 @@ k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, 
   const uint4 v = *reinterpret_cast<const uint4*>(codes + n * (K >> 1) + 32 * g + 16 * h);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-  bool bad = false;
 #pragma unroll
   for (int f = 0; f < 32; ++f) {
     const uint32_t nib = (w[f >> 3] >> (4 * (f & 7))) & 0xFu;
     const int q = (nib & 8u) ? (int)nib - 16 : (int)nib;
-    bad |= (q == -8);
-    const uint32_t fld = e2m3_field(q < -7 ? -7 : q);
+    const uint32_t fld = e2m3_field(q);
     const int pos = 6 * f, word = pos >> 5, bit = pos & 31;
     o[word] |= fld << bit;
     if (bit > 26) o[word + 1] |= fld >> (32 - bit);
@@ -49,7 +47,6 @@ k_pack_int4_codes(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, 
   uint8_t* chunk = out + (size_t)rest * 1536;
   *reinterpret_cast<uint4*>(chunk + slot * 16) = make_uint4(o[0], o[1], o[2], o[3]);
   *reinterpret_cast<uint2*>(chunk + 1024 + slot * 8) = make_uint2(o[4], o[5]);
-  if (bad) atomicOr(flag, 1);
 }
 
 // Weight scale records, one per pair of groups: {sw[n, 2p], sw[n, 2p + 1], 0, 0}.
@@ -116,7 +113,7 @@ hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_
   hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
   const int64_t total = (int64_t)N * G * 2;
   hipLaunchKernelGGL(k_pack_int4_codes, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     codes, out_codes, N, K, flag);
+                     codes, out_codes, N, K);
   const int64_t ts = (int64_t)N * (G / 2);
   hipLaunchKernelGGL(k_pair_scales, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
                      scales, reinterpret_cast<uint2*>(out_scales), N, G);

@@ -10,7 +10,7 @@
 //          column of L1 signed so its largest-magnitude entry is positive, then bf16
 //   R     = What - L1_bf16 L2_bf16  (float64, stored as float32)
 //   R quantized per output column in groups of 64 along K: s = bf16(fl32(amax / 7)),
-//   q = round-half-even(R / s) in [-7, 7]; or NVFP4: g_w = fl32(amax|R| / 2688), E4M3
+//   q = round-half-even(R / s) in [-8, 7]; or NVFP4: g_w = fl32(amax|R| / 2688), E4M3
 //   block scales and E2M1 codes per 16 (the activation quantizer's rule), and the
 //   static activation scale g_x = fl32(amax|bf16(x_cal m)| / 2688);
 //   AWQ (no smoothing, no factorization): asymmetric uint4 per column and group of 64.
@@ -434,7 +434,7 @@ k_prep_quant(const float* __restrict__ R, int K, int N, uint8_t* __restrict__ qw
       for (int u = 0; u < 2; ++u) {
         // the quotient in float64 decides the round-half-even exactly
         const double v = s > 0.0 ? rint((double)T[t][kk + u] / s) : 0.0;
-        q[u] = (int)fmin(fmax(v, -7.0), 7.0);
+        q[u] = (int)fmin(fmax(v, -8.0), 7.0);
       }
       dst[kk / 2] = (uint8_t)((q[0] & 15) | ((q[1] & 15) << 4));
     }

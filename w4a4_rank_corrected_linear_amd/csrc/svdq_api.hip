@@ -257,9 +257,7 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
                      "pack flag copy"));
   SVDQ_TRY(hip_check(hipStreamSynchronize(stream), "pack synchronize"));
   if (host_flag)
-    return fail(SVDQ_ERR_RANGE, nv ? "nvfp4 weight scale is an E4M3 NaN code"
-                                   : "int4 weight code -8 found: the packed layout holds the "
-                                     "symmetric range [-7, 7]");
+    return fail(SVDQ_ERR_RANGE, "nvfp4 weight scale is an E4M3 NaN code");
   return ok();
 }
 
