@@ -170,6 +170,26 @@ svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight
                                   const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* svdq_w4a4_linear for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, layouts, result and errors as svdq_w4a4_linear, without the workspace
+ * arguments: the layer's intermediates (quantized activations, scales, partial
+ * low-rank sums, and the GEMM's K-split partials when they fit) live in a scratch
+ * array of svdq_noalloc_max_workspace_bytes() = 64 MiB that the library holds on each
+ * device it runs on until the process ends.  The call allocates nothing and makes no
+ * allocating library call; its first use on a device (or svdq_check_device on it)
+ * looks up the array's address.  A shape whose workspace (svdq_workspace_bytes without
+ * the optional K-split area) exceeds 64 MiB returns SVDQ_ERR_WORKSPACE before any device
+ * access; for int4 that is about M * K <= 70 million (M = 4608 at K = 12288 fits).
+ * Every call on one device shares that device's array: calls that overlap in time on
+ * one device (other streams, other threads) race and give undefined results; calls
+ * ordered on one stream are safe.  Nothing in the array needs to start at zero (every
+ * call writes what it reads). */
+size_t svdq_noalloc_max_workspace_bytes(void);
+svdq_status svdq_w4a4_linear_noalloc(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                     const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                                     hipStream_t stream);
+
 /* The fused QKV projection of a DiT attention block with its per-head Q/K RMSNorm and
  * rotary embedding in the GEMM epilogue (Diffusers docs "Nunchaku Lite", "Fused
  * kernels": the original engine fuses the Q, K, V projections with RMSNorm and RoPE;

@@ -276,3 +276,26 @@ def test_prepare_entry_validation():
     assert lib.awq_prepare_weight(512, 512, None, FAKE, FAKE, FAKE, None) == L.ERR_NULL
     assert lib.awq_prepare_weight(500, 512, FAKE, FAKE, FAKE, FAKE, None) == L.ERR_SHAPE
     assert lib.awq_prepare_weight(512, 512, FAKE_MISALIGNED, FAKE, FAKE, FAKE, None) == L.ERR_ALIGN
+
+
+def test_noalloc_entry_point_validates_on_the_host():
+    """svdq_w4a4_linear_noalloc: the scratch maximum, NULL checks, and shapes whose
+    workspace exceeds the scratch array rejected with SVDQ_ERR_WORKSPACE before any
+    device access (here there is no device: a call that passed every host check would
+    return SVDQ_ERR_DEVICE instead)."""
+    lib = L.lib()
+    assert lib.svdq_noalloc_max_workspace_bytes() == 64 << 20
+    c = cfg()
+
+    def call(w, M=16, x=FAKE, y=FAKE):
+        return lib.svdq_w4a4_linear_noalloc(ctypes.byref(c), ctypes.byref(w), x, M, 1.0, y, None)
+
+    assert call(weight(), x=None) == L.ERR_NULL
+    assert call(weight(), y=None) == L.ERR_NULL
+    assert call(weight(), x=FAKE_MISALIGNED) == L.ERR_ALIGN
+    big = weight(K=12288, N=3072)
+    assert call(big, M=8192) == L.ERR_WORKSPACE
+    assert "64" in L.last_error() or "67108864" in L.last_error()
+    if not HAVE_GPU:
+        assert call(big, M=4608) == L.ERR_DEVICE      # fits: only the device check is left
+        assert call(weight(), M=0) == L.OK            # nothing to do, no device access

@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.svdq_w4a4_linear_gelu.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32, vp, vp,
                                    ctypes.c_size_t, vp]
     L.svdq_w4a4_linear_gelu.restype = st
+    L.svdq_w4a4_linear_noalloc.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32, vp, vp]
+    L.svdq_w4a4_linear_noalloc.restype = st
+    L.svdq_noalloc_max_workspace_bytes.argtypes = []
+    L.svdq_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
     L.svdq_w4a4_linear_qkv_norm_rope.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32,
                                                  vp, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]
     L.svdq_w4a4_linear_qkv_norm_rope.restype = st

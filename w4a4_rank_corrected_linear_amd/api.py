@@ -162,6 +162,25 @@ class SvdqLinear:
 
     __call__ = forward
 
+    def forward_noalloc(self, x: torch.Tensor, out: torch.Tensor | None = None,
+                        act_global: float | None = None):
+        """y = layer(x) through svdq_w4a4_linear_noalloc: the library's own scratch
+        array holds the workspace (no device allocation in the call; ``out`` may be
+        given so that nothing is allocated here either)."""
+        _want(x, torch.bfloat16, "x")
+        M, K = x.shape
+        if K != self.K:
+            raise ValueError(f"x has K = {K}, layer expects {self.K}")
+        y = torch.empty((M, self.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+        if M == 0:  # nothing to compute (empty tensors carry no device address)
+            return y
+        g = self.act_global if act_global is None else float(act_global)
+        fn = "svdq_w4a4_linear_noalloc"
+        st = getattr(L.lib(), fn)(ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), M, g,
+                                  _p(y), _stream())
+        L.check(st, fn)
+        return y
+
     def qkv_norm_rope(self, x: torch.Tensor, norm_q: torch.Tensor, norm_k: torch.Tensor,
                       eps: float, rope: torch.Tensor, out: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None, act_global: float | None = None):

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -73,6 +74,37 @@ svdq_status check_current_device() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device memory of the allocation-free entry point (svdq_w4a4_linear_noalloc): the
+// layer's workspace lives in this array, one copy per device, held until the process
+// ends.  Host code never passes the array's name to a kernel (in host code it is a
+// stand-in, not a device address): its address on each device is looked up once,
+// with that device current, and kept in g_scratch_addr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// The scratch array's address on the current device (looked up on first use).
+svdq_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(SVDQ_ERR_DEVICE, "no current HIP device (%s)", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SVDQ_ERR_DEVICE, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SVDQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  e != hipSuccess ? hipGetErrorString(e) : "null address");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SVDQ_OK;
+}
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -204,7 +236,17 @@ void timer_release() {
 extern "C" {
 
 svdq_status svdq_check_device(int hip_device) {
-  const svdq_status s = check_device_impl(hip_device);
+  svdq_status s = check_device_impl(hip_device);
+  if (s != SVDQ_OK) return s;
+  // set-up of the allocation-free entry point: the scratch array's address on this
+  // device, looked up with the device current
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(SVDQ_ERR_DEVICE, "no current HIP device");
+  if (cur != hip_device && hipSetDevice(hip_device) != hipSuccess)
+    return fail(SVDQ_ERR_DEVICE, "cannot make device %d current", hip_device);
+  void* p = nullptr;
+  s = scratch_address(&p);
+  if (cur != hip_device) (void)hipSetDevice(cur);
   return s == SVDQ_OK ? ok() : s;
 }
 
@@ -316,11 +358,21 @@ svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t
 namespace {
 
 // The layer call behind svdq_w4a4_linear (gelu = false) and svdq_w4a4_linear_gelu.
+// The layer's workspace: the caller's buffer, or (scratch = true) the library's own
+// scratch array of kScratchBytes, whose address is looked up after every host check.
+struct Workspace {
+  void* ptr;
+  size_t bytes;
+  bool scratch;
+};
+
 svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_weight* w,
                         const uint16_t* x, int64_t M, float act_global, uint16_t* y,
-                        void* workspace, size_t workspace_bytes, int epi, const svdq::QkEpi& qk,
-                        hipStream_t stream) {
-  if (!cfg || !w || !x || !y || !workspace || !w->qweight || !w->wscales || !w->smooth)
+                        Workspace wsa, int epi, const svdq::QkEpi& qk, hipStream_t stream) {
+  void* workspace = wsa.ptr;
+  const size_t workspace_bytes = wsa.bytes;
+  if (!cfg || !w || !x || !y || (!workspace && !wsa.scratch) || !w->qweight || !w->wscales ||
+      !w->smooth)
     return fail(SVDQ_ERR_NULL, "%s: NULL argument", fn);
   if (epi == svdq::kEpiQkNormRope && (!qk.norm_q || !qk.norm_k || !qk.rope))
     return fail(SVDQ_ERR_NULL, "%s: NULL norm weight or rotary table", fn);
@@ -351,12 +403,18 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
     return fail(SVDQ_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   const WsLayout L = ws_layout(cfg, M, w->K);
   const size_t need = L.split ? L.split : L.total;  // the split area is optional
-  if (workspace_bytes < need)
+  if (workspace_bytes < need) {
+    if (wsa.scratch)
+      return fail(SVDQ_ERR_WORKSPACE, "%s: M = %lld, K = %lld needs %zu bytes of workspace; the "
+                  "allocation-free entry point holds at most %zu", fn, (long long)M,
+                  (long long)w->K, need, workspace_bytes);
     return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 workspace_bytes, need);
+  }
   const bool split_room = L.split && workspace_bytes >= L.total;
   if (M == 0) return ok();
   SVDQ_TRY(check_current_device());
+  if (wsa.scratch) SVDQ_TRY(scratch_address(&workspace));
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* a_codes = ws + L.codes;
   uint2* a_scales = reinterpret_cast<uint2*>(ws + L.scales);
@@ -407,15 +465,27 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
 svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w, const uint16_t* x,
                              int64_t M, float act_global, uint16_t* y, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  return linear_impl("svdq_w4a4_linear", cfg, w, x, M, act_global, y, workspace, workspace_bytes,
+  return linear_impl("svdq_w4a4_linear", cfg, w, x, M, act_global, y,
+                     Workspace{workspace, workspace_bytes, false},
                      svdq::kEpiPlain, svdq::QkEpi{}, stream);
 }
 
 svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight* w,
                                   const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return linear_impl("svdq_w4a4_linear_gelu", cfg, w, x, M, act_global, y, workspace,
-                     workspace_bytes, svdq::kEpiGelu, svdq::QkEpi{}, stream);
+  return linear_impl("svdq_w4a4_linear_gelu", cfg, w, x, M, act_global, y,
+                     Workspace{workspace, workspace_bytes, false}, svdq::kEpiGelu, svdq::QkEpi{},
+                     stream);
+}
+
+size_t svdq_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+svdq_status svdq_w4a4_linear_noalloc(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                     const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                                     hipStream_t stream) {
+  return linear_impl("svdq_w4a4_linear_noalloc", cfg, w, x, M, act_global, y,
+                     Workspace{nullptr, kScratchBytes, true}, svdq::kEpiPlain, svdq::QkEpi{},
+                     stream);
 }
 
 svdq_status svdq_w4a4_linear_qkv_norm_rope(const svdq_config* cfg, const svdq_w4a4_weight* w,
@@ -424,9 +494,9 @@ svdq_status svdq_w4a4_linear_qkv_norm_rope(const svdq_config* cfg, const svdq_w4
                                            float eps, const float* rope, uint16_t* y,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream) {
-  return linear_impl("svdq_w4a4_linear_qkv_norm_rope", cfg, w, x, M, act_global, y, workspace,
-                     workspace_bytes, svdq::kEpiQkNormRope, svdq::QkEpi{norm_q, norm_k, rope, eps},
-                     stream);
+  return linear_impl("svdq_w4a4_linear_qkv_norm_rope", cfg, w, x, M, act_global, y,
+                     Workspace{workspace, workspace_bytes, false}, svdq::kEpiQkNormRope,
+                     svdq::QkEpi{norm_q, norm_k, rope, eps}, stream);
 }
 
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w, const uint16_t* x,
