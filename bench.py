@@ -493,12 +493,80 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     print("\n".join(lines + t))
 
 
+def summarize_counters(name: str, what: str, *runs: str) -> None:
+    """rocprofv3 --pmc runs (each given as "<csv_dir>=<command>") as one text summary
+    profiles/<name>_counters.txt: per kernel, the mean of every counter per dispatch,
+    and derived figures (host only, no GPU).  SQ_BUSY_CYCLES is summed over the chip's
+    32 shader engines, so SQ_BUSY_CYCLES / 32 is the kernel's duration in cycles
+    (GRBM_GUI_ACTIVE spans the profiler's serialized dispatch, not the kernel alone);
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES are per-SIMD counts summed
+    over the 1024 SIMDs, so the MFMA-busy fraction is busy / 1024 / kernel cycles, and
+    the co-exec share is the part of the MFMA-busy cycles in which the SIMD also
+    executed VALU work."""
+    import csv
+    import glob
+    simds, engines = 1024, 32
+    per = {}      # kernel -> counter -> [values per dispatch]
+    cmds = []
+    for run in runs:
+        d, cmd = run.split("=", 1)
+        cmds.append(cmd)
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(os.path.join(d, "**/*counter_collection.csv"))
+        acc = {}
+        for r in csv.DictReader(open(files[0])):
+            nm = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            nm = nm[: nm.index("(")] if "(" in nm else nm
+            nm = nm.replace("void ", "").replace("svdq::", "")
+            key = (nm, r["Counter_Name"], r["Dispatch_Id"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        for (nm, c, _), v in acc.items():
+            per.setdefault(nm, {}).setdefault(c, []).append(v)
+    lines = [f"# rocprofv3 hardware counters: {what}"]
+    lines += [f"# command: {c}" for c in cmds]
+    lines.append(f"# summary: python bench.py --summarize-counters {name} <what> <csv_dir>=<command> ...")
+    lines.append(f"# gemm_source_sha256_16 = {gemm_source_hash()}")
+    for nm in sorted(per, key=lambda k: -max(len(v) for v in per[k].values())):
+        cs = per[nm]
+        n = max(len(v) for v in cs.values())
+        if n < 5:
+            continue
+        lines.append(f"[{nm}]  dispatches {n}")
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        for c in sorted(mean):
+            lines.append(f"  {c} = {mean[c]:.1f}")
+        kc = mean.get("SQ_BUSY_CYCLES", 0.0) / engines
+        if kc > 0:
+            lines.append(f"  kernel_cycles = {kc:.0f}")
+        if kc > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+            lines.append(f"  mfma_busy_cycles_per_simd = {busy:.0f}")
+            lines.append(f"  mfma_busy_fraction = {busy / kc:.3f}")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean and mean.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            lines.append(f"  coexec_share_of_mfma_busy = "
+                         f"{mean['SQ_VALU_MFMA_COEXEC_CYCLES'] / mean['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+        if mean.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in mean:
+            lines.append(f"  lds_bank_conflict_cycles_per_lds_inst = "
+                         f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_INSTS_LDS']:.3f}")
+        if mean.get("SQ_INSTS_VALU"):
+            lines.append(f"  valu_insts_per_simd = {mean['SQ_INSTS_VALU'] / simds:.0f}")
+            if mean.get("SQ_INSTS_MFMA"):
+                lines.append(f"  valu_insts_per_mfma = {mean['SQ_INSTS_VALU'] / mean['SQ_INSTS_MFMA']:.2f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{name}_counters.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
 def main() -> int:
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
         summarize_profiles(sys.argv[2])
         return 0
     if len(sys.argv) == 6 and sys.argv[1] == "--summarize-stats":
         summarize_stats(*sys.argv[2:6])
+        return 0
+    if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-counters":
+        summarize_counters(*sys.argv[2:])
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

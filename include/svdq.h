@@ -104,7 +104,10 @@ svdq_status svdq_check_device(int hip_device);
  *          {scale of group 2p, scale of group 2p+1, 0, 0} in bf16: the rescale MFMA's
  *          operand as stored, one record per pair of groups; a 256-byte trailer the
  *          pack clears)
- *   nvfp4: codes N*K*2 (exact dequantized bf16 [N][K]), scales 256 (range flag) */
+ *   nvfp4: codes N*K/2 (E2M1 codes in the GEMM's FP4 lane slots: chunks of 1024 bytes
+ *          per 32 output columns and 64-group, 4 bits per weight), scales
+ *          round_up(N*K/8, 256) + 256 (each E4M3 block scale as its exact fp16 value,
+ *          [K/64][N][4]; range flag) -- 4.5 bits per weight in all */
 size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,
                                 size_t* codes_bytes, size_t* scales_bytes);
 

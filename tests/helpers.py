@@ -152,8 +152,26 @@ def int4_workspace(buf: np.ndarray, rows_pad: int, K: int, rank: int):
     return q, s, u
 
 
+def decode_fp4_operand(buf: np.ndarray, rows_pad: int, K: int):
+    """NVFP4 GEMM operand (FP4 lane slots, then fp16 block scales) -> (E2M1 codes
+    [rows_pad, K], block scales as float64 [rows_pad, K/16]).
+
+    Chunk (row // 32, q) of 1 KiB: lane slot 32 h + row % 32 holds in dword j the codes
+    of k = 64 q + 16 j + 8 h + [0, 8), element e in bits 4e..4e+3.  The scales follow at
+    the next 256-byte boundary as fp16 [K/64][rows_pad][4] (block 4 q + j of a row)."""
+    Q = K // 64
+    w = np.asarray(buf, dtype=np.uint8)
+    d = w[: rows_pad * K // 2].view(np.uint32).reshape(rows_pad // 32, Q, 2, 32, 4)  # rb,q,h,r,j
+    nib = np.stack([(d >> np.uint32(4 * e)) & np.uint32(15) for e in range(8)], axis=-1)
+    codes = nib.transpose(0, 3, 1, 4, 2, 5).reshape(rows_pad, K).astype(np.uint8)   # rb,r,q,j,h,e
+    off = _round256(rows_pad * K // 2)
+    s16 = w[off: off + rows_pad * K // 8].view(np.float16).reshape(Q, rows_pad, 4)
+    scales = s16.transpose(1, 0, 2).reshape(rows_pad, K // 16).astype(np.float64)
+    return codes, scales
+
+
 def nvfp4_workspace_values(buf: np.ndarray, rows_pad: int, K: int) -> np.ndarray:
     """The NVFP4 linear's staged activations -> float64 values [rows_pad, K]: the exact
-    dequantized bf16 operand e2m1 * s_b (without the tensor scale), [rows_pad][K]."""
-    a = np.asarray(buf, dtype=np.uint8)[: rows_pad * K * 2].view(np.uint16).reshape(rows_pad, K)
-    return F.bf16_to_f64(a)
+    dequantized operand e2m1 * s_b (without the tensor scale)."""
+    codes, scales = decode_fp4_operand(buf, rows_pad, K)
+    return F.e2m1_decode(codes) * np.repeat(scales, 16, axis=1)

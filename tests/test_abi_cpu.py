@@ -101,7 +101,8 @@ def test_workspace_size_and_check():
     assert linear(cfg(), weight(), M=100, ws_bytes=base - 1) == L.ERR_WORKSPACE
     assert lib.svdq_workspace_bytes(ctypes.byref(cfg(rank=0)), 100, 512) == 98304 + 16384 + split
     nv = lib.svdq_workspace_bytes(ctypes.byref(cfg(precision=L.NVFP4, group=16)), 100, 512)
-    assert nv == 256 * 512 * 2 + 256 * 32 * 4   # exact bf16 operand [M_pad][K] and U
+    # E2M1 codes (1/2 byte per value), fp16 block scales (1/8 byte per value) and U
+    assert nv == 256 * 512 // 2 + 256 * 512 // 8 + 256 * 32 * 4
 
 
 def test_packed_weight_bytes():
@@ -150,12 +151,14 @@ def test_timing_start_without_device_is_a_clear_error():
 def test_nvfp4_sizes_and_global_scale_check():
     lib = L.lib()
     c = cfg(precision=L.NVFP4, group=16)
-    # rows padded to the GEMM's 256-row tile: bf16 operand 256 x 512 x 2, no scales,
-    # U 256 x 32 x 4
-    assert lib.svdq_workspace_bytes(ctypes.byref(c), 100, 512) == 262144 + 32768
+    # rows padded to the GEMM's 256-row tile: E2M1 codes 256 x 512 / 2, fp16 block
+    # scales 256 x 512 / 8, U 256 x 32 x 4
+    assert lib.svdq_workspace_bytes(ctypes.byref(c), 100, 512) == 65536 + 16384 + 32768
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     tot = lib.svdq_packed_weight_bytes(ctypes.byref(c), 512, 256, ctypes.byref(cb), ctypes.byref(sb))
-    assert (cb.value, sb.value, tot) == (256 * 512 * 2, 256, 256 * 512 * 2 + 256)
+    # 4 bits of code and (2 bytes / 16 =) 1 bit of scale per weight, then the flag trailer
+    assert (cb.value, sb.value, tot) == (256 * 512 // 2, 256 * 512 // 8 + 256,
+                                         256 * 512 // 2 + 256 * 512 // 8 + 256)
     w = weight()
     for gx, gw in [(0.0, 1.0), (1.0, 0.0), (float("nan"), 1.0), (1.0, float("inf")), (-1.0, 1.0)]:
         w.w_global = gw

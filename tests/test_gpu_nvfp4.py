@@ -97,13 +97,17 @@ def test_quantize_act_nvfp4_scale_saturation_and_subnormal_scales():
     assert np.any((seen > 0) & (seen < 8)), "no subnormal block scale exercised"
 
 
-def test_pack_weight_nvfp4_is_exact_dequantization(tiny):
+def test_pack_weight_nvfp4_layout(tiny):
+    """The packed weights are the interchange codes in FP4 lane slots and the E4M3 scales
+    as their exact fp16 values (4.5 bits per weight)."""
+    from helpers import decode_fp4_operand
     _, layer = tiny
-    pc, _ = svdq.pack_weight(dev_u8(layer.qweight), dev_u8(layer.wscales), precision="nvfp4")
-    w = host_bits(pc).view(np.uint16).reshape(layer.N, layer.K)
-    expect = F.e2m1_decode(F.unpack_nibbles(layer.qweight)) * np.repeat(
-        F.e4m3_decode(layer.wscales), 16, axis=1)
-    assert np.array_equal(F.bf16_to_f64(w), expect)
+    pc, ps = svdq.pack_weight(dev_u8(layer.qweight), dev_u8(layer.wscales), precision="nvfp4")
+    assert pc.numel() == layer.N * layer.K // 2
+    buf = np.concatenate([host_bits(pc), host_bits(ps)])
+    codes, scales = decode_fp4_operand(buf, layer.N, layer.K)
+    assert np.array_equal(codes, F.unpack_nibbles(layer.qweight))
+    assert np.array_equal(scales, F.e4m3_decode(layer.wscales))
 
 
 def test_pack_weight_nvfp4_rejects_nan_scale(tiny):
@@ -167,7 +171,9 @@ def test_linear_nvfp4_grid_exact_is_bit_exact():
     assert np.array_equal(host_bits(y), ref["y"])
 
 
-def test_workspace_holds_exact_dequantized_activations(tiny):
+def test_workspace_holds_codes_and_scales(tiny):
+    """The layer's quantizer leaves the E2M1 codes and the block scales (fp16) of the
+    activations in the workspace, bit for bit the oracle's, zeros in the padding rows."""
     li, layer = tiny
     M = 200
     dl = _layer_dev(layer)
@@ -179,12 +185,11 @@ def test_workspace_holds_exact_dequantized_activations(tiny):
     torch.cuda.synchronize()
     assert bool((buf[need:] == 0xA5).all()), "the NVFP4 linear wrote past its workspace"
     ref = Q.quantize_act_nvfp4(li.x[:M], layer.smooth, layer.act_global, layer.lora_down)
-    w = host_bits(ws)
-    M_pad, K = 256, layer.K
-    a = w[: M_pad * K * 2].view(np.uint16).reshape(M_pad, K)
-    expect = F.e2m1_decode(ref["e2m1"]) * np.repeat(F.e4m3_decode(ref["scales"]), 16, axis=1)
-    assert np.array_equal(F.bf16_to_f64(a[:M]), expect)
-    assert np.all(F.bf16_to_f64(a[M:]) == 0)
+    from helpers import decode_fp4_operand
+    codes, scales = decode_fp4_operand(host_bits(ws), 256, layer.K)
+    assert np.array_equal(codes[:M], ref["e2m1"])
+    assert np.array_equal(scales[:M], F.e4m3_decode(ref["scales"]))
+    assert np.all(codes[M:] == 0) and np.all(scales[M:] == 0)
 
 
 @pytest.fixture(scope="module")

@@ -17,6 +17,17 @@
 // 0-3 sit at chunk + 16 l and dwords 4-5 at chunk + 1024 + 8 l, so a 64-lane
 // 16-byte and a 64-lane 8-byte access read one whole operand.
 //
+// FP4 lane-slot layout of NVFP4 GEMM operands
+// ---------------------------------------------
+// The NVFP4 GEMM runs on v_mfma_f32_32x32x16_f16, one 16-value NVFP4 block of k per
+// MFMA, in which lane l takes row l % 32 and k = 8 (l / 32) + [0, 8) of the block.  Both
+// operands (activations written by the quantizer, weights written by the pack) keep
+// their E2M1 codes in that order: chunk (row / 32, q) of 1 KiB holds the 64-group
+// k = 64 q .. 64 q + 63 of a 32-row block, lane slot l = 32 h + row % 32 (16 bytes) holds
+// in dword j the eight codes of block 4 q + j, k = 64 q + 16 j + 8 h + [0, 8) (element 2i
+// in the low nibble of byte i).  Block scales are the exact fp16 values of the E4M3
+// scales, [K/64][rows][4]: the four blocks of a row's 64-group are 8 adjacent bytes.
+//
 // Scale records (operands of the rescale MFMA, one 64-bit load each)
 // -------------------------------------------------------------------
 // Activation scales sit group-major as 8-byte records, record g * M_pad + row: the

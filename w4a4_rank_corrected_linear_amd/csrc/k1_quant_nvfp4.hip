@@ -12,13 +12,13 @@
 // k0 .. k0 + 31 of a 128-wide k-block (k0 = 128 kb + 32 q, q = l/16), i.e. two whole
 // NVFP4 blocks, so every amax is an in-lane max.
 //
-// Two kernels share the quantizer below: k1_nvfp4_fused (the layer's own path, batch
-// skeleton of k1_batch.h) writes the exact dequantized GEMM operand
-// A' = e2m1(code) * s as bf16 [M_pad][K] (|e2m1| has 2 and s 4 significant bits, so the
-// product is exact in bf16) and partial U per k-split; the per-tensor scale g stays
-// out of A' and is applied to the GEMM's fp32 result.  k1_nvfp4_interchange
-// (svdq_quantize_act) writes codes [M][K/2] (element 2j in bits 3:0), E4M3 scale
-// bytes [M][K/16] and U [M][r].
+// Two kernels share the quantizer below: k1_nvfp4_fused and k1_nvfp4_fused32 (the
+// layer's own path, the batch and row-pair skeletons of k1_batch.h and k1_rows32.h)
+// write the GEMM operand 4-bit: the E2M1 codes in the FP4 lane-slot layout of common.h
+// and each block's E4M3 scale as its exact fp16 value, plus partial U per k-split; the
+// per-tensor scale g stays out of the operand and is applied to the GEMM's fp32
+// result.  k1_nvfp4_interchange (svdq_quantize_act) writes codes [M][K/2] (element 2j
+// in bits 3:0), E4M3 scale bytes [M][K/16] and U [M][r].
 #include "common.h"
 #include "k1_batch.h"
 #include "k1_rows32.h"
@@ -33,13 +33,28 @@ struct QuantNvfp4Fused {
     uint32_t codes[32], sc[2];
     float deq[32];
     nvfp4_quant32(xh, a.g, codes, deq, sc);
-    uint32_t w[16];
+    // the lane's 32 values are blocks j0 and j0 + 1 of the 64-group k0 / 64; in each,
+    // half h (eight codes, one dword) goes to lane slot 32 h + row % 32 of the chunk
+    uint32_t d[2][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      w[i] = (__float_as_uint(deq[2 * i]) >> 16) | (__float_as_uint(deq[2 * i + 1]) & 0xFFFF0000u);
-    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)row * a.K + k0);
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dst[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= codes[16 * b + 8 * h + i] << (4 * i);
+        d[b][h] = w;
+      }
+    const int g64 = k0 >> 6, j0 = (k0 >> 4) & 3;
+    uint8_t* chunk = a.out + ((size_t)(row >> 5) * (a.K >> 6) + g64) * 1024;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint2*>(chunk + (h * 32 + (row & 31)) * 16 + j0 * 4) = make_uint2(d[0][h], d[1][h]);
+    // the two block scales as fp16 (exact: E4M3 values are fp16 numbers)
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)e4m3_value(sc[0]));
+    const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)e4m3_value(sc[1]));
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.scales) + ((size_t)g64 * a.M_pad + row) * 4 + j0) =
+        h0 | (h1 << 16);
   }
 };
 
@@ -173,8 +188,9 @@ k1_nvfp4_interchange(const uint16_t* __restrict__ x, int M, int K,
 }
 
 // fused = false: codes [M][K/2], scales [M][K/16] (E4M3 bytes), U [M][r] fp32.
-// fused = true : A' bf16 [M_pad][K] (rows >= M are zero), partial U per k-split in the
-//                fragment layout of common.h.
+// fused = true : E2M1 codes in the FP4 lane-slot layout and fp16 block scales
+//                [K/64][M_pad][4] (common.h; rows >= M are zero), partial U per k-split
+//                in the fragment layout of common.h.
 hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {

@@ -1,0 +1,326 @@
+// K2, nvfp4: the 4-bit x 4-bit GEMM of the NVFP4 layer, fused with the per-tensor
+// scale, the rank-r up projection, the bias and the bf16 store.
+//
+//   Y[m,n] = bf16( g * sum_k A'[m,k] B'[n,k] + sum_j U[m,j] L2t[n,j] + b[n] ),
+//   A' = e2m1(x code) * s_x,  B' = e2m1(w code) * s_w,  g = g_x g_w
+//
+// (Diffusers docs "Nunchaku Lite", "Supported quantization types": svdq_w4a4 nvfp4,
+// group 16 with E4M3 block scales, SVDQ low-rank correction.)
+//
+// Both operands stay 4-bit in memory: E2M1 codes in the FP4 lane-slot layout of
+// common.h and the block scales as fp16 values.  CDNA4's scaled MFMAs take
+// power-of-two scales per 32 values, and its scaled FP4 converters use only the
+// exponent of their scale, so an E4M3 scale (with mantissa bits) is applied in
+// registers instead: each lane converts its eight codes of a 16-block to fp16 (scale
+// 1) and multiplies them by the block scale with packed fp16 multiplies.  Every
+// product e2m1 * s has at most six significant bits and lies in [2^-10, 2688], so the
+// operand is exact in fp16 and v_mfma_f32_32x32x16_f16 (k = 16: one NVFP4 block per
+// MFMA) accumulates the exact products in fp32; no per-block rescale is needed.
+//
+// Tiling: one 512-thread workgroup (8 waves, two per SIMD) per CU, tile 256 x BN with
+// BN = 64 WN (192 or 128), wave tile 64 x BN/2 (2 x WN blocks of 32 x 32), the
+// accumulators held transposed (the weight fragment is the MFMA's first operand): lane
+// l % 32 is the output row, its 16 elements are columns 8 q + 4 (l / 32) + p of the
+// block (element 4 q + p).  A stage is one 64-group of k (four NVFP4 blocks).  A 3-slot
+// LDS ring holds per stage the eight activation code chunks (8 KiB), the weight code
+// chunks (BN/32 KiB) and both tiles' scales (8 bytes per row or column), copied by LDS
+// DMA two stages ahead; at the top of stage t every wave waits for its own copies of
+// stage t+1, one barrier publishes them and frees the slot of stage t+2, and the
+// fragments of stage t+1 (one 16-byte code read and one 8-byte scale read per row or
+// column block) are read into registers while stage t is computed.  The tile order is
+// XCD-aware (tile_coords in k2_common.h).
+//
+// Epilogues: + bias and the bf16 store; the same with the exact GELU before the
+// rounding; or the fused QKV epilogue (128-wide tiles, one head each: per-row RMSNorm
+// over the head, the channel weights and the rotary turn of adjacent column pairs on
+// the Q and K tiles), as in the int4 GEMM.
+#include "common.h"
+#include "k2_common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// The fp16 MFMA operand of one lane and NVFP4 block: the eight E2M1 codes of dword d
+// (element 2i in the low nibble of byte i) times the block scale s, exact.
+__device__ __forceinline__ v8h fp4_expand(uint32_t d, uint32_t s16) {
+  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)s16);
+  const v2h ss = {s, s};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * ss;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * ss;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * ss;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * ss;
+  return (v8h){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int WN, int EPI>
+__global__ void __launch_bounds__(512, 1)
+k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
+            const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
+            const uint16_t* __restrict__ sB, const uint16_t* __restrict__ L2t,
+            const uint16_t* __restrict__ bias, float g, uint16_t* __restrict__ Y, int M, int N,
+            int K, int M_pad, int rank, QkEpi qk) {
+  constexpr int BM = 256, BN = 64 * WN, CB = BN / 32;
+  constexpr int AC = 8 * 1024, BC = CB * 1024;  // code bytes per stage
+  constexpr int AS = BM * 8, BS = BN * 8;       // scale bytes per stage
+  constexpr int SLOT = AC + BC + AS + BS;
+  constexpr int NF = 2 + WN;                    // fragments per wave and stage
+  static_assert(WN == 2 || WN == 3, "tile width 128 or 192");
+  static_assert(EPI != kEpiQkNormRope || WN == 2, "the QKV epilogue needs one head per tile");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * SLOT];
+  __shared__ float red[EPI == kEpiQkNormRope ? 512 : 1];  // per-row sums of squares, by wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = N / BN, tiles_m = M_pad / BM;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * BM, col0 = tn * BN;
+  const int rb0 = row0 >> 5, cb0 = col0 >> 5;
+  const int Q = K >> 6;  // stages (64-groups); K is a multiple of 128, so Q is even
+
+  // Copies of stage s into slot sl: wave w copies activation chunk rb0 + w; waves below
+  // CB weight chunk cb0 + w; the others the scale rows of the stage (activations: 2
+  // KiB, weights: BS bytes), 1 KiB per copy instruction.
+  const uint32_t voff = lane * 16;
+  auto dma = [&](int s, int sl) {
+    uint8_t* base = ring + sl * SLOT;
+    dma16(voff, A + ((size_t)(rb0 + wave) * Q + s) * 1024, lds_addr(base + wave * 1024));
+    if (wave < CB) {
+      dma16(voff, B + ((size_t)(cb0 + wave) * Q + s) * 1024, lds_addr(base + AC + wave * 1024));
+    } else {
+      const uint8_t* sa = reinterpret_cast<const uint8_t*>(sA + ((size_t)s * M_pad + row0) * 4);
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(sB + ((size_t)s * N + col0) * 4);
+      constexpr int JOBS = 2 + (BS + 1023) / 1024;
+      for (int j = wave - CB; j < JOBS; j += 8 - CB) {
+        if (j < 2) {
+          dma16(voff, sa + j * 1024, lds_addr(base + AC + BC + j * 1024));
+        } else {
+          const int kb = j - 2;
+          if (kb * 1024 + (int)voff < BS) dma16(voff, sb + kb * 1024, lds_addr(base + AC + BC + AS + kb * 1024));
+        }
+      }
+    }
+  };
+
+  struct Frag {
+    v4i c[NF];  // codes: dword j = NVFP4 block j of the stage
+    v2i s[NF];  // fp16 block scales of the lane's row (or column), blocks 0..3
+  };
+  typedef __attribute__((address_space(3))) const v4i lds_u4;
+  typedef __attribute__((address_space(3))) const v2i lds_u2;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  auto read = [&](int sl, Frag& f) {
+    const uint32_t base = ring0 + sl * SLOT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f.c[i] = *(lds_u4*)(uintptr_t)(base + (wm * 2 + i) * 1024 + lane * 16);
+      f.s[i] = *(lds_u2*)(uintptr_t)(base + AC + BC + ((wm * 2 + i) * 32 + lr) * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+      f.c[2 + c] = *(lds_u4*)(uintptr_t)(base + AC + (wn * WN + c) * 1024 + lane * 16);
+      f.s[2 + c] = *(lds_u2*)(uintptr_t)(base + AC + BC + AS + ((wn * WN + c) * 32 + lr) * 8);
+    }
+  };
+
+  v16f acc[2][WN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < WN; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
+
+  auto word = [](const v4i& v, int j) { return (uint32_t)v[j]; };
+  auto half = [](const v2i& v, int j) { return (uint32_t)v[j >> 1] >> (16 * (j & 1)); };
+  auto compute = [&](const Frag& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v8h a[2], b[WN];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = fp4_expand(word(f.c[i], j), half(f.s[i], j));
+#pragma unroll
+      for (int c = 0; c < WN; ++c) b[c] = fp4_expand(word(f.c[2 + c], j), half(f.s[2 + c], j));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < WN; ++c)
+          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[c], a[i], acc[i][c], 0, 0, 0);
+    }
+  };
+
+  dma(0, 0);
+  dma(1, 1);
+  wait_vm0();
+  barrier_lds();
+  Frag F0, F1;
+  read(0, F0);
+  // Two stages per iteration (Q is even), so each fragment set keeps its registers.
+  for (int t = 0; t < Q; t += 2) {
+    if (t > 0) {
+      wait_vm0();
+      barrier_lds();
+    }
+    if (t + 2 < Q) dma(t + 2, (t + 2) % 3);
+    read((t + 1) % 3, F1);
+    compute(F0);
+    wait_vm0();
+    barrier_lds();
+    if (t + 3 < Q) dma(t + 3, (t + 3) % 3);
+    if (t + 2 < Q) read((t + 2) % 3, F0);
+    compute(F1);
+  }
+  wait_vm0();
+  barrier_lds();  // every wave is past its operand reads: the ring is free for staging
+
+  // Epilogue: acc * g, + U @ L2t^T (U split into three bf16 terms), + bias, then (QKV
+  // mode) the per-head norm and rotation, and bf16 stores through a per-wave LDS tile.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rowb = row0 + wm * 64 + 32 * i;
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+      const int colb = col0 + (wn * WN + c) * 32;
+      v16f v = acc[i][c];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] *= g;
+      for (int kk = 0; kk < rank; kk += 16) {
+        // U = sum of the quantizer's k-split partials, added in order
+        float uf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < nsplit; ++sp) {
+          // fragment layout: ranks 0-3 of the lane's eight, then 4-7 one KiB further
+          const float* up = U + u_frag_index(sp, rowb + lr, kk + 8 * lh, M_pad, rank);
+          const float4 u0 = *reinterpret_cast<const float4*>(up);
+          const float4 u1 = *reinterpret_cast<const float4*>(up + 256);
+          uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w;
+          uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z; uf[7] += u1.w;
+        }
+        v8bf hi, mid, lo;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const Bf16x3 s3 = split3_bf16(uf[q]);
+          hi[q] = s3.h;
+          mid[q] = s3.m;
+          lo[q] = s3.l;
+        }
+        const uint4 lb = *reinterpret_cast<const uint4*>(L2t + (size_t)(colb + lr) * rank + kk + 8 * lh);
+        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), hi, v, 0, 0, 0);
+        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), mid, v, 0, 0, 0);
+        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lb), lo, v, 0, 0, 0);
+      }
+      if (bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(bias + colb + 8 * q + 4 * lh);
+          v[4 * q + 0] += __uint_as_float(b2.x << 16);
+          v[4 * q + 1] += __uint_as_float(b2.x & 0xFFFF0000u);
+          v[4 * q + 2] += __uint_as_float(b2.y << 16);
+          v[4 * q + 3] += __uint_as_float(b2.y & 0xFFFF0000u);
+        }
+      }
+      acc[i][c] = v;
+    }
+  }
+  if constexpr (EPI == kEpiQkNormRope) {
+    // Q and K tiles (the first two thirds of the columns) are one head each: the lane
+    // pair (l, l + 32) holds one row's 32 + 32 columns of the wave, the partner wave
+    // (wave ^ 1, same rows) the other 64.  Tile-uniform branch around the barrier.
+    const int third = N / 3;
+    if (col0 < 2 * third) {
+      const uint16_t* nw = col0 < third ? qk.norm_q : qk.norm_k;
+      float ss[2] = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < WN; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss[i] = fmaf(acc[i][c][e], acc[i][c][e], ss[i]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ss[i] += __shfl_xor(ss[i], 32);
+      if (lh == 0) {
+        red[wave * 64 + lr] = ss[0];
+        red[wave * 64 + 32 + lr] = ss[1];
+      }
+      barrier_lds();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float inv = 1.0f / sqrtf((ss[i] + red[(wave ^ 1) * 64 + 32 * i + lr]) * (1.0f / 128.0f) +
+                                       qk.eps);
+        const int row = min(row0 + wm * 64 + 32 * i + lr, M - 1);  // pad rows are not stored
+#pragma unroll
+        for (int c = 0; c < WN; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ch = wn * 64 + 32 * c + 8 * q + 4 * lh;  // channel of element 4q
+            const uint2 w2 = *reinterpret_cast<const uint2*>(nw + ch);
+            const float w[4] = {__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xFFFF0000u),
+                                __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xFFFF0000u)};
+            const float4 cs = *reinterpret_cast<const float4*>(qk.rope + (size_t)row * 128 + ch);
+            float n[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) n[p] = acc[i][c][4 * q + p] * inv * w[p];
+            acc[i][c][4 * q + 0] = n[0] * cs.x - n[1] * cs.y;
+            acc[i][c][4 * q + 1] = n[1] * cs.x + n[0] * cs.y;
+            acc[i][c][4 * q + 2] = n[2] * cs.z - n[3] * cs.w;
+            acc[i][c][4 * q + 3] = n[3] * cs.z + n[2] * cs.w;
+          }
+      }
+    }
+  }
+  // bf16 stores: each 32 x 32 block through the wave's LDS tile (rows of 80 B), then 16
+  // bytes per lane, four lanes per row
+  uint16_t* tile = reinterpret_cast<uint16_t*>(ring) + wave * (32 * 40);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rowb = row0 + wm * 64 + 32 * i;
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+      const int colb = col0 + (wn * WN + c) * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float v = acc[i][c][4 * q + p];
+          h[p] = f32_to_bf16_rne(EPI == kEpiGelu ? gelu_f32(v) : v);
+        }
+        *reinterpret_cast<uint2*>(tile + lr * 40 + 8 * q + 4 * lh) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int qd = lane + 64 * t;
+        const int rin = qd >> 2, ch = qd & 3;
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + rin * 40 + ch * 8);
+        const int row = rowb + rin;
+        if (row < M) *reinterpret_cast<uint4*>(Y + (size_t)row * N + colb + ch * 8) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_k2_fp4(const uint8_t* A, const uint16_t* sA, const float* U, int nsplit,
+                         const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
+                         const uint16_t* bias, float g, uint16_t* Y, int M, int N, int K,
+                         int M_pad, int rank, int epi, const QkEpi& qk, hipStream_t st,
+                         hipEvent_t ev0, hipEvent_t ev1) {
+  if (M_pad % 256 != 0 || N % 128 != 0 || K % 128 != 0) return hipErrorInvalidValue;
+  if (epi == kEpiQkNormRope && (N % 384 != 0 || !qk.norm_q || !qk.norm_k || !qk.rope))
+    return hipErrorInvalidValue;
+  const bool wide = N % 192 == 0 && epi != kEpiQkNormRope;
+  const int bn = wide ? 192 : 128;
+  dim3 grid((N / bn) * (M_pad / 256));
+  auto k = epi == kEpiQkNormRope ? k2_gemm_fp4<2, kEpiQkNormRope>
+           : wide ? (epi == kEpiGelu ? k2_gemm_fp4<3, kEpiGelu> : k2_gemm_fp4<3, kEpiPlain>)
+                  : (epi == kEpiGelu ? k2_gemm_fp4<2, kEpiGelu> : k2_gemm_fp4<2, kEpiPlain>);
+  hipExtLaunchKernelGGL(k, grid, dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB, L2t, bias,
+                        g, Y, M, N, K, M_pad, rank, qk);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -10,9 +10,10 @@
 //       k-block kb (128 values), rank slice sl (16 ranks) and call c (0..3), lane
 //       l = 16 q + i holds lora_down[16 sl + i][128 kb + 32 q + 8 c .. + 8] (16 B), and
 //       the 64 lanes of one (kb, sl, c) are 1 KiB contiguous.
-// nvfp4: codes [N][K/2] E2M1 nibbles and scales [N][K/16] E4M3 bytes -> the exact
-//       dequantized weights e2m1 * s as bf16 [N][K] (2 and 4 significant bits: the
-//       product is a bf16 number).  An E4M3 NaN scale raises the range flag.
+// nvfp4: codes [N][K/2] E2M1 nibbles and scales [N][K/16] E4M3 bytes -> the FP4
+//       lane-slot chunks of common.h (4 bits per weight, per 32 output columns and
+//       64-group) and the scales as exact fp16 values [K/64][N][4].  An E4M3 NaN scale
+//       raises the range flag.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,36 +59,48 @@ k_pair_scales(const uint16_t* __restrict__ in, uint2* __restrict__ out, int N, i
   out[t] = make_uint2((uint32_t)in[n * G + 2 * p] | ((uint32_t)in[n * G + 2 * p + 1] << 16), 0u);
 }
 
-// One thread per 8 weights (4 code bytes, one E4M3 scale).
+// NVFP4 codes: one thread per (column block, 64-group, lane slot 32 h + n % 32): the
+// four dwords of blocks 4 q + j, each the eight codes k = 64 q + 16 j + 8 h + [0, 8) of
+// column n, are 4 interchange bytes apiece (element 2i in the low nibble of byte i).
 __global__ void __launch_bounds__(256)
-k_pack_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-             uint4* __restrict__ out, int N, int K, int* __restrict__ flag) {
+k_pack_nvfp4_codes(const uint8_t* __restrict__ codes, uint4* __restrict__ out, int N, int K) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)N * K / 8;
-  if (t >= total) return;
-  const int64_t n = t / (K / 8), k8 = t % (K / 8);
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + 4 * k8);
-  const uint32_t sc = scales[n * (K / 16) + k8 / 2];
-  if ((sc & 0x7Fu) == 0x7Fu) atomicOr(flag, 1);
-  const uint32_t e = (sc >> 3) & 15u, m = sc & 7u;
-  float s = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  if (sc & 0x80u) s = -s;
-  uint32_t o[4];
+  const int Q = K >> 6;
+  if (t >= (int64_t)N * Q * 2) return;
+  const int slot = (int)(t & 63), h = slot >> 5;
+  const int64_t rest = t >> 6;  // (column block, group)
+  const int q = (int)(rest % Q);
+  const int64_t n = (rest / Q) * 32 + (slot & 31);
+  const uint8_t* src = codes + n * (K / 2) + 32 * q + 4 * h;
+  uint32_t w[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t half[2];
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint32_t*>(src + 8 * j);
+  out[t] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// NVFP4 scales: one thread per (64-group q, column n): the four E4M3 scales of the
+// group as their exact fp16 values, at [q][n][0..3]; a NaN code raises the flag.
+__global__ void __launch_bounds__(256)
+k_pack_nvfp4_scales(const uint8_t* __restrict__ scales, uint2* __restrict__ out, int N, int K,
+                    int* __restrict__ flag) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int Q = K >> 6;
+  if (t >= (int64_t)N * Q) return;
+  const int64_t q = t / N, n = t % N;
+  const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(scales + n * (K / 16) + 4 * q);
+  uint32_t h[4];
+  bool nan = false;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t c = (w >> (4 * (2 * p + h))) & 15u;
-      const uint32_t mag = c & 7u;
-      const float a = mag < 4 ? 0.5f * (float)mag
-                              : (float)(2u << ((mag - 4u) >> 1)) * (1.0f + 0.5f * (float)(mag & 1u));
-      const float v = (c & 8u) ? -(a * s) : a * s;
-      half[h] = __float_as_uint(v) >> 16;
-    }
-    o[p] = half[0] | (half[1] << 16);
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sc = (sc4 >> (8 * j)) & 0xFFu;
+    nan |= (sc & 0x7Fu) == 0x7Fu;
+    const uint32_t e = (sc >> 3) & 15u, m = sc & 7u;
+    float s = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    if (sc & 0x80u) s = -s;
+    h[j] = __builtin_bit_cast(uint16_t, (_Float16)s);  // exact: E4M3 values are fp16 numbers
   }
-  out[t] = make_uint4(o[0], o[1], o[2], o[3]);
+  out[t] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  if (nan) atomicOr(flag, 1);
 }
 
 // One thread per 16-byte unit of the packed lora_down.
@@ -129,12 +142,15 @@ hipError_t launch_pack_lora_down(const uint16_t* in, uint16_t* out, int rank, in
   return hipGetLastError();
 }
 
-hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
-                             int N, int K, hipStream_t st) {
+hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint8_t* out_codes,
+                             uint16_t* out_scales, int* flag, int N, int K, hipStream_t st) {
   hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
-  const int64_t total = (int64_t)N * K / 8;
-  hipLaunchKernelGGL(k_pack_nvfp4, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, codes,
-                     scales, reinterpret_cast<uint4*>(out), N, K, flag);
+  const int64_t tc = (int64_t)N * (K / 64) * 2;
+  hipLaunchKernelGGL(k_pack_nvfp4_codes, dim3((unsigned)((tc + 255) / 256)), dim3(256), 0, st, codes,
+                     reinterpret_cast<uint4*>(out_codes), N, K);
+  const int64_t ts = (int64_t)N * (K / 64);
+  hipLaunchKernelGGL(k_pack_nvfp4_scales, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
+                     scales, reinterpret_cast<uint2*>(out_scales), N, K, flag);
   return hipGetLastError();
 }
 

@@ -63,10 +63,12 @@ hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const ui
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                            hipEvent_t ev1 = nullptr);
 
-hipError_t launch_k2_bf16(const uint16_t* A, const float* U, int nsplit, const uint16_t* B,
-                          const uint16_t* L2t, const uint16_t* bias, float g, uint16_t* Y, int M,
-                          int N, int K, int M_pad, int rank, int epi, const QkEpi& qk,
-                          hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// NVFP4 GEMM on 4-bit operands (FP4 lane slots and fp16 block scales, common.h).
+hipError_t launch_k2_fp4(const uint8_t* A, const uint16_t* sA, const float* U, int nsplit,
+                         const uint8_t* B, const uint16_t* sB, const uint16_t* L2t,
+                         const uint16_t* bias, float g, uint16_t* Y, int M, int N, int K,
+                         int M_pad, int rank, int epi, const QkEpi& qk, hipStream_t st,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc, const uint8_t* Z,
                          const uint16_t* bias, uint16_t* Y, int M, int N, int K, hipStream_t st,
@@ -74,8 +76,10 @@ hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc
 
 hipError_t launch_pack_lora_down(const uint16_t* in, uint16_t* out, int rank, int K, hipStream_t st);
 
-hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int* flag,
-                             int N, int K, hipStream_t st);
+// NVFP4 weights: interchange codes [N][K/2] and E4M3 scales [N][K/16] -> FP4 lane-slot
+// chunks and fp16 scales [K/64][N][4] (common.h); an E4M3 NaN scale raises *flag.
+hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint8_t* out_codes,
+                             uint16_t* out_scales, int* flag, int N, int K, hipStream_t st);
 
 hipError_t launch_pack_int4(const uint8_t* codes, const uint16_t* scales, uint8_t* out_codes,
                             void* out_scales, int* flag, int N, int K, hipStream_t st);

@@ -158,10 +158,10 @@ WsLayout ws_layout(const svdq_config* c, int64_t M, int64_t K) {
   L.M_pad = round_up(M, 256);
   const int64_t G = K / c->group_size;
   // int4: GEMM A operand as E2M3 lane slots, 6 bits per value (3/4 byte), scale
-  // records [G][M_pad] (8 bytes); nvfp4: the exact dequantized operand in bf16
-  // [M_pad][K], no scales
-  const size_t codes = nv ? (size_t)(L.M_pad * K * 2) : (size_t)(L.M_pad * K * 3 / 4);
-  const size_t scales = nv ? 0 : (size_t)(G * L.M_pad * 8);
+  // records [G][M_pad] (8 bytes); nvfp4: E2M1 codes in FP4 lane slots (1/2 byte per
+  // value) and fp16 block scales [K/64][M_pad][4] (1/8 byte per value)
+  const size_t codes = nv ? (size_t)(L.M_pad * K / 2) : (size_t)(L.M_pad * K * 3 / 4);
+  const size_t scales = nv ? (size_t)(L.M_pad * K / 8) : (size_t)(G * L.M_pad * 8);
   // fp32 partial U per k-split of the quantizer
   const size_t lora = (size_t)(svdq::k1_splits((int)K) * L.M_pad * c->rank * 4);
   L.codes = 0;
@@ -259,11 +259,12 @@ size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N, si
   }
   const int64_t G = K / cfg->group_size;
   // int4: E2M3 lane slots (3/4 byte per weight) and [G/2][N] 8-byte scale records,
-  // one per pair of groups; nvfp4: exact dequantized bf16 weights [N][K]; both with a
-  // 256-byte range-flag trailer
+  // one per pair of groups; nvfp4: E2M1 codes in FP4 lane slots (1/2 byte per weight)
+  // and fp16 block scales [K/64][N][4] (1/8 byte per weight); both with a 256-byte
+  // trailer (the range flag)
   const bool nv = cfg->precision == SVDQ_NVFP4;
-  const size_t cb = nv ? (size_t)(N * K * 2) : (size_t)(N * K * 3 / 4);
-  const size_t sb = nv ? 256 : (size_t)round_up(G / 2 * N * 8, 256) + 256;
+  const size_t cb = nv ? (size_t)(N * K / 2) : (size_t)(N * K * 3 / 4);
+  const size_t sb = (size_t)round_up(nv ? N * K / 8 : G / 2 * N * 8, 256) + 256;
   if (codes_bytes) *codes_bytes = cb;
   if (scales_bytes) *scales_bytes = sb;
   return cb + sb;
@@ -283,11 +284,11 @@ svdq_status svdq_pack_weight(const svdq_config* cfg, int64_t K, int64_t N, const
   const int64_t G = K / cfg->group_size;
   const bool nv = cfg->precision == SVDQ_NVFP4;
   int* flag = reinterpret_cast<int*>(static_cast<uint8_t*>(packed_scales) +
-                                     (nv ? 0 : round_up(G / 2 * N * 8, 256)));
+                                     round_up(nv ? N * K / 8 : G / 2 * N * 8, 256));
   if (nv)
     SVDQ_TRY(hip_check(svdq::launch_pack_nvfp4(codes, static_cast<const uint8_t*>(scales),
-                                                reinterpret_cast<uint16_t*>(packed_codes), flag,
-                                                (int)N, (int)K, stream),
+                                                packed_codes, static_cast<uint16_t*>(packed_scales),
+                                                flag, (int)N, (int)K, stream),
                        "pack kernel launch"));
   else
     SVDQ_TRY(hip_check(svdq::launch_pack_int4(codes, static_cast<const uint16_t*>(scales),
@@ -424,18 +425,18 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
   if (nv) {
     SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(true, x, (int)M, (int)w->K, w->smooth,
                                               cfg->rank ? w->lora_down : nullptr, cfg->rank,
-                                              act_global, a_codes, nullptr,
+                                              act_global, a_codes, ws + L.scales,
                                               cfg->rank ? a_lora : nullptr, (int)L.M_pad, stream,
                                               e1.start, e1.end),
                        "quantize kernel launch"));
     const EvPair e2 = timer_kernel();
     const float g = act_global * w->w_global;
-    SVDQ_TRY(hip_check(svdq::launch_k2_bf16(reinterpret_cast<const uint16_t*>(a_codes), a_lora,
-                                             svdq::k1_splits((int)w->K),
-                                             reinterpret_cast<const uint16_t*>(w->qweight),
-                                             w->lora_up, w->bias, g, y, (int)M, (int)w->N,
-                                             (int)w->K, (int)L.M_pad, cfg->rank, epi, qk, stream,
-                                             e2.start, e2.end),
+    SVDQ_TRY(hip_check(svdq::launch_k2_fp4(a_codes, reinterpret_cast<const uint16_t*>(ws + L.scales),
+                                            a_lora, svdq::k1_splits((int)w->K), w->qweight,
+                                            static_cast<const uint16_t*>(w->wscales), w->lora_up,
+                                            w->bias, g, y, (int)M, (int)w->N, (int)w->K,
+                                            (int)L.M_pad, cfg->rank, epi, qk, stream, e2.start,
+                                            e2.end),
                        "gemm kernel launch"));
     return ok();
   }
