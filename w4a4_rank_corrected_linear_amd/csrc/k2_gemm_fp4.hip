@@ -24,11 +24,12 @@
 // block (element 4 q + p).  A stage is one 64-group of k (four NVFP4 blocks).  A 3-slot
 // LDS ring holds per stage the eight activation code chunks (8 KiB), the weight code
 // chunks (BN/32 KiB) and both tiles' scales (8 bytes per row or column), copied by LDS
-// DMA two stages ahead; at the top of stage t every wave waits for its own copies of
-// stage t+1, one barrier publishes them and frees the slot of stage t+2, and the
-// fragments of stage t+1 (one 16-byte code read and one 8-byte scale read per row or
-// column block) are read into registers while stage t is computed.  The tile order is
-// XCD-aware (tile_coords in k2_common.h).
+// DMA two stages ahead.  Activation operands are expanded per wave, in registers
+// (each is used by the two waves of a row range); weight operands (used by four waves)
+// are expanded once per workgroup, a stage ahead and split evenly over the waves, into
+// one of two fp16 LDS tiles in the MFMA's operand order, from which every wave reads
+// its stage's fragments.  One barrier per stage.  The tile order is XCD-aware
+// (tile_coords in k2_common.h).
 //
 // Epilogues: + bias and the bf16 store; the same with the exact GELU before the
 // rounding; or the fused QKV epilogue (128-wide tiles, one head each: per-row RMSNorm
@@ -83,37 +84,61 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   const int rb0 = row0 >> 5, cb0 = col0 >> 5;
   const int Q = K >> 6;  // stages (64-groups); K is a multiple of 128, so Q is even
 
-  // Copies of stage s into slot sl: wave w copies activation chunk rb0 + w; waves below
-  // CB weight chunk cb0 + w; the others the scale rows of the stage (activations: 2
-  // KiB, weights: BS bytes), 1 KiB per copy instruction.
+  // Copies of a stage: wave w copies activation chunk rb0 + w; waves below CB weight
+  // chunk cb0 + w; the others the stage's scale rows (activations: 2 KiB, weights: BS
+  // bytes) as up to two 1 KiB jobs each.  Every source pointer is formed once and
+  // advances by a fixed stride per stage; the destinations are fixed offsets into the
+  // slot (LDS base in M0).
   const uint32_t voff = lane * 16;
-  auto dma = [&](int s, int sl) {
-    uint8_t* base = ring + sl * SLOT;
-    dma16(voff, A + ((size_t)(rb0 + wave) * Q + s) * 1024, lds_addr(base + wave * 1024));
-    if (wave < CB) {
-      dma16(voff, B + ((size_t)(cb0 + wave) * Q + s) * 1024, lds_addr(base + AC + wave * 1024));
+  constexpr int JOBS = 2 + (BS + 1023) / 1024;  // scale jobs: A KiB 0, 1; B KiB 0 (, 1)
+  const uint8_t* srcA = A + (size_t)(rb0 + wave) * Q * 1024;
+  const uint8_t* srcB = B + (size_t)(cb0 + (wave < CB ? wave : 0)) * Q * 1024;
+  const uint8_t* srcS[2] = {nullptr, nullptr};
+  uint32_t dstS[2] = {0, 0};
+  size_t strideS[2] = {0, 0};
+  bool partS[2] = {false, false};
+  int njobs = 0;
+  for (int j = wave - CB, n = 0; wave >= CB && j < JOBS && n < 2; j += 8 - CB, ++n) {
+    if (j < 2) {
+      srcS[n] = reinterpret_cast<const uint8_t*>(sA + (size_t)row0 * 4) + j * 1024;
+      dstS[n] = AC + BC + j * 1024;
+      strideS[n] = (size_t)M_pad * 8;
     } else {
-      const uint8_t* sa = reinterpret_cast<const uint8_t*>(sA + ((size_t)s * M_pad + row0) * 4);
-      const uint8_t* sb = reinterpret_cast<const uint8_t*>(sB + ((size_t)s * N + col0) * 4);
-      constexpr int JOBS = 2 + (BS + 1023) / 1024;
-      for (int j = wave - CB; j < JOBS; j += 8 - CB) {
-        if (j < 2) {
-          dma16(voff, sa + j * 1024, lds_addr(base + AC + BC + j * 1024));
-        } else {
-          const int kb = j - 2;
-          if (kb * 1024 + (int)voff < BS) dma16(voff, sb + kb * 1024, lds_addr(base + AC + BC + AS + kb * 1024));
-        }
-      }
+      srcS[n] = reinterpret_cast<const uint8_t*>(sB + (size_t)col0 * 4) + (j - 2) * 1024;
+      dstS[n] = AC + BC + AS + (j - 2) * 1024;
+      strideS[n] = (size_t)N * 8;
+      partS[n] = (j - 2) * 1024 + 1024 > BS;  // the last weight-scale KiB is partial
     }
+    njobs = n + 1;
+  }
+  const bool lane_in_part = (int)voff < BS % 1024;
+  auto dma = [&](int s, int sl) {
+    const uint32_t base = lds_addr(ring) + sl * SLOT;
+    dma16(voff, srcA + (size_t)s * 1024, base + wave * 1024);
+    if (wave < CB) dma16(voff, srcB + (size_t)s * 1024, base + AC + wave * 1024);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      if (n < njobs && (!partS[n] || lane_in_part))
+        dma16(voff, srcS[n] + (size_t)s * strideS[n], base + dstS[n]);
   };
 
+  // fp16 weight operand tiles, two buffers: fragment (column block cb, block j) is
+  // 1 KiB, lane l's 16 bytes at (cb 4 + j) KiB + 16 l (the MFMA's operand order)
+  constexpr int W16 = CB * 4 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t w16[2 * W16];
+
   struct Frag {
-    v4i c[NF];  // codes: dword j = NVFP4 block j of the stage
-    v2i s[NF];  // fp16 block scales of the lane's row (or column), blocks 0..3
+    v4i c[2];  // activation codes of the wave's two row blocks: dword j = block j
+    v2i s[2];  // their fp16 block scales, blocks 0..3
   };
   typedef __attribute__((address_space(3))) const v4i lds_u4;
   typedef __attribute__((address_space(3))) const v2i lds_u2;
+  typedef __attribute__((address_space(3))) const uint32_t lds_u1;
+  typedef __attribute__((address_space(3))) const uint16_t lds_h1;
+  typedef __attribute__((address_space(3))) const v8h lds_h8;
+  typedef __attribute__((address_space(3))) v8h lds_h8w;
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  const uint32_t w160 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)w16;
   auto read = [&](int sl, Frag& f) {
     const uint32_t base = ring0 + sl * SLOT;
 #pragma unroll
@@ -121,10 +146,25 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
       f.c[i] = *(lds_u4*)(uintptr_t)(base + (wm * 2 + i) * 1024 + lane * 16);
       f.s[i] = *(lds_u2*)(uintptr_t)(base + AC + BC + ((wm * 2 + i) * 32 + lr) * 8);
     }
+  };
+  auto word = [](const v4i& v, int j) { return (uint32_t)v[j]; };
+  auto half = [](const v2i& v, int j) { return (uint32_t)v[j >> 1] >> (16 * (j & 1)); };
+  // The weight operand of the stage in ring slot sl, expanded once per workgroup into
+  // buffer wb.  A column half (wn) has 4 WN fragments (column block, NVFP4 block) per
+  // stage, used by its four waves (wm = 0..3); each of those waves expands WN of them
+  // (fragment q = WN wm + n: column block wn WN + q / 4, block q % 4): lane l reads
+  // dword j of lane slot l of the code chunk and the column's scale of block j, and
+  // writes the fp16 fragment.  Expanding each fragment once instead of in all four
+  // waves cuts the VALU work that would otherwise bound this kernel, and the even
+  // split keeps the two waves of every SIMD equally loaded.
+  auto expandB = [&](int sl, int wb) {
+    const uint32_t base = ring0 + sl * SLOT;
 #pragma unroll
-    for (int c = 0; c < WN; ++c) {
-      f.c[2 + c] = *(lds_u4*)(uintptr_t)(base + AC + (wn * WN + c) * 1024 + lane * 16);
-      f.s[2 + c] = *(lds_u2*)(uintptr_t)(base + AC + BC + AS + ((wn * WN + c) * 32 + lr) * 8);
+    for (int n = 0; n < WN; ++n) {
+      const int q = WN * wm + n, cb = wn * WN + (q >> 2), j = q & 3;
+      const uint32_t c = *(lds_u1*)(uintptr_t)(base + AC + cb * 1024 + lane * 16 + j * 4);
+      const uint32_t sc = *(lds_h1*)(uintptr_t)(base + AC + BC + AS + (cb * 32 + lr) * 8 + j * 2);
+      *(lds_h8w*)(uintptr_t)(w160 + wb * W16 + (cb * 4 + j) * 1024 + lane * 16) = fp4_expand(c, sc);
     }
   };
 
@@ -136,21 +176,35 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
 
-  auto word = [](const v4i& v, int j) { return (uint32_t)v[j]; };
-  auto half = [](const v2i& v, int j) { return (uint32_t)v[j >> 1] >> (16 * (j & 1)); };
-  auto compute = [&](const Frag& f) {
+  // Stage with activation fragments f and weight buffer wb: the stage's fp16 weight
+  // fragments are read at its start; block j's activation operands are expanded in
+  // registers (one set each for even and odd blocks) while block j - 1's MFMAs run;
+  // after block 0, `next` issues the next stage's activation reads and expands its
+  // weight operand into the other buffer.
+  auto compute = [&](const Frag& f, int wb, auto&& next) {
+    v8h bw[4][WN];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < WN; ++c)
+        bw[j][c] = *(lds_h8*)(uintptr_t)(w160 + wb * W16 + ((wn * WN + c) * 4 + j) * 1024 + lane * 16);
+    v8h a[2][2];
+    auto expand = [&](int j) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[j & 1][i] = fp4_expand(word(f.c[i], j), half(f.s[i], j));
+    };
+    expand(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v8h a[2], b[WN];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = fp4_expand(word(f.c[i], j), half(f.s[i], j));
-#pragma unroll
-      for (int c = 0; c < WN; ++c) b[c] = fp4_expand(word(f.c[2 + c], j), half(f.s[2 + c], j));
+      if (j < 3) expand(j + 1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int c = 0; c < WN; ++c)
-          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[c], a[i], acc[i][c], 0, 0, 0);
+          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bw[j][c], a[j & 1][i], acc[i][c], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 0) next();
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -160,20 +214,30 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   barrier_lds();
   Frag F0, F1;
   read(0, F0);
+  expandB(0, 0);
   // Two stages per iteration (Q is even), so each fragment set keeps its registers.
+  // Slots rotate 0, 1, 2: stage t in slot t % 3, tracked without a division; stage t's
+  // fp16 weights are in buffer t % 2.
+  int sl0 = 0;  // slot of stage t
   for (int t = 0; t < Q; t += 2) {
-    if (t > 0) {
-      wait_vm0();
-      barrier_lds();
-    }
-    if (t + 2 < Q) dma(t + 2, (t + 2) % 3);
-    read((t + 1) % 3, F1);
-    compute(F0);
+    const int sl1 = sl0 == 2 ? 0 : sl0 + 1, sl2 = sl1 == 2 ? 0 : sl1 + 1;
+    wait_vm0();
+    barrier_lds();  // slot of t + 1 landed, weight buffer 0 (stage t) written
+    if (t + 2 < Q) dma(t + 2, sl2);
+    compute(F0, 0, [&] {
+      read(sl1, F1);
+      expandB(sl1, 1);
+    });
     wait_vm0();
     barrier_lds();
-    if (t + 3 < Q) dma(t + 3, (t + 3) % 3);
-    if (t + 2 < Q) read((t + 2) % 3, F0);
-    compute(F1);
+    if (t + 3 < Q) dma(t + 3, sl0);
+    compute(F1, 1, [&] {
+      if (t + 2 < Q) {
+        read(sl2, F0);
+        expandB(sl2, 0);
+      }
+    });
+    sl0 = sl2;
   }
   wait_vm0();
   barrier_lds();  // every wave is past its operand reads: the ring is free for staging
