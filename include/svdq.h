@@ -142,7 +142,11 @@ svdq_status svdq_pack_lora_down(const svdq_config* cfg, int64_t K, const uint16_
 size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);
 
 /* Activation side of the layer (smoothing, low-rank down projection, quantization)
- * in the interchange layout:
+ * in the interchange layout.  Defined by the Diffusers docs "Nunchaku Lite",
+ * "Supported quantization types" table (svdq_w4a4: activations quantized to int4 in
+ * groups of 64 or to nvfp4 in blocks of 16, with the SVDQ low-rank branch) and the
+ * infolabhq tutorial's section on why 4-bit inference matters (activations, not only
+ * weights, are 4-bit); the smoothing and the unrounded U are readings of those pages.
  *   x          [M][K] bf16 activations
  *   smooth     [K] bf16 multiplier m;  lora_down [r][K] bf16 (NULL iff r == 0)
  *   act_global NVFP4 static activation scale g_x (ignored for int4)
@@ -157,8 +161,15 @@ svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t
                               const uint16_t* smooth, const uint16_t* lora_down, float act_global,
                               uint8_t* codes, void* scales, float* lora_act, hipStream_t stream);
 
-/* The whole layer: Y[M][N] (bf16) = svdq_w4a4(X[M][K]).  `workspace` holds the
- * quantized activations between the two kernels (svdq_workspace_bytes). */
+/* The whole layer: Y[M][N] (bf16) = svdq_w4a4(X[M][K]), the formula at the top of this
+ * file, as the Diffusers docs "Nunchaku Lite", "Supported quantization types" table
+ * defines svdq_w4a4 (4-bit weights and activations, int4 g64 or nvfp4 g16, plus the
+ * SVDQ low-rank correction; rank 32 in the "NunchakuLiteQuantizationConfig" example).
+ * w: the packed layer (svdq_pack_weight, svdq_pack_lora_down); x [M][K] bf16; y
+ * [M][N] bf16 out; act_global: g_x for nvfp4, ignored for int4.  `workspace` holds
+ * the quantized activations between the two kernels (svdq_workspace_bytes); the
+ * caller owns it and its contents on return are unspecified.  M >= 0 (M = 0 launches
+ * nothing); K a multiple of 128, N of 128.  Errors as in the conventions above. */
 svdq_status svdq_w4a4_linear(const svdq_config* cfg, const svdq_w4a4_weight* w,
                              const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -230,8 +241,13 @@ svdq_status svdq_qk_norm_rope_bf16(const uint16_t* x, uint16_t* y, int64_t M, in
                                    const uint16_t* norm_q, const uint16_t* norm_k, float eps,
                                    const float* rope, hipStream_t stream);
 
-/* The AWQ W4A16 comparison layer: Y[M][N] (bf16) from bf16 X[M][K].  cfg must be
- * {int4, 64, rank 0, bf16}. */
+/* The AWQ W4A16 comparison layer: Y[M][N] (bf16) from bf16 X[M][K], the formula at
+ * the top of this file.  Defined by the Diffusers docs "Nunchaku Lite", "Supported
+ * quantization types" table (awq_w4a16: int4, group 64, an INT4 weight-only AWQ-style
+ * kernel) and "NunchakuLiteQuantizationConfig" (awq_w4a16 targets keep bf16
+ * activations).  cfg must be {int4, 64, rank 0, bf16}; the weight layout is
+ * awq_w4a16_weight's; x, y device bf16, 16-byte aligned; M >= 0.  Errors as in the
+ * conventions above. */
 svdq_status awq_w4a16_linear(const svdq_config* cfg, const awq_w4a16_weight* w,
                              const uint16_t* x, int64_t M, uint16_t* y, hipStream_t stream);
 

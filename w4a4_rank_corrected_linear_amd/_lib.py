@@ -10,7 +10,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+# SVDQ_LIBRARY names another build of the same ABI (the host-ASan test build)
+LIB_PATH = os.environ.get("SVDQ_LIBRARY") or os.path.join(_HERE, "libsvdq.so")
 
 # status codes (svdq_status)
 OK, ERR_NULL, ERR_CONFIG, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP, ERR_RANGE = range(9)

@@ -107,40 +107,52 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
   const int sbase = piece < 0 ? 0 : piece * S_all / ks;                 // first stage
   const int S = piece < 0 ? S_all : (piece + 1) * S_all / ks - sbase;   // stages here
 
-  auto slotA = [&](int sl) { return ring + sl * SLOT; };
-  auto slotB = [&](int sl) { return ring + sl * SLOT + ASZ; };
-  auto slotSA = [&](int sl) { return reinterpret_cast<uint2*>(ring + sl * SLOT + ASZ + BSZ); };
-  auto slotSB = [&](int sl) { return reinterpret_cast<uint2*>(ring + sl * SLOT + ASZ + BSZ) + 2 * BM; };
 
-  // Copies of stage s: wave w copies A row-block w (3 KiB: both groups); waves below
+  // Copies of a stage: wave w copies A row-block w (3 KiB: both groups); waves below
   // CB copy B col-block w; wave CB the row scale records (2 x 2 KiB), wave CB+1 the
-  // column scale records of the group pair (BN * 8 bytes).  A 64-lane copy moves 128
-  // records.
+  // column scale records of the group pair (BN * 8 bytes).  A 64-lane copy moves 1 KiB.
+  // Every source pointer is formed once and advances by a fixed stride per stage; the
+  // KiB within a copy is a per-lane offset (voff + 1024 j) and the LDS destination (M0)
+  // a fixed offset from the slot base, so a copy costs one scalar add for M0.  (s is the
+  // stage relative to the piece's first.)
   const uint32_t voff = lane * 16;
+  const uint32_t voff1 = voff + 1024, voff2 = voff + 2048;
+  const uint32_t ring_lds = lds_addr(ring);
+  const uint8_t* pA = A + ((size_t)(rb0 + wave) * G + 2 * sbase) * 1536;
+  const uint8_t* pB = B + ((size_t)(cb0 + (wave < CB ? wave : 0)) * G + 2 * sbase) * 1536;
+  // scale records: wave CB reads group 2s at pS and group 2s+1 M_pad records further
+  // (voffS); wave CB+1 reads the BN records of pair s at pS
+  const bool sa_wave = wave == CB;
+  const uint8_t* pS = sa_wave ? reinterpret_cast<const uint8_t*>(sA + (size_t)2 * sbase * M_pad + row0)
+                              : reinterpret_cast<const uint8_t*>(sB + (size_t)sbase * N + col0);
+  const size_t strideS = sa_wave ? (size_t)2 * M_pad * 8 : (size_t)N * 8;
+  const uint32_t voffS = voff + (uint32_t)M_pad * 8;
+  const bool sb_tail_lane = lane < (BN - 128) / 2;
   auto dma = [&](int s, int sl) {
-    {
-      const uint8_t* src = A + ((size_t)(rb0 + wave) * G + 2 * (sbase + s)) * 1536;
-      const uint32_t dst = lds_addr(slotA(sl) + wave * 768);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) dma16(voff, src + t * 1024, dst + t * 1024);
-    }
+    const uint32_t base = ring_lds + sl * (SLOT * 4);
+    const uint32_t da = base + wave * 3072;
+    const uint8_t* a = pA + (size_t)s * 3072;
+    dma16(voff, a, da);
+    dma16(voff1, a, da + 1024);
+    dma16(voff2, a, da + 2048);
     if (wave < CB) {
-      const uint8_t* src = B + ((size_t)(cb0 + wave) * G + 2 * (sbase + s)) * 1536;
-      const uint32_t dst = lds_addr(slotB(sl) + wave * 768);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) dma16(voff, src + t * 1024, dst + t * 1024);
-    } else if (wave == CB) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int gl = t >> 1, part = t & 1;
-        dma16(voff, sA + (size_t)(2 * (sbase + s) + gl) * M_pad + row0 + 128 * part,
-              lds_addr(slotSA(sl) + gl * BM + 128 * part));
-      }
+      const uint32_t db = base + (ASZ + wave * 768) * 4;
+      const uint8_t* b = pB + (size_t)s * 3072;
+      dma16(voff, b, db);
+      dma16(voff1, b, db + 1024);
+      dma16(voff2, b, db + 2048);
+    } else if (sa_wave) {
+      const uint32_t ds = base + (ASZ + BSZ) * 4;
+      const uint8_t* c = pS + (size_t)s * strideS;
+      dma16(voff, c, ds);
+      dma16(voff1, c, ds + 1024);
+      dma16(voffS, c, ds + BM * 8);
+      dma16(voffS + 1024, c, ds + BM * 8 + 1024);
     } else if (wave == CB + 1) {
-      const uint2* src = sB + (size_t)(sbase + s) * N + col0;
-      const uint32_t dst = lds_addr(slotSB(sl));
-      dma16(voff, src, dst);
-      if (BN > 128 && lane < (BN - 128) / 2) dma16(voff, src + 128, dst + 1024);
+      const uint32_t ds = base + (ASZ + BSZ + 4 * BM) * 4;
+      const uint8_t* c = pS + (size_t)s * strideS;
+      dma16(voff, c, ds);
+      if (BN > 128 && sb_tail_lane) dma16(voff1, c, ds + 1024);
     }
   };
 
@@ -347,17 +359,21 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // stage t sits in slot sl0 = t % 3 (tracked without a division)
+  int sl0 = 0;
   for (int t = 0; t + 1 < S; ++t) {
+    const int sl1 = sl0 == 2 ? 0 : sl0 + 1, sl2 = sl1 == 2 ? 0 : sl1 + 1;
     if (t > 0) {
       wait_vm0();
       barrier_lds();
     }
-    if (t + 2 < S) dma(t + 2, (t + 2) % 3);
-    else if (late_seed) seed_copy(0, (t + 2) % 3);
+    if (t + 2 < S) dma(t + 2, sl2);
+    else if (late_seed) seed_copy(0, sl2);
     __builtin_amdgcn_sched_barrier(0);
-    const Bases cq = bases(t % 3), nq = bases((t + 1) % 3);
+    const Bases cq = bases(sl0), nq = bases(sl1);
 #pragma unroll
     for (int b = 0; b < NB; ++b) step(b, cq, nq, true);
+    sl0 = sl1;
   }
   {
     const int t = S - 1;
@@ -368,8 +384,8 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     // the tile's bias goes to LDS under the last stage (wave 0, 16 B per lane), and
     // the second k-split of U to the slot stage t-1 has just freed
     if (bias && wave == 0 && lane < BN / 8) dma16(voff, bias + col0, lds_addr(bias_s));
-    if (late_seed && nsplit == 2) seed_copy(1, (t + 2) % 3);
-    const Bases cq = bases(t % 3);
+    if (late_seed && nsplit == 2) seed_copy(1, sl0 == 0 ? 2 : sl0 - 1);
+    const Bases cq = bases(sl0);
 #pragma unroll
     for (int b = 0; b < NB; ++b) step(b, cq, cq, false);
     // keeps the last rescale ahead of the epilogue
