@@ -39,6 +39,17 @@ def test_awq_no_bias_wide_k():
     check_y(host_bits(y), OL.awq_w4a16_linear(li.x, awq)["r"])
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 640, 640), (1000, 768, 512), (64, 384, 384)])
+def test_awq_ragged_tiles(M, N, K):
+    """Several 256-row tiles with a partial last one: 128-wide tiles in row-major order
+    (M = 300, N = 640) and 192-wide tiles in the XCD-aware order (M = 1000, N = 768);
+    K/64 not a multiple of 8 (K = 640, 384) takes the two-group scale loads."""
+    li = I.layer_inputs(config_id=9, M=M, K=K, N=N, outlier_count=8, factor=20.0)
+    awq = P.prepare_awq(li.w, li.bias)
+    y = _dev(awq)(dev_bf16(li.x))
+    check_y(host_bits(y), OL.awq_w4a16_linear(li.x, awq)["r"])
+
+
 def test_awq_grid_exact_is_bit_exact():
     """X = small integers times 2^-3, power-of-two scales in a narrow range: every
     product and partial sum is exact in fp32, so Y equals bf16(r) bit for bit."""

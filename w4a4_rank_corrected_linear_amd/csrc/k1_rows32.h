@@ -160,10 +160,16 @@ __device__ __forceinline__ void k1_rows32(const K1Args& a) {
         ured[wave][16 * h + 4 * q + i][16 + r] = u1[h][i];
       }
     __syncthreads();
+    // the nb partials of an element are read at once, then added in wave order
     for (int t = threadIdx.x; t < 32 * rank; t += 64 * NW) {
       const int rr = t / rank, cc = t % rank;
-      float v = ured[0][rr][cc];
-      for (int w = 1; w < nb; ++w) v += ured[w][rr][cc];
+      float p[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) p[w] = w < nb ? ured[w][rr][cc] : 0.f;
+      float v = p[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w)
+        if (w < nb) v += p[w];
       a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)] = v;
     }
   }

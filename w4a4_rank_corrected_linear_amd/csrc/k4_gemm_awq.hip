@@ -3,195 +3,313 @@
 //   Y[m,n] = bf16( sum_g s[n,g] D_g[m,n] + b[n] ),  D_g = sum_{k in g} x[m,k] (q[n,k] - z[n,g])
 //
 // (Diffusers docs "Nunchaku Lite", "Supported quantization types": awq_w4a16, INT4
-// weight-only, group 64.)  The weights stay 4-bit in HBM and in LDS; per stage (one
-// 64-group) the workgroup expands its 128 x 64 weight slice into the exact bf16
-// values q - z (integers in [-15, 15]), the bf16 MFMA forms D_g in fp32, and one fp32
-// FMA per output element applies the group scale: acc = fma(s, D_g, acc).
+// weight-only, group 64.)  The weights stay 4-bit in HBM and in LDS.  Per 64-group the
+// workgroup expands its BN x 64 weight slice into the exact bf16 values q - z (integers
+// in [-15, 15]), the bf16 MFMA forms D_g in fp32 (four k-chunks of 16 chained on one
+// accumulator), and one fp32 FMA per output element applies the group scale:
+// acc = fma(s, D_g, acc).
 //
-// Tiling: 256 threads (2 x 2 waves), tile 128 x 128, wave tile 64 x 64 (2 x 2 blocks
-// of v_mfma_f32_32x32x16_bf16), two workgroups per CU.  X tiles (bf16) and the raw
-// weight nibbles are copied into LDS by global_load_lds, double-buffered; rows of X
-// past M read row M - 1 (their outputs are not stored).  The bf16 tiles use the
-// 16-byte unit swizzle u = row * 8 + (c ^ (row & 7)) (c = k / 8 within the group).
+// Tiling: one 512-thread workgroup (8 waves, two per SIMD) per CU, tile 256 x BN with
+// BN = 64 WN (192 where N allows, else 128), wave tile 64 x BN/2 (2 x WN blocks of
+// 32 x 32).  The accumulators are held in the MFMA's own orientation: lane l % 32 is
+// the output column, so a block's group scale and bias are one value per lane.  A
+// stage is one 64-group.  LDS holds two activation tiles (256 x 64 bf16, 16-byte units
+// swizzled as u = row 8 + (c ^ (row & 7)), c = k / 8), three raw weight slices (BN x
+// 32 bytes of nibbles) and two expanded weight tiles (BN x 64 bf16, the same swizzle
+// by column).  At the top of stage t every wave waits for its own copies, one barrier
+// publishes them together with the weight tile expanded during stage t - 1, and the
+// copies of stage t + 1's activations and stage t + 2's nibbles start (LDS DMA, 16
+// bytes per lane), after the global loads of the next group's scales and the zero
+// points of the group after it.  A wave then reads its stage's activation fragments (kept
+// in registers for the stage), then per column block its weight fragments, the MFMAs,
+// the scale FMAs and one unit of its share of stage t + 1's weight expansion.
+// Rows of X at or past M read row M - 1 (their outputs are not stored).  The tile
+// order is XCD-aware (tile_coords in k2_common.h).
 #include "common.h"
+#include "k2_common.h"
 #include "kernels.h"
 
 namespace svdq {
 
-__global__ void __launch_bounds__(256, 2)
+template <int WN, int W>
+__global__ void __launch_bounds__(512, 1)
 k4_gemm_awq(const uint16_t* __restrict__ X, const uint8_t* __restrict__ Q,
             const uint16_t* __restrict__ Sc, const uint8_t* __restrict__ Z,
             const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K) {
-  constexpr int BM = 128, BN = 128;
-  constexpr int TILE = 128 * 64;  // bf16 elements of a 128 x 64 tile
-  __shared__ __attribute__((aligned(16))) uint16_t A0[TILE], A1[TILE], Bt[TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t Q0[128 * 32], Q1[128 * 32];
+  constexpr int BM = 256, BN = 64 * WN;
+  constexpr int AB = BM * 128;         // bytes of an activation tile (256 x 64 bf16)
+  constexpr int QB = BN * 32;          // bytes of a raw weight slice (BN x 64 nibbles)
+  constexpr int WB = BN * 128;         // bytes of an expanded weight tile (BN x 64 bf16)
+  constexpr int OFF_Q = 2 * AB, OFF_W = OFF_Q + 3 * QB, LDS = OFF_W + 2 * WB;
+  constexpr int UPL = WN;              // expansion units (8 values) per lane and stage
+  constexpr int TS = BN / 2 + 8;       // row pitch (bf16) of a wave's staging tile
+  static_assert(WN == 2 || WN == 3, "tile width 128 or 192");
+  static_assert(8 * 64 * TS * 2 <= LDS, "staging tiles fit in the freed LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = N / BN;
-  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  const int tiles_n = N / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * BM, col0 = tn * BN;
   const int G = K >> 6;
+  const uint32_t lds0 = lds_addr(lds);
 
-  // Per stage each wave copies 4 KiB of the X tile (4 instructions) and 1 KiB of the
-  // weight nibbles (column c's 32 bytes of group g are 16-byte units 2c and 2c + 1).
-  auto dma = [&](int g, uint16_t* Ab, uint8_t* Qb) {
+  // Copies.  Activations: wave w moves 16-byte units (4w + t) 64 + lane, t < 4, i.e.
+  // rows 32w + 8t + lane / 8, chunk (lane % 8) ^ (row % 8); the source is a fixed
+  // per-lane offset from a per-stage base.  Weight nibbles: wave j < QB / 1 KiB moves
+  // units 64 j + lane (column u / 2, half u % 2).
+  const uint8_t* xbase = reinterpret_cast<const uint8_t*>(X) + (size_t)row0 * K * 2;
+  uint32_t voffA[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int u = 64 * (4 * wave + t) + lane;
-      const int r = u >> 3, c = (u & 7) ^ (r & 7);
-      const int gr = min(row0 + r, M - 1);
-      __builtin_amdgcn_global_load_lds(X + (size_t)gr * K + 64 * g + 8 * c,
-                                       Ab + 8 * 64 * (4 * wave + t), 16, 0, 0);
-    }
-    {
-      const int u = 64 * wave + lane;
-      const int c = u >> 1, h = u & 1;
-      __builtin_amdgcn_global_load_lds(Q + (size_t)(col0 + c) * (K / 2) + 32 * g + 16 * h,
-                                       Qb + 1024 * wave, 16, 0, 0);
-    }
+  for (int t = 0; t < 4; ++t) {
+    const int r = 32 * wave + 8 * t + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    voffA[t] = (uint32_t)(min(row0 + r, M - 1) - row0) * (uint32_t)K * 2u + 16u * c;
+  }
+  const uint8_t* qbase = Q + (size_t)col0 * (K / 2);
+  const bool q_wave = wave < QB / 1024;
+  const uint32_t voffQ = (uint32_t)(((64 * wave + lane) >> 1) * (K / 2) + 16 * (lane & 1));
+  auto dma_a = [&](int g, int sl) {
+    const uint8_t* src = xbase + (size_t)g * 128;
+    const uint32_t dst = lds0 + sl * AB + wave * 4096;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(voffA[t], src, dst + 1024 * t);
+  };
+  auto dma_q = [&](int g, int sl) {
+    if (q_wave) dma16(voffQ, qbase + (size_t)g * 32, lds0 + OFF_Q + sl * QB + wave * 1024);
   };
 
-  // Expansion: thread t takes column t / 2 and 32 values of k (half t % 2 of the group).
-  const int ec = tid >> 1, eh = tid & 1;
-  auto expand = [&](const uint8_t* Qb, int z) {
-    const uint4 v = *reinterpret_cast<const uint4*>(Qb + 16 * tid);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t zb = (uint32_t)z * 0x01010101u;
+  // Expansion units of this lane: u = 64 (UPL wave + t) + lane, column u / 8, values
+  // 8 (u % 8) .. + 8 of the group.  Their zero points, and this lane's output columns'
+  // scales, are read from global memory W groups at a time (W = 8 when K / 64 allows,
+  // else 2; scales and zero points are stored column-major, [N][K/64]) into small
+  // register queues that shift by one group per stage.  The offsets are 32-bit from the
+  // tile's first column (the empty asm keeps them opaque, so the compiler does not turn
+  // them into per-lane 64-bit pointers that advance with the group).
+  constexpr int SD = W / 2;  // dwords of scales per column and load (W bf16)
+  constexpr int ZD = W / 4 > 0 ? W / 4 : 1;  // dwords of zero points per unit and load
+  const uint8_t* zbase = Z + (size_t)col0 * G;
+  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(Sc + (size_t)col0 * G);
+  uint32_t zoff[UPL], soff[WN];  // byte offsets
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      // bytes of (q + 16 - z) for the even and the odd elements: no borrows, as
-      // q + 16 - z lies in [1, 31]
-      const uint32_t ev = ((w[d] & 0x0F0F0F0Fu) | 0x10101010u) - zb;
-      const uint32_t od = (((w[d] >> 4) & 0x0F0F0F0Fu) | 0x10101010u) - zb;
-      uint32_t o[4];
+  for (int t = 0; t < UPL; ++t) zoff[t] = (uint32_t)(((64 * (UPL * wave + t) + lane) >> 3) * G);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float fe = (float)((ev >> (8 * b)) & 0xFFu) - 16.0f;
-        const float fo = (float)((od >> (8 * b)) & 0xFFu) - 16.0f;
-        o[b] = (__float_as_uint(fe) >> 16) | (__float_as_uint(fo) & 0xFFFF0000u);
+  for (int j = 0; j < WN; ++j) soff[j] = (uint32_t)(((wn * WN + j) * 32 + lr) * G * 2);
+  uint32_t sq[WN][SD], zq[UPL][ZD];
+  auto load_s = [&](int g) {  // groups g .. g + W - 1
+    const uint8_t* sg = sbase + 2 * g;
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      asm volatile("" : "+v"(soff[j]));
+      if constexpr (W == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(sg + soff[j]);
+        sq[j][0] = v.x; sq[j][1] = v.y; sq[j][2] = v.z; sq[j][3] = v.w;
+      } else {
+        sq[j][0] = *reinterpret_cast<const uint32_t*>(sg + soff[j]);
       }
-      const int c = 4 * eh + d;  // 8-value chunk within the group
-      *reinterpret_cast<uint4*>(Bt + 8 * (ec * 8 + (c ^ (ec & 7)))) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
-
-  auto frag = [&](const uint16_t* T, int row, int kk) {
-    const int c = 2 * kk + (lane >> 5);
-    return *reinterpret_cast<const v8bf*>(T + 8 * (row * 8 + (c ^ (row & 7))));
+  auto load_z = [&](int g) {
+    const uint8_t* zg = zbase + g;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+      asm volatile("" : "+v"(zoff[u]));
+      if constexpr (W == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(zg + zoff[u]);
+        zq[u][0] = v.x; zq[u][1] = v.y;
+      } else {
+        zq[u][0] = *reinterpret_cast<const uint16_t*>(zg + zoff[u]);
+      }
+    }
+  };
+  // the queue heads, then a shift by one group
+  auto pop_s = [&](float (&sv)[WN]) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      sv[j] = __uint_as_float(sq[j][0] << 16);
+#pragma unroll
+      for (int d = 0; d < SD - 1; ++d) sq[j][d] = __builtin_amdgcn_alignbit(sq[j][d + 1], sq[j][d], 16);
+      sq[j][SD - 1] >>= 16;
+    }
+  };
+  auto pop_z = [&](uint32_t (&zv)[UPL]) {
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+      zv[u] = zq[u][0] & 0xFFu;
+#pragma unroll
+      for (int d = 0; d < ZD - 1; ++d) zq[u][d] = __builtin_amdgcn_alignbit(zq[u][d + 1], zq[u][d], 8);
+      zq[u][ZD - 1] >>= 8;
+    }
+  };
+  // q - z as bf16 for the 8 nibbles of dword w (value 2i in the low nibble of byte i):
+  // the bytes q + 16 - z lie in [1, 31], so one subtraction serves four values with no
+  // borrow, and the float of each byte minus 16 is the exact small integer.
+  auto raw = [&](int g_slot, int t) {
+    const int u = 64 * (UPL * wave + t) + lane;
+    return *reinterpret_cast<const uint32_t*>(lds + OFF_Q + g_slot * QB + (u >> 3) * 32 + 4 * (u & 7));
+  };
+  auto expand = [&](uint32_t w, int buf, int t, uint32_t z) {
+    const int u = 64 * (UPL * wave + t) + lane;
+    const int c = u >> 3, h = u & 7;
+    const uint32_t zb = z * 0x01010101u;
+    const uint32_t ev = ((w & 0x0F0F0F0Fu) | 0x10101010u) - zb;
+    const uint32_t od = (((w >> 4) & 0x0F0F0F0Fu) | 0x10101010u) - zb;
+    uint32_t o[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float fe = (float)((ev >> (8 * b)) & 0xFFu) - 16.0f;
+      const float fo = (float)((od >> (8 * b)) & 0xFFu) - 16.0f;
+      o[b] = (__float_as_uint(fe) >> 16) | (__float_as_uint(fo) & 0xFFFF0000u);
+    }
+    *reinterpret_cast<uint4*>(lds + OFF_W + buf * WB + 16 * (c * 8 + (h ^ (c & 7)))) =
+        make_uint4(o[0], o[1], o[2], o[3]);
   };
 
-  v16f acc[2][2];
+  // Fragment addresses: lane l reads row (or column) 32 blk + l % 32, 16-byte unit
+  // (2 c + l / 32) ^ (l % 8) of k-chunk c; the per-lane part is the same for both
+  // operands.
+  uint32_t foff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) foff[c] = (uint32_t)(lr * 128 + 16 * ((2 * c + lh) ^ (lane & 7)));
+  typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
+  auto frag = [&](uint32_t base, int c) { return *(lds_v8bf*)(uintptr_t)(base + foff[c]); };
+
+  v16f acc[2][WN];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const v16f zero = {};
 
-  // this lane's output columns (one per 32-column block j) and this thread's
-  // expansion column: scales and zero points of the next group are prefetched
-  const int ocol[2] = {col0 + wn * 64 + (lane & 31), col0 + wn * 64 + 32 + (lane & 31)};
-  uint16_t s_nxt[2] = {Sc[(size_t)ocol[0] * G], Sc[(size_t)ocol[1] * G]};
-  int z_nxt = Z[(size_t)(col0 + ec) * G];
+  // prologue: the first scale and zero-point loads, activations of stage 0, nibbles of
+  // stages 0 and 1; then the expansion of stage 0's weights
+  load_s(0);
+  load_z(0);
+  dma_a(0, 0);
+  dma_q(0, 0);
+  if (G > 1) dma_q(1, 1);
+  wait_vm0();
+  barrier_lds();
+  uint32_t zc[UPL];
+  pop_z(zc);  // zero points of group 0; the queue head is now group 1
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) expand(raw(0, u), 0, u, zc[u]);
 
-  auto compute = [&](const uint16_t* Ab, float s0, float s1) {
-    v16f d[2][2];
+  // Stage t: blocks b = 0 .. 2 WN - 1 (column block b / 2, row block b % 2) in turn:
+  // block b's four chained MFMAs, then block b - 1's scale FMAs (so they overlap the
+  // MFMA latency), and after each column block one unit of stage t + 1's weight
+  // expansion, whose nibbles were read at the top of the stage.
+  int qs1 = 1;  // raw slot of stage t + 1 (t + 1 mod 3)
+  for (int t = 0; t < G; ++t) {
+    const int qs2 = qs1 == 2 ? 0 : qs1 + 1;
+    wait_vm0();
+    barrier_lds();  // stage t's activations and expanded weights are visible to all
+    // the stage's first fragments and the expansion's nibbles are read first, so that
+    // their latency overlaps the copies issued below
+    const uint32_t abase = lds0 + (t & 1) * AB + wm * 64 * 128;
+    const uint32_t bbase = lds0 + OFF_W + (t & 1) * WB + wn * WN * 32 * 128;
+    v8bf af[2][4], bfc[4], bfn[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bfc[c] = frag(bbase, c);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) d[i][j] = zero;
+      for (int c = 0; c < 4; ++c) af[i][c] = frag(abase + i * 32 * 128, c);
+    uint32_t qraw[UPL];
+    if (t + 1 < G) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      v8bf a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = frag(Ab, wm * 64 + 32 * i + (lane & 31), kk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = frag(Bt, wn * 64 + 32 * j + (lane & 31), kk);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          d[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], d[i][j], 0, 0, 0);
+      for (int u = 0; u < UPL; ++u) qraw[u] = raw(qs1, u);
     }
+    float sv[WN];
+    pop_s(sv);                                   // scales of group t
+    if ((t + 1) % W == 0 && t + 1 < G) load_s(t + 1);
+    pop_z(zc);                                   // zero points of group t + 1
+    if ((t + 2) % W == 0 && t + 2 < G) load_z(t + 2);
+    if (t + 1 < G) dma_a(t + 1, (t + 1) & 1);
+    if (t + 2 < G) dma_q(t + 2, qs2);
+
+    v16f d[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int b = 0; b <= 2 * WN; ++b) {
+      const int j = b >> 1, i = b & 1;
+      if (b < 2 * WN) {
+        if (i == 1 && j + 1 < WN) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        acc[i][0][e] = __builtin_fmaf(s0, d[i][0][e], acc[i][0][e]);
-        acc[i][1][e] = __builtin_fmaf(s1, d[i][1][e], acc[i][1][e]);
+          for (int c = 0; c < 4; ++c) bfn[c] = frag(bbase + (j + 1) * 32 * 128, c);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          d[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][c], bfc[c], c == 0 ? zero : d[i], 0, 0, 0);
       }
-  };
-
-  auto sync_all = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-  };
-
-  // Stage g: wait for its copies, expand the weights, synchronize, start the next
-  // stage's copies (the compiler completes outstanding memory operations before a
-  // barrier, so they are issued after the stage's last one), then the MFMAs and the
-  // scale FMAs.
-  auto stage = [&](int g, uint16_t* Ab, uint8_t* Qb, uint16_t* An, uint8_t* Qn) {
-    const float s0 = bf16_to_f32(s_nxt[0]), s1 = bf16_to_f32(s_nxt[1]);
-    const int z = z_nxt;
-    sync_all();
-    expand(Qb, z);
-    sync_all();
-    if (g + 1 < G) {
-      dma(g + 1, An, Qn);
-      s_nxt[0] = Sc[(size_t)ocol[0] * G + g + 1];
-      s_nxt[1] = Sc[(size_t)ocol[1] * G + g + 1];
-      z_nxt = Z[(size_t)(col0 + ec) * G + g + 1];
+      if (b > 0) {
+        const int pj = (b - 1) >> 1, pi = (b - 1) & 1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[pi][pj][e] = __builtin_fmaf(sv[pj], d[pi][e], acc[pi][pj][e]);
+        // the rescale stays here (not sunk to the end of the stage, which would keep
+        // every block's D alive at once)
+        asm volatile("" : "+v"(acc[pi][pj]));
+        if (pi == 1 && t + 1 < G) expand(qraw[pj], (t + 1) & 1, pj, zc[pj]);
+      }
+      if (i == 1 && b < 2 * WN) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bfc[c] = bfn[c];
+      }
     }
-    compute(Ab, s0, s1);
-  };
-
-  dma(0, A0, Q0);
-  for (int g = 0; g < G; g += 2) {
-    stage(g, A0, Q0, A1, Q1);
-    if (g + 1 < G) stage(g + 1, A1, Q1, A0, Q0);
+    qs1 = qs2;
   }
-  sync_all();
+  wait_vm0();
+  barrier_lds();  // every wave is done with the tiles: the LDS is free for staging
 
-  // Epilogue: + bias, bf16 stores through a per-wave LDS tile (rows of 80 B).
-  const int lr = lane & 31, lh = lane >> 5;
-  uint16_t* tile = A0 + wave * (32 * 40);
+  // Epilogue: + bias, bf16, through a per-wave staging tile (64 rows x BN/2) so that
+  // each row segment is written with 16-byte stores.  Element e of lane l is row
+  // 8 (e / 4) + 4 (l / 32) + e % 4 of its block, column l % 32.
+  uint16_t* tile = reinterpret_cast<uint16_t*>(lds) + wave * (64 * TS);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rowb = row0 + wm * 64 + 32 * i;
+  for (int j = 0; j < WN; ++j) {
+    const int col = (wn * WN + j) * 32 + lr;
+    const float bv = bias ? bf16_to_f32(bias[col0 + col]) : 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int colb = col0 + wn * 64 + 32 * j;
-      const float bv = bias ? bf16_to_f32(bias[colb + lr]) : 0.f;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
-        tile[rin * 40 + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][e] + bv);
+        const int r = 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+        tile[r * TS + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][e] + bv);
       }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int UPR = BN / 16;  // 16-byte units per staged row
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int qd = lane + 64 * t;
-        const int rin = qd >> 2, ch = qd & 3;
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + rin * 40 + ch * 8);
-        const int row = rowb + rin;
-        if (row < M) *reinterpret_cast<uint4*>(Y + (size_t)row * N + colb + ch * 8) = v;
-      }
-    }
+  for (int k = 0; k < UPR; ++k) {
+    const int idx = lane + 64 * k;
+    const int r = idx / UPR, ch = idx % UPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + r * TS + ch * 8);
+    const int row = row0 + wm * 64 + r;
+    if (row < M) *reinterpret_cast<uint4*>(Y + (size_t)row * N + col0 + wn * (BN / 2) + ch * 8) = v;
   }
 }
 
 hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc, const uint8_t* Z,
                          const uint16_t* bias, uint16_t* Y, int M, int N, int K, hipStream_t st,
                          hipEvent_t ev0, hipEvent_t ev1) {
-  const int tiles_m = (M + 127) / 128;
-  dim3 grid((N / 128) * tiles_m);
-  hipExtLaunchKernelGGL(k4_gemm_awq, grid, dim3(256), 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M,
-                        N, K);
+  if (M <= 0 || N % 128 != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  const int tiles_m = (M + 255) / 256;
+  const bool w8 = (K / 64) % 8 == 0;  // scale and zero-point loads of 8 groups
+  const dim3 blk(512);
+  if (N % 192 == 0) {
+    const dim3 grid((N / 192) * tiles_m);
+    if (w8) hipExtLaunchKernelGGL(k4_gemm_awq<3, 8>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
+    else hipExtLaunchKernelGGL(k4_gemm_awq<3, 2>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
+  } else {
+    const dim3 grid((N / 128) * tiles_m);
+    if (w8) hipExtLaunchKernelGGL(k4_gemm_awq<2, 8>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
+    else hipExtLaunchKernelGGL(k4_gemm_awq<2, 2>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
+  }
   return hipGetLastError();
 }
 
