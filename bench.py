@@ -56,14 +56,28 @@ WORKLOADS = {
 }
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
-GEMM_SOURCES = ["w4a4_rank_corrected_linear_amd/csrc/k2_gemm_int4.hip",
-                "w4a4_rank_corrected_linear_amd/csrc/common.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k2_gemm_int4_attn_proj_traffic.txt")
+# Workloads with committed counter summaries: (K1 kernel, GEMM kernel, GEMM sources whose
+# hash stamps the summary, the summaries' base names)
+PROFILED = {
+    "attn_proj": ("k1_int4_fused", "k2_gemm_int4",
+                  ["w4a4_rank_corrected_linear_amd/csrc/k2_gemm_int4.hip",
+                   "w4a4_rank_corrected_linear_amd/csrc/common.h"],
+                  "svdq_w4a4_int4_attn_proj", "k2_gemm_int4_attn_proj"),
+    "nvfp4_sq": ("k1_nvfp4_fused", "k2_gemm_fp4",
+                 ["w4a4_rank_corrected_linear_amd/csrc/k2_gemm_fp4.hip",
+                  "w4a4_rank_corrected_linear_amd/csrc/k2_common.h",
+                  "w4a4_rank_corrected_linear_amd/csrc/common.h"],
+                 "svdq_w4a4_nvfp4_sq", "k2_gemm_fp4_nvfp4_sq"),
+}
 
 
-def gemm_source_hash() -> str:
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{PROFILED[workload][4]}_traffic.txt")
+
+
+def gemm_source_hash(workload: str = "attn_proj") -> str:
     h = hashlib.sha256()
-    for p in GEMM_SOURCES:
+    for p in PROFILED[workload][2]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -71,15 +85,15 @@ def gemm_source_hash() -> str:
 
 def recorded_traffic(workload: str):
     """HBM bytes per GEMM launch from the committed counter summary, or None."""
-    if workload != "attn_proj" or not os.path.exists(TRAFFIC_FILE):
+    if workload not in PROFILED or not os.path.exists(traffic_file(workload)):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(traffic_file(workload)) as f:
         for line in f:
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash(workload):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -392,13 +406,14 @@ def run_prep(args) -> int:
 
 PROFILE_CMDS = {
     "stats": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_stats "
-             "-o run --output-format csv -- python3 <repo>/bench.py --no-cpu-baseline",
+             "-o run --output-format csv -- python3 <repo>/bench.py --workload {w} --no-cpu-baseline "
+             "--no-cold",
     "fetch": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_fetch -o run "
-             "--output-format csv -- python3 <repo>/bench.py --no-cpu-baseline --steps 20 "
-             "--warmup 5 --copy-probe",
+             "--output-format csv -- python3 <repo>/bench.py --workload {w} --no-cpu-baseline "
+             "--no-cold --steps 20 --warmup 5 --copy-probe",
     "write": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_write -o run "
-             "--output-format csv -- python3 <repo>/bench.py --no-cpu-baseline --steps 20 "
-             "--warmup 5 --copy-probe",
+             "--output-format csv -- python3 <repo>/bench.py --workload {w} --no-cpu-baseline "
+             "--no-cold --steps 20 --warmup 5 --copy-probe",
 }
 
 
@@ -432,6 +447,8 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     import csv
     import glob
 
+    k1_name, k2_name, _, stats_base, _ = PROFILED[workload]
+
     def one(pattern):
         files = glob.glob(os.path.join(out_dir, pattern), recursive=True)
         if not files:
@@ -439,23 +456,25 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
         return files[0]
 
     def short(name):
-        for key in ("k1_int4_fused", "k2_gemm_int4", "MulFunctor", "FillFunctor", "k_pack_int4",
+        for key in (k1_name, k2_name, "MulFunctor", "FillFunctor", "k_pack_int4", "k_pack_nvfp4",
                     "k_pack_lora_down", "k_pair_scales", "k_zero_flag", "copyBuffer"):
             if key in name:
                 return key
         return name[:40]
 
-    _, cid, M, K, N, rank = WORKLOADS[workload]
+    method, cid, M, K, N, rank = WORKLOADS[workload]
+    desc = {"int4": "int4 g64", "nvfp4": "nvfp4 g16"}[method]
+    cmds = {k: v.format(w=workload) for k, v in PROFILE_CMDS.items()}
     lines = [f"# rocprofv3 kernel statistics: bench.py, workload {workload} "
-             f"(M={M} K={K} N={N} rank {rank}, int4 g64), 50 warmup + 500 timed + 500 event-timed calls",
-             f"# command: {PROFILE_CMDS['stats']}",
+             f"(M={M} K={K} N={N} rank {rank}, {desc}), 50 warmup + 500 timed + 500 event-timed calls",
+             f"# command: {cmds['stats']}",
              "# kernel                      calls     avg_us     min_us     max_us   share_%"]
     for r in csv.DictReader(open(one("prof_stats/**/*kernel_stats.csv"))):
         lines.append(f"{short(r['Name']):28s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} "
                      f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
                      f"{float(r['Percentage']):8.2f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"svdq_w4a4_int4_{workload}_kernel_stats.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{stats_base}_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     per = {}
@@ -470,12 +489,12 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     copy_bytes = 256.0 * 1024 * 1024
     f_fetch = per["fetch"]["MulFunctor"] * 1024 / copy_bytes
     f_write = per["write"]["MulFunctor"] * 1024 / copy_bytes
-    k2_traffic = per["fetch"]["k2_gemm_int4"] * 1024 / f_fetch + per["write"]["k2_gemm_int4"] * 1024 / f_write
-    k1_traffic = per["fetch"]["k1_int4_fused"] * 1024 / f_fetch + per["write"]["k1_int4_fused"] * 1024 / f_write
+    k2_traffic = per["fetch"][k2_name] * 1024 / f_fetch + per["write"][k2_name] * 1024 / f_write
+    k1_traffic = per["fetch"][k1_name] * 1024 / f_fetch + per["write"][k1_name] * 1024 / f_write
     t = [f"# HBM traffic per dispatch from rocprofv3 counters, workload {workload} "
-         f"(M={M} K={K} N={N} rank {rank}, int4 g64)",
-         f"# fetch command: {PROFILE_CMDS['fetch']}",
-         f"# write command: {PROFILE_CMDS['write']}",
+         f"(M={M} K={K} N={N} rank {rank}, {desc})",
+         f"# fetch command: {cmds['fetch']}",
+         f"# write command: {cmds['write']}",
          "# scale: the copy probe (elementwise multiply, float32, 256 MiB read + 256 MiB write)",
          "# reads FETCH_SIZE = copy_fetch_KiB and WRITE_SIZE = copy_write_KiB; bytes = counter KiB",
          "# * 1024 / factor, factor = counter bytes of the probe / 256 MiB",
@@ -483,13 +502,13 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
          f"copy_write_KiB = {per['write']['MulFunctor']:.1f}",
          f"fetch_factor = {f_fetch:.4f}",
          f"write_factor = {f_write:.4f}"]
-    for k in ("k1_int4_fused", "k2_gemm_int4"):
+    for k in (k1_name, k2_name):
         t.append(f"{k}_fetch_KiB = {per['fetch'][k]:.1f}")
         t.append(f"{k}_write_KiB = {per['write'][k]:.1f}")
     t += [f"k1_traffic_bytes_per_launch = {k1_traffic:.0f}",
           f"traffic_bytes_per_launch = {k2_traffic:.0f}",
-          f"gemm_source_sha256_16 = {gemm_source_hash()}"]
-    with open(TRAFFIC_FILE, "w") as f:
+          f"gemm_source_sha256_16 = {gemm_source_hash(workload)}"]
+    with open(traffic_file(workload), "w") as f:
         f.write("\n".join(t) + "\n")
     print("\n".join(lines + t))
 
@@ -527,7 +546,8 @@ def summarize_counters(name: str, what: str, *runs: str) -> None:
     lines = [f"# rocprofv3 hardware counters: {what}"]
     lines += [f"# command: {c}" for c in cmds]
     lines.append(f"# summary: python bench.py --summarize-counters {name} <what> <csv_dir>=<command> ...")
-    lines.append(f"# gemm_source_sha256_16 = {gemm_source_hash()}")
+    wl = next((w for w, v in PROFILED.items() if v[4] == name), "attn_proj")
+    lines.append(f"# gemm_source_sha256_16 = {gemm_source_hash(wl)}")
     for nm in sorted(per, key=lambda k: -max(len(v) for v in per[k].values())):
         cs = per[nm]
         n = max(len(v) for v in cs.values())
@@ -598,8 +618,8 @@ def cold_cache_pass(args, inp, layer_args, M: int, N: int, K: int, dev) -> dict:
 
 
 def main() -> int:
-    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
-        summarize_profiles(sys.argv[2])
+    if len(sys.argv) in (3, 4) and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(*sys.argv[2:4])
         return 0
     if len(sys.argv) == 6 and sys.argv[1] == "--summarize-stats":
         summarize_stats(*sys.argv[2:6])
