@@ -138,8 +138,18 @@ svdq_status svdq_pack_lora_down(const svdq_config* cfg, int64_t K, const uint16_
  * tile count leaves the CUs' last round part empty, those tiles are split along K,
  * their fp32 partial tiles stored here and added up (in a fixed order) by a second,
  * small kernel.  A workspace that stops short of that area (at least the size without
- * it) is accepted; the GEMM then runs every tile whole. */
+ * it) is accepted; the GEMM then splits only as far as the room it is given allows (no
+ * split without room).  svdq_workspace_bytes_n sizes the area for one layer. */
 size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K);
+
+/* Workspace bytes for M tokens of a layer with K inputs and N outputs: the same areas
+ * as svdq_workspace_bytes, with the int4 K-split area sized for the split the GEMM
+ * takes at this (M, N, K) on the current device (the larger of the plain and the fused
+ * QKV plans; none when neither splits), instead of the 48 MiB maximum.  A call given a
+ * workspace of this size runs the same kernels as with the full one.  Host-only query
+ * (it reads the current device's CU count, 256 when no device is visible); 0 for an
+ * invalid config or shape. */
+size_t svdq_workspace_bytes_n(const svdq_config* cfg, int64_t M, int64_t K, int64_t N);
 
 /* Activation side of the layer (smoothing, low-rank down projection, quantization)
  * in the interchange layout.  Defined by the Diffusers docs "Nunchaku Lite",

@@ -105,6 +105,26 @@ def test_workspace_size_and_check():
     assert nv == 256 * 512 // 2 + 256 * 512 // 8 + 256 * 32 * 4
 
 
+def test_workspace_sized_for_a_layer():
+    """svdq_workspace_bytes_n: the K-split area sized for the layer's GEMM plan (on a
+    host without a GPU the plan assumes 256 CUs)."""
+    lib = L.lib()
+    full = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 4096, 3072)
+    split = 256 * 256 * 192 * 4
+    # 4096 x 3072 -> 3072: 256 tiles of 256 x 192, one round, no split
+    assert lib.svdq_workspace_bytes_n(ctypes.byref(cfg()), 4096, 3072, 3072) == full - split
+    # 4608 x 3072 -> 9216: 864 tiles leave a last round of 96, split into pieces
+    qkv = lib.svdq_workspace_bytes_n(ctypes.byref(cfg()), 4608, 3072, 9216)
+    full_qkv = lib.svdq_workspace_bytes(ctypes.byref(cfg()), 4608, 3072)
+    assert full_qkv - split < qkv < full_qkv
+    assert (qkv - (full_qkv - split)) % (256 * 192 * 4) == 0
+    nv = cfg(precision=L.NVFP4, group=16)
+    assert lib.svdq_workspace_bytes_n(ctypes.byref(nv), 100, 512, 384) == \
+        lib.svdq_workspace_bytes(ctypes.byref(nv), 100, 512)
+    assert lib.svdq_workspace_bytes_n(ctypes.byref(cfg()), 100, 512, 100) == 0     # N % 128
+    assert lib.svdq_workspace_bytes_n(None, 100, 512, 384) == 0
+
+
 def test_packed_weight_bytes():
     lib = L.lib()
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)

@@ -385,18 +385,22 @@ def test_linear_with_tail_split(split_layer, mode):
             return dev.qkv_norm_rope(x, dev_bf16(nq), dev_bf16(nk), I.QK_NORM_EPS, rope, workspace=ws)
         return dev(x, workspace=ws, gelu=(mode == "gelu"))
 
-    # each workspace is followed by a guard region that the calls must leave alone
+    # the full workspace (the 48 MiB K-split area), the one sized for this layer
+    # (svdq_workspace_bytes_n) and one without the split area; each is followed by a
+    # guard region that the calls must leave alone
+    full = svdq.workspace_bytes("int4", 32, M, li.x.shape[1])
     need, guard, split_area = dev.workspace_bytes(M), 1 << 20, 256 * 256 * 192 * 4
-    full_buf = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device="cuda")
-    small_buf = torch.full((need - split_area + guard,), 0xA5, dtype=torch.uint8, device="cuda")
-    full_ws, small_ws = full_buf[:need], small_buf[:need - split_area]
-    svdq.timing_start(1)
-    y_split = host_bits(run(full_ws))
-    assert len(svdq.timing_stop()[1]) == 3      # quantizer, GEMM, tail kernel
-    svdq.timing_start(1)
-    y_whole = host_bits(run(small_ws))
-    assert len(svdq.timing_stop()[1]) == 2      # quantizer, GEMM
-    assert bool((full_buf[need:] == 0xA5).all()) and bool((small_buf[need - split_area:] == 0xA5).all())
+    base = full - split_area
+    assert base < need < full
+    bufs = {n: torch.full((n + guard,), 0xA5, dtype=torch.uint8, device="cuda") for n in (full, need, base)}
+    ys = {}
+    for n, kernels in ((full, 3), (need, 3), (base, 2)):   # quantizer, GEMM (, tail kernel)
+        svdq.timing_start(1)
+        ys[n] = host_bits(run(bufs[n][:n]))
+        assert len(svdq.timing_stop()[1]) == kernels
+        assert bool((bufs[n][n:] == 0xA5).all())
+    y_split, y_whole = ys[full], ys[base]
+    assert np.array_equal(ys[need], y_split)   # the sized workspace takes the same split
     r = OL.w4a4_linear("int4", li.x, layer)["r"]
     ref = {"plain": r, "gelu": A.gelu_f64(r),
            "qkv": AT.qkv_norm_rope_f64(r, nq, nk, I.QK_NORM_EPS, rope_np)}[mode]

@@ -53,8 +53,9 @@ def test_noalloc_dit_shape_sampled_rows():
                         wscales=pb.wscales, w_global=1.0, act_global=1.0, smooth=pb.smooth,
                         lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
     dl = _dev(layer)
-    base = dl.workspace_bytes(4608) - 256 * 256 * 192 * 4     # without the split area
-    assert base <= 64 << 20 < dl.workspace_bytes(4608)
+    full = svdq.workspace_bytes("int4", 32, 4608, 12288)
+    base = full - 256 * 256 * 192 * 4     # without the split area
+    assert base <= 64 << 20 < full
     xd = dev_bf16(x)
     y = host_bits(dl.forward_noalloc(xd))
     rows = np.unique(np.concatenate([np.arange(11, 4608, 397), [4607]]))

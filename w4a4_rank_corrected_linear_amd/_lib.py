@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.svdq_pack_weight.restype = st
     L.svdq_pack_lora_down.argtypes = [cfgp, i64, vp, vp, vp]
     L.svdq_pack_lora_down.restype = st
+    L.svdq_workspace_bytes_n.argtypes = [cfgp, i64, i64, i64]
+    L.svdq_workspace_bytes_n.restype = ctypes.c_size_t
     L.svdq_workspace_bytes.argtypes = [cfgp, i64, i64]
     L.svdq_workspace_bytes.restype = ctypes.c_size_t
     L.svdq_quantize_act.argtypes = [cfgp, vp, i64, i64, vp, vp, f32, vp, vp, vp, vp]

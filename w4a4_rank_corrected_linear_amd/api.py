@@ -42,6 +42,23 @@ def workspace_bytes(precision: str, rank: int, M: int, K: int) -> int:
     return int(L.lib().svdq_workspace_bytes(ctypes.byref(cfg), M, K))
 
 
+_SHARED_WS: dict = {}
+
+
+def shared_workspace(need: int, device) -> torch.Tensor:
+    """A uint8 workspace of at least `need` bytes for calls on `device`'s current stream,
+    kept per (device, stream) and reused by every layer (reallocated larger when a call
+    needs more).  Layers run on different streams get different buffers."""
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
+    ws = _SHARED_WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", idx))
+        _SHARED_WS[key] = ws
+    return ws
+
+
 def _scale_dtype(precision: str):
     return torch.bfloat16 if precision == "int4" else torch.uint8
 
@@ -120,7 +137,6 @@ class SvdqLinear:
                                    None if lora_down is None else lora_down.data_ptr(),
                                    None if lora_up is None else lora_up.data_ptr(),
                                    None if bias is None else bias.data_ptr())
-        self._ws = None
 
     @classmethod
     def from_interchange(cls, codes, scales, smooth, lora_down, lora_up, bias,
@@ -131,14 +147,14 @@ class SvdqLinear:
         return cls(2 * K2, N, pc, ps, smooth, ld, lora_up, bias, precision, w_global, act_global)
 
     def workspace_bytes(self, M: int) -> int:
-        """svdq_workspace_bytes for M tokens of this layer (at least 256)."""
-        return max(int(L.lib().svdq_workspace_bytes(ctypes.byref(self.cfg), M, self.K)), 256)
+        """svdq_workspace_bytes_n for M tokens of this layer (at least 256): the int4
+        K-split area is sized for this layer's own GEMM plan."""
+        return max(int(L.lib().svdq_workspace_bytes_n(ctypes.byref(self.cfg), M, self.K, self.N)), 256)
 
     def workspace(self, M: int, device) -> torch.Tensor:
-        need = self.workspace_bytes(M)
-        if self._ws is None or self._ws.numel() < need or self._ws.device != device:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
-        return self._ws
+        """The default workspace: one buffer per (device, current stream), shared by every
+        layer and grown on demand, since calls ordered on one stream never overlap."""
+        return shared_workspace(self.workspace_bytes(M), device)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, act_global: float | None = None,

@@ -324,6 +324,30 @@ size_t svdq_workspace_bytes(const svdq_config* cfg, int64_t M, int64_t K) {
   return ws_layout(cfg, M, K).total;
 }
 
+// Bytes of the int4 GEMM's K-split area for an N-column layer: the pieces of the plan
+// taken with the full room, the larger of the plain (and GELU) plan and the fused-QKV
+// one; 0 when neither splits.  The plan uses the current device's CU count (256 when no
+// device is visible).
+static size_t split_area_bytes(int64_t M_pad, int64_t N, int64_t K) {
+  size_t best = 0;
+  for (int epi : {svdq::kEpiPlain, svdq::kEpiQkNormRope}) {
+    if (epi == svdq::kEpiQkNormRope && N % 384 != 0) continue;
+    const svdq::K2Plan p =
+        svdq::plan_k2_int4((int)M_pad, (int)N, (int)K, epi, svdq::kSplitMaxPieces);
+    if (p.ks > 1) best = std::max(best, (size_t)(p.tiles - p.full) * p.ks * svdq::kSplitTileBytes);
+  }
+  return best;
+}
+
+size_t svdq_workspace_bytes_n(const svdq_config* cfg, int64_t M, int64_t K, int64_t N) {
+  if (!cfg || check_svdq_config(cfg) != SVDQ_OK || check_k(K) != SVDQ_OK ||
+      check_n(N) != SVDQ_OK || check_m(M, K) != SVDQ_OK)
+    return 0;
+  const WsLayout L = ws_layout(cfg, M, K);
+  if (!L.split) return L.total;
+  return L.split + split_area_bytes(L.M_pad, N, K);
+}
+
 svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t M, int64_t K,
                               const uint16_t* smooth, const uint16_t* lora_down, float act_global,
                               uint8_t* codes, void* scales, float* lora_act, hipStream_t stream) {
@@ -412,7 +436,10 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
     return fail(SVDQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 workspace_bytes, need);
   }
-  const bool split_room = L.split && workspace_bytes >= L.total;
+  // K-split pieces the workspace has room for (the GEMM's plan splits only within them)
+  const int split_pieces =
+      L.split ? (int)std::min<size_t>(svdq::kSplitMaxPieces, (workspace_bytes - L.split) / svdq::kSplitTileBytes)
+              : 0;
   if (M == 0) return ok();
   SVDQ_TRY(check_current_device());
   if (wsa.scratch) SVDQ_TRY(scratch_address(&workspace));
@@ -446,7 +473,7 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                                            stream, e1.start, e1.end),
                      "quantize kernel launch"));
   const svdq::K2Plan plan = svdq::plan_k2_int4((int)L.M_pad, (int)w->N, (int)w->K, epi,
-                                               split_room ? svdq::kSplitMaxPieces : 0);
+                                               split_pieces);
   const EvPair e2 = timer_kernel();
   const EvPair e3 = plan.kernels() > 1 ? timer_kernel() : EvPair{};
   SVDQ_TRY(hip_check(svdq::launch_k2_int4(plan, a_codes, a_scales, a_lora,
@@ -454,7 +481,7 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                                            static_cast<const uint2*>(w->wscales), w->lora_up,
                                            w->bias, y, (int)M, (int)w->N, (int)w->K, (int)L.M_pad,
                                            cfg->rank, epi, qk,
-                                           split_room ? reinterpret_cast<float*>(ws + L.split)
+                                           split_pieces ? reinterpret_cast<float*>(ws + L.split)
                                                       : nullptr,
                                            stream, e2.start, e2.end, e3.start, e3.end),
                      "gemm kernel launch"));
