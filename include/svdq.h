@@ -105,7 +105,8 @@ svdq_status svdq_check_device(int hip_device);
  *          operand as stored, one record per pair of groups; a 256-byte trailer the
  *          pack clears)
  *   nvfp4: codes N*K/2 (E2M1 codes in the GEMM's FP4 lane slots: chunks of 1024 bytes
- *          per 32 output columns and 64-group, 4 bits per weight), scales
+ *          per 32 output columns and 64-group, dword j of lane slot l at byte
+ *          256 j + 4 l, 4 bits per weight), scales
  *          round_up(N*K/8, 256) + 256 (each E4M3 block scale as its exact fp16 value,
  *          [K/64][N][4]; range flag) -- 4.5 bits per weight in all */
 size_t svdq_packed_weight_bytes(const svdq_config* cfg, int64_t K, int64_t N,

@@ -152,16 +152,22 @@ def int4_workspace(buf: np.ndarray, rows_pad: int, K: int, rank: int):
     return q, s, u
 
 
-def decode_fp4_operand(buf: np.ndarray, rows_pad: int, K: int):
+def decode_fp4_operand(buf: np.ndarray, rows_pad: int, K: int, dword_major: bool = False):
     """NVFP4 GEMM operand (FP4 lane slots, then fp16 block scales) -> (E2M1 codes
     [rows_pad, K], block scales as float64 [rows_pad, K/16]).
 
     Chunk (row // 32, q) of 1 KiB: lane slot 32 h + row % 32 holds in dword j the codes
-    of k = 64 q + 16 j + 8 h + [0, 8), element e in bits 4e..4e+3.  The scales follow at
-    the next 256-byte boundary as fp16 [K/64][rows_pad][4] (block 4 q + j of a row)."""
+    of k = 64 q + 16 j + 8 h + [0, 8), element e in bits 4e..4e+3; slot-major (slot l's
+    dwords at 16 l, the quantizer's activations) or dword-major (dword j of slot l at
+    256 j + 4 l, the packed weights).  The scales follow at the next 256-byte boundary
+    as fp16 [K/64][rows_pad][4] (block 4 q + j of a row)."""
     Q = K // 64
     w = np.asarray(buf, dtype=np.uint8)
-    d = w[: rows_pad * K // 2].view(np.uint32).reshape(rows_pad // 32, Q, 2, 32, 4)  # rb,q,h,r,j
+    if dword_major:
+        d = w[: rows_pad * K // 2].view(np.uint32).reshape(rows_pad // 32, Q, 4, 2, 32)  # rb,q,j,h,r
+        d = d.transpose(0, 1, 3, 4, 2)                                                 # rb,q,h,r,j
+    else:
+        d = w[: rows_pad * K // 2].view(np.uint32).reshape(rows_pad // 32, Q, 2, 32, 4)  # rb,q,h,r,j
     nib = np.stack([(d >> np.uint32(4 * e)) & np.uint32(15) for e in range(8)], axis=-1)
     codes = nib.transpose(0, 3, 1, 4, 2, 5).reshape(rows_pad, K).astype(np.uint8)   # rb,r,q,j,h,e
     off = _round256(rows_pad * K // 2)

@@ -105,7 +105,7 @@ def test_pack_weight_nvfp4_layout(tiny):
     pc, ps = svdq.pack_weight(dev_u8(layer.qweight), dev_u8(layer.wscales), precision="nvfp4")
     assert pc.numel() == layer.N * layer.K // 2
     buf = np.concatenate([host_bits(pc), host_bits(ps)])
-    codes, scales = decode_fp4_operand(buf, layer.N, layer.K)
+    codes, scales = decode_fp4_operand(buf, layer.N, layer.K, dword_major=True)
     assert np.array_equal(codes, F.unpack_nibbles(layer.qweight))
     assert np.array_equal(scales, F.e4m3_decode(layer.wscales))
 

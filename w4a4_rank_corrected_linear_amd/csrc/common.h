@@ -25,8 +25,13 @@
 // their E2M1 codes in that order: chunk (row / 32, q) of 1 KiB holds the 64-group
 // k = 64 q .. 64 q + 63 of a 32-row block, lane slot l = 32 h + row % 32 (16 bytes) holds
 // in dword j the eight codes of block 4 q + j, k = 64 q + 16 j + 8 h + [0, 8) (element 2i
-// in the low nibble of byte i).  Block scales are the exact fp16 values of the E4M3
-// scales, [K/64][rows][4]: the four blocks of a row's 64-group are 8 adjacent bytes.
+// in the low nibble of byte i).  The quantizer writes the activation chunks slot-major
+// (lane slot l's four dwords at bytes 16 l .. 16 l + 15, one 16-byte read per lane);
+// the pack writes the weight chunks dword-major (dword j of lane slot l at byte
+// 256 j + 4 l), so that the 64 dwords of one block, which the GEMM's weight expansion
+// reads together, are one run of 256 bytes with no LDS bank conflicts.  Block scales
+// are the exact fp16 values of the E4M3 scales, [K/64][rows][4]: the four blocks of a
+// row's 64-group are 8 adjacent bytes.
 //
 // Scale records (operands of the rescale MFMA, one 64-bit load each)
 // -------------------------------------------------------------------

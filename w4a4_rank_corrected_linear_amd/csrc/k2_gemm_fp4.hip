@@ -153,8 +153,9 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
   // buffer wb.  A column half (wn) has 4 WN fragments (column block, NVFP4 block) per
   // stage, used by its four waves (wm = 0..3); each of those waves expands WN of them
   // (fragment q = WN wm + n: column block wn WN + q / 4, block q % 4): lane l reads
-  // dword j of lane slot l of the code chunk and the column's scale of block j, and
-  // writes the fp16 fragment.  Expanding each fragment once instead of in all four
+  // dword j of lane slot l of the code chunk (the weight chunks are dword-major, so a
+  // wave's 64 reads are one 256-byte run) and the column's scale of block j, and writes
+  // the fp16 fragment.  Expanding each fragment once instead of in all four
   // waves cuts the VALU work that would otherwise bound this kernel, and the even
   // split keeps the two waves of every SIMD equally loaded.
   auto expandB = [&](int sl, int wb) {
@@ -162,7 +163,7 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
       const int q = WN * wm + n, cb = wn * WN + (q >> 2), j = q & 3;
-      const uint32_t c = *(lds_u1*)(uintptr_t)(base + AC + cb * 1024 + lane * 16 + j * 4);
+      const uint32_t c = *(lds_u1*)(uintptr_t)(base + AC + cb * 1024 + j * 256 + lane * 4);
       const uint32_t sc = *(lds_h1*)(uintptr_t)(base + AC + BC + AS + (cb * 32 + lr) * 8 + j * 2);
       *(lds_h8w*)(uintptr_t)(w160 + wb * W16 + (cb * 4 + j) * 1024 + lane * 16) = fp4_expand(c, sc);
     }

@@ -63,7 +63,7 @@ k_pair_scales(const uint16_t* __restrict__ in, uint2* __restrict__ out, int N, i
 // four dwords of blocks 4 q + j, each the eight codes k = 64 q + 16 j + 8 h + [0, 8) of
 // column n, are 4 interchange bytes apiece (element 2i in the low nibble of byte i).
 __global__ void __launch_bounds__(256)
-k_pack_nvfp4_codes(const uint8_t* __restrict__ codes, uint4* __restrict__ out, int N, int K) {
+k_pack_nvfp4_codes(const uint8_t* __restrict__ codes, uint32_t* __restrict__ out, int N, int K) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int Q = K >> 6;
   if (t >= (int64_t)N * Q * 2) return;
@@ -75,7 +75,9 @@ k_pack_nvfp4_codes(const uint8_t* __restrict__ codes, uint4* __restrict__ out, i
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint32_t*>(src + 8 * j);
-  out[t] = make_uint4(w[0], w[1], w[2], w[3]);
+  // dword-major chunk (weights): dword j of lane slot s at dword 64 j + s of the chunk
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[(rest * 4 + j) * 64 + slot] = w[j];
 }
 
 // NVFP4 scales: one thread per (64-group q, column n): the four E4M3 scales of the
@@ -147,7 +149,7 @@ hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, uint8_
   hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, st, flag);
   const int64_t tc = (int64_t)N * (K / 64) * 2;
   hipLaunchKernelGGL(k_pack_nvfp4_codes, dim3((unsigned)((tc + 255) / 256)), dim3(256), 0, st, codes,
-                     reinterpret_cast<uint4*>(out_codes), N, K);
+                     reinterpret_cast<uint32_t*>(out_codes), N, K);
   const int64_t ts = (int64_t)N * (K / 64);
   hipLaunchKernelGGL(k_pack_nvfp4_scales, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, st,
                      scales, reinterpret_cast<uint2*>(out_scales), N, K, flag);
