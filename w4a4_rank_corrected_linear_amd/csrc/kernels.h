@@ -42,7 +42,7 @@ int device_cu_count();
 // whose fp32 partial tiles a second, small kernel adds up and finishes).  max_pieces
 // is the number of 256 x 192 fp32 partial tiles the caller has room for (0: no split).
 struct K2Plan {
-  int bn = 192;
+  int bm = 256, bn = 192;  // tile
   int tiles = 0, full = 0, ks = 1;
   int kernels() const { return ks > 1 ? 2 : 1; }
 };
