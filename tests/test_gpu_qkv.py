@@ -29,7 +29,8 @@ def dev_f32(a):
 def _layer_dev(layer, bias=True):
     return svdq.SvdqLinear.from_interchange(
         dev_u8(layer.qweight), dev_bf16(layer.wscales), dev_bf16(layer.smooth),
-        dev_bf16(layer.lora_down), dev_bf16(layer.lora_up),
+        dev_bf16(layer.lora_down) if layer.rank else None,
+        dev_bf16(layer.lora_up) if layer.rank else None,
         dev_bf16(layer.bias) if bias else None)
 
 
@@ -82,6 +83,24 @@ def test_qkv_norm_rope_zero_rows_and_m0(tiny_qkv):
     out = dev.qkv_norm_rope(e, dev_bf16(nq), dev_bf16(nk), EPS,
                             torch.empty((0, 64, 2), dtype=torch.float32, device="cuda"))
     assert out.shape == (0, 768)
+
+
+@pytest.mark.parametrize("K,N,rank", [(4608, 1152, 32), (640, 1152, 16), (1024, 768, 0)])
+def test_qkv_norm_rope_shapes(K, N, rank):
+    """Tiles of three heads that are all Q, all K or all V (N = 1152), or mixed
+    (N = 768); the low-rank term before the main loop (three k-splits at K = 4608, where
+    the few tiles are also split along K and finished per head by the tail kernel) or
+    after it, and ranks 32, 16 and 0."""
+    li = I.layer_inputs(config_id=1, M=77, K=K, N=N, outlier_count=4, factor=20.0)
+    layer = P.prepare_svdq(li.w, li.x_cal, li.bias, rank=rank)
+    rng = np.random.default_rng(K + N + rank)
+    ang = rng.uniform(-np.pi, np.pi, (77, 64))
+    rope = np.stack([np.cos(ang), np.sin(ang)], axis=2).astype(np.float32)
+    nq, nk = I.qk_norm_weights()
+    dev = _layer_dev(layer)
+    y = dev.qkv_norm_rope(dev_bf16(li.x), dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope))
+    r = OL.w4a4_linear("int4", li.x, layer)["r"]
+    check_y(host_bits(y), AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope))
 
 
 def test_qkv_norm_rope_dit_block_full_size():
