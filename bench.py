@@ -417,6 +417,37 @@ PROFILE_CMDS = {
 }
 
 
+# published dense peaks (TFLOP/s or TOP/s) of the probe's instruction types
+MFMA_PUBLISHED = {"fp6": 10100.0, "fp4": 10100.0, "fp8": 5000.0, "int8": 5000.0, "fp16": 2500.0,
+                  "bf16": 2500.0, "bf16_k8": 2500.0}
+
+
+def mfma_achievable(iters: int = 2048, reps: int = 3) -> dict:
+    """The dense rate the matrix cores sustain per instruction type (svdq_mfma_probe:
+    every CU, two waves per SIMD, four independent MFMAs per round), timed with HIP
+    events on the launching stream: the median of `reps` launches after one warm-up."""
+    import torch
+
+    import w4a4_rank_corrected_linear_amd as svdq
+    out = {}
+    sink = None
+    for op in svdq.MFMA_OPS:
+        sink, ops = svdq.mfma_probe(op, iters, sink)
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            svdq.mfma_probe(op, iters, sink)
+            e1.record()
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = sorted(ms)[len(ms) // 2]
+        rate = ops / (t * 1e-3) / 1e12
+        out[op] = {"tflops": round(rate, 1), "published": MFMA_PUBLISHED[op],
+                   "frac_of_published": round(rate / MFMA_PUBLISHED[op], 4)}
+    return out
+
+
 def summarize_stats(csv_dir: str, name: str, command: str, what: str) -> None:
     """One rocprofv3 --kernel-trace --stats run (CSV under csv_dir) as a text summary
     profiles/<name>_kernel_stats.txt: the kernel table with the command that made it
@@ -819,6 +850,11 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    # the achievable dense rate of the matrix instructions, beside the published peaks
+    out["mfma_achievable"] = mfma_achievable()
+    ach = out["mfma_achievable"][{"int4": "fp6", "nvfp4": "fp16", "awq": "bf16"}[method]]["tflops"]
+    out["roofline"]["achievable_peak"] = ach
+    out["roofline"]["frac_of_achievable"] = round(achieved / ach, 4)
     if method != "awq":
         # device bytes the layer keeps resident: packed codes and scales, smoothing,
         # lora_down, lora_up, bias

@@ -366,6 +366,27 @@ svdq_status svdq_graph_destroy(svdq_graph* graph);
 svdq_status svdq_timing_start(int max_calls);
 svdq_status svdq_timing_stop(int* calls, int* kernels, float* mean_ms, int max_kernels);
 
+/* ---- Measurement aid (not part of the layer): achievable dense MFMA rate ---------
+ * The roofline of a GEMM is read against the chip's published dense matrix peak; these
+ * calls measure what the matrix cores sustain for each instruction type the kernels
+ * issue (FP6 and the 32x32x8 bf16 outer product in the int4 GEMM, fp16 in the NVFP4
+ * GEMM, bf16 in the low-rank terms and the AWQ GEMM) and for the FP4, FP8 and int8
+ * forms the published peaks are quoted for.
+ *   op: 0 FP6 E2M3 32x32x64 (scaled, unit scales), 1 FP4 E2M1 32x32x64, 2 FP8 E4M3
+ *       32x32x64, 3 int8 32x32x32, 4 fp16 32x32x16, 5 bf16 32x32x16, 6 bf16 32x32x8.
+ * svdq_mfma_probe launches one 512-thread workgroup per CU of the current device;
+ * every wave runs `iters` (1 .. 2^20) rounds of four independent MFMAs of type op on
+ * register operands and writes one float per thread to `sink` (device,
+ * svdq_mfma_probe_sink_floats() floats, 16-byte aligned; its values carry no meaning).
+ * The caller times the launch (HIP events on `stream`); svdq_mfma_probe_ops(op, iters)
+ * gives the operations (multiply and add counted separately) of one launch on the
+ * current device, 0 for an invalid op or iters.  Errors: NULL sink -> SVDQ_ERR_NULL,
+ * unknown op -> SVDQ_ERR_CONFIG, iters out of range -> SVDQ_ERR_RANGE, misaligned sink
+ * -> SVDQ_ERR_ALIGN, no gfx950 device current -> SVDQ_ERR_DEVICE. */
+int64_t svdq_mfma_probe_sink_floats(void);
+double svdq_mfma_probe_ops(int op, int iters);
+svdq_status svdq_mfma_probe(int op, int iters, float* sink, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* svdq_status_str(svdq_status s);
 

@@ -255,6 +255,19 @@ def test_qkv_norm_rope_entry_validation():
     assert call(cfg(), w, rope=FAKE_MISALIGNED) == L.ERR_ALIGN
 
 
+def test_mfma_probe_validation():
+    lib = L.lib()
+    assert lib.svdq_mfma_probe_sink_floats() % 512 == 0
+    assert lib.svdq_mfma_probe_ops(0, 1) == lib.svdq_mfma_probe_sink_floats() / 64 * 4 * 2 * 32 * 32 * 64
+    assert lib.svdq_mfma_probe_ops(7, 1) == 0.0 and lib.svdq_mfma_probe_ops(0, 0) == 0.0
+    assert lib.svdq_mfma_probe(0, 16, None, None) == L.ERR_NULL
+    assert lib.svdq_mfma_probe(7, 16, FAKE, None) == L.ERR_CONFIG
+    assert lib.svdq_mfma_probe(-1, 16, FAKE, None) == L.ERR_CONFIG
+    assert lib.svdq_mfma_probe(0, 0, FAKE, None) == L.ERR_RANGE
+    assert lib.svdq_mfma_probe(0, (1 << 20) + 1, FAKE, None) == L.ERR_RANGE
+    assert lib.svdq_mfma_probe(0, 16, FAKE_MISALIGNED, None) == L.ERR_ALIGN
+
+
 def test_separate_qk_norm_rope_validation():
     lib = L.lib()
 

@@ -18,6 +18,8 @@ from .api import (  # noqa: F401
     capture,
     check_device,
     gelu,
+    MFMA_OPS,
+    mfma_probe,
     pack_lora_down,
     pack_weight,
     prepare_awq_layer,

@@ -114,6 +114,12 @@ def lib() -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     L.svdq_timing_stop.argtypes = [ip, ip, ctypes.POINTER(ctypes.c_float), ctypes.c_int]
     L.svdq_timing_stop.restype = st
+    L.svdq_mfma_probe_sink_floats.argtypes = []
+    L.svdq_mfma_probe_sink_floats.restype = i64
+    L.svdq_mfma_probe_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.svdq_mfma_probe_ops.restype = ctypes.c_double
+    L.svdq_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    L.svdq_mfma_probe.restype = st
     L.svdq_status_str.argtypes = [st]
     L.svdq_status_str.restype = ctypes.c_char_p
     L.svdq_last_error.argtypes = []

@@ -391,3 +391,19 @@ def timing_stop(max_kernels: int = 4):
     L.check(L.lib().svdq_timing_stop(ctypes.byref(calls), ctypes.byref(kernels), buf, max_kernels),
             "svdq_timing_stop")
     return calls.value, [float(buf[i]) for i in range(min(kernels.value, max_kernels))]
+
+
+# Instruction types of the dense MFMA rate probe (svdq_mfma_probe), by name.
+MFMA_OPS = {"fp6": 0, "fp4": 1, "fp8": 2, "int8": 3, "fp16": 4, "bf16": 5, "bf16_k8": 6}
+
+
+def mfma_probe(op: str, iters: int, sink: torch.Tensor | None = None) -> tuple[torch.Tensor, float]:
+    """svdq_mfma_probe: one launch of the dense MFMA rate probe for instruction type
+    `op` (a key of MFMA_OPS) on the current stream; returns (sink, operations of the
+    launch).  The caller times it."""
+    n = int(L.lib().svdq_mfma_probe_sink_floats())
+    if sink is None:
+        sink = torch.empty(n, dtype=torch.float32, device="cuda")
+    _want(sink, torch.float32, "sink", (n,))
+    L.check(L.lib().svdq_mfma_probe(MFMA_OPS[op], int(iters), _p(sink), _stream()), "svdq_mfma_probe")
+    return sink, float(L.lib().svdq_mfma_probe_ops(MFMA_OPS[op], int(iters)))

@@ -37,6 +37,14 @@ struct QkEpi {
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cu_count();
 
+// Dense MFMA rate probe (a measurement aid): instruction types, the operations one
+// instruction performs, and the launch (one 512-thread workgroup per CU, `iters`
+// rounds of four instructions per wave, one float per thread into sink).
+enum MfmaOp { kMfmaFp6 = 0, kMfmaFp4 = 1, kMfmaFp8 = 2, kMfmaI8 = 3, kMfmaF16 = 4, kMfmaBf16 = 5,
+              kMfmaBf16K8 = 6 };
+double mfma_probe_flops_per_instr(int op);
+hipError_t launch_mfma_probe(int op, int iters, float* sink, hipStream_t st);
+
 // Launch plan of the int4 GEMM: tile width, tile count, and the K-split of the tiles
 // of a last, partial round on the CUs (tiles [full, tiles) split into ks pieces each,
 // whose fp32 partial tiles a second, small kernel adds up and finishes).  max_pieces

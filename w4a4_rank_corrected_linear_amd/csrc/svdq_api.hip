@@ -692,6 +692,25 @@ svdq_status svdq_graph_destroy(svdq_graph* graph) {
   return hip_check(e2, "hipGraphDestroy");
 }
 
+int64_t svdq_mfma_probe_sink_floats(void) { return (int64_t)svdq::device_cu_count() * 512; }
+
+double svdq_mfma_probe_ops(int op, int iters) {
+  if (op < svdq::kMfmaFp6 || op > svdq::kMfmaBf16K8 || iters < 1 || iters > (1 << 20)) return 0.0;
+  // waves x rounds x four instructions x operations per instruction
+  return (double)svdq::device_cu_count() * 8.0 * iters * 4.0 * svdq::mfma_probe_flops_per_instr(op);
+}
+
+svdq_status svdq_mfma_probe(int op, int iters, float* sink, hipStream_t stream) {
+  if (!sink) return fail(SVDQ_ERR_NULL, "svdq_mfma_probe: NULL sink");
+  if (op < svdq::kMfmaFp6 || op > svdq::kMfmaBf16K8)
+    return fail(SVDQ_ERR_CONFIG, "svdq_mfma_probe: unknown instruction type %d", op);
+  if (iters < 1 || iters > (1 << 20))
+    return fail(SVDQ_ERR_RANGE, "svdq_mfma_probe: iters = %d outside [1, 2^20]", iters);
+  if (!aligned16(sink)) return fail(SVDQ_ERR_ALIGN, "svdq_mfma_probe: sink must be 16-byte aligned");
+  SVDQ_TRY(check_current_device());
+  return hip_check(svdq::launch_mfma_probe(op, iters, sink, stream), "mfma probe launch");
+}
+
 svdq_status svdq_qk_norm_rope_bf16(const uint16_t* x, uint16_t* y, int64_t M, int64_t N,
                                    const uint16_t* norm_q, const uint16_t* norm_k, float eps,
                                    const float* rope, hipStream_t stream) {
