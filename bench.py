@@ -472,6 +472,11 @@ def summarize_stats(csv_dir: str, name: str, command: str, what: str) -> None:
     print("\n".join(lines))
 
 
+def svdq_mfma_ops():
+    """Names of the probe's instruction types in op order (host only: no GPU)."""
+    return {"fp6": 0, "fp4": 1, "fp8": 2, "int8": 3, "fp16": 4, "bf16": 5, "bf16_k8": 6}
+
+
 def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     """Turn the CSV output of the three rocprofv3 runs in PROFILE_CMDS (under
     out_dir) into the text summaries kept under profiles/ (host only, no GPU)."""
@@ -491,6 +496,9 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
                     "k_pack_lora_down", "k_pair_scales", "k_zero_flag", "copyBuffer"):
             if key in name:
                 return key
+        if "k_mfma_probe<" in name:   # the achievable-rate probe, by instruction type
+            op = int(name.split("k_mfma_probe<")[1].split(">")[0])
+            return "k_mfma_probe " + list(svdq_mfma_ops())[op]
         return name[:40]
 
     method, cid, M, K, N, rank = WORKLOADS[workload]
