@@ -43,8 +43,10 @@ __device__ __forceinline__ void k1_rows32(const K1Args& a) {
   static_assert(NW * 128 == kK1SplitK, "one k-block per wave");
   __shared__ __attribute__((aligned(16))) uint16_t XS[NW][2][RB];   // 96 KiB
   __shared__ __attribute__((aligned(16))) float MSf[NW][128];       // 6 KiB
-  // partial U tiles, in the X tiles' memory once every wave is done with them
-  float(*ured)[32][33] = reinterpret_cast<float(*)[32][33]>(&XS[0][0][0]);
+  // partial U tiles of the waves (rows padded to 36 floats, so a row's four consecutive
+  // values are one aligned float4), apart from the X tiles so that a wave writes its
+  // partial as soon as it is done
+  __shared__ __attribute__((aligned(16))) float ured[NW][32][36];  // 54 KiB
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -150,7 +152,6 @@ __device__ __forceinline__ void k1_rows32(const K1Args& a) {
     }
   }
   if (rank > 0) {
-    __syncthreads();  // every wave is done with its X tiles
     // C layout of the 16x16 MFMA: lane l holds column l%16, rows 4(l/16) + i
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -160,17 +161,26 @@ __device__ __forceinline__ void k1_rows32(const K1Args& a) {
         ured[wave][16 * h + 4 * q + i][16 + r] = u1[h][i];
       }
     __syncthreads();
-    // the nb partials of an element are read at once, then added in wave order
-    for (int t = threadIdx.x; t < 32 * rank; t += 64 * NW) {
-      const int rr = t / rank, cc = t % rank;
-      float p[NW];
+    // thread t sums four consecutive ranks 4 (t % (rank/4)) .. + 3 of row t / (rank/4):
+    // the nb partials are read at once (float4 each), added in wave order, and stored as
+    // one float4 (four consecutive ranks are contiguous in the fragment layout)
+    const int t = threadIdx.x;
+    if (t < 8 * rank) {
+      const int rr = t / (rank >> 2), cc = 4 * (t % (rank >> 2));
+      float4 p[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) p[w] = w < nb ? ured[w][rr][cc] : 0.f;
-      float v = p[0];
+      for (int w = 0; w < NW; ++w)
+        p[w] = w < nb ? *reinterpret_cast<const float4*>(&ured[w][rr][cc]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 v = p[0];
 #pragma unroll
       for (int w = 1; w < NW; ++w)
-        if (w < nb) v += p[w];
-      a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)] = v;
+        if (w < nb) {
+          v.x += p[w].x;
+          v.y += p[w].y;
+          v.z += p[w].z;
+          v.w += p[w].w;
+        }
+      *reinterpret_cast<float4*>(&a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)]) = v;
     }
   }
 }
