@@ -203,9 +203,10 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
 #pragma unroll
         for (int c = 0; c < WN; ++c)
           acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bw[j][c], a[j & 1][i], acc[i][c], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      // (no scheduling barrier around it: letting the compiler interleave the next
+      // stage's reads and weight expansion with this block's MFMAs saves 1.2 us at
+      // 4096 x 3072 x 3072)
       if (j == 0) next();
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
