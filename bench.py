@@ -68,6 +68,12 @@ PROFILED = {
                   "w4a4_rank_corrected_linear_amd/csrc/k2_common.h",
                   "w4a4_rank_corrected_linear_amd/csrc/common.h"],
                  "svdq_w4a4_nvfp4_sq", "k2_gemm_fp4_nvfp4_sq"),
+    # the AWQ W4A16 layer is one kernel (no quantizer)
+    "awq_sq": (None, "k4_gemm_awq",
+               ["w4a4_rank_corrected_linear_amd/csrc/k4_gemm_awq.hip",
+                "w4a4_rank_corrected_linear_amd/csrc/k2_common.h",
+                "w4a4_rank_corrected_linear_amd/csrc/common.h"],
+               "awq_w4a16_sq", "k4_gemm_awq_awq_sq"),
 }
 
 
@@ -494,7 +500,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     def short(name):
         for key in (k1_name, k2_name, "MulFunctor", "FillFunctor", "k_pack_int4", "k_pack_nvfp4",
                     "k_pack_lora_down", "k_pair_scales", "k_zero_flag", "copyBuffer"):
-            if key in name:
+            if key and key in name:
                 return key
         if "k_mfma_probe<" in name:   # the achievable-rate probe, by instruction type
             op = int(name.split("k_mfma_probe<")[1].split(">")[0])
@@ -502,7 +508,7 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
         return name[:40]
 
     method, cid, M, K, N, rank = WORKLOADS[workload]
-    desc = {"int4": "int4 g64", "nvfp4": "nvfp4 g16"}[method]
+    desc = {"int4": "int4 g64", "nvfp4": "nvfp4 g16", "awq": "awq_w4a16 int4 g64"}[method]
     cmds = {k: v.format(w=workload) for k, v in PROFILE_CMDS.items()}
     lines = [f"# rocprofv3 kernel statistics: bench.py, workload {workload} "
              f"(M={M} K={K} N={N} rank {rank}, {desc}), 50 warmup + 500 timed + 500 event-timed calls",
@@ -529,7 +535,8 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     f_fetch = per["fetch"]["MulFunctor"] * 1024 / copy_bytes
     f_write = per["write"]["MulFunctor"] * 1024 / copy_bytes
     k2_traffic = per["fetch"][k2_name] * 1024 / f_fetch + per["write"][k2_name] * 1024 / f_write
-    k1_traffic = per["fetch"][k1_name] * 1024 / f_fetch + per["write"][k1_name] * 1024 / f_write
+    k1_traffic = (per["fetch"][k1_name] * 1024 / f_fetch + per["write"][k1_name] * 1024 / f_write
+                  if k1_name else None)
     t = [f"# HBM traffic per dispatch from rocprofv3 counters, workload {workload} "
          f"(M={M} K={K} N={N} rank {rank}, {desc})",
          f"# fetch command: {cmds['fetch']}",
@@ -542,10 +549,12 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
          f"fetch_factor = {f_fetch:.4f}",
          f"write_factor = {f_write:.4f}"]
     for k in (k1_name, k2_name):
-        t.append(f"{k}_fetch_KiB = {per['fetch'][k]:.1f}")
-        t.append(f"{k}_write_KiB = {per['write'][k]:.1f}")
-    t += [f"k1_traffic_bytes_per_launch = {k1_traffic:.0f}",
-          f"traffic_bytes_per_launch = {k2_traffic:.0f}",
+        if k:
+            t.append(f"{k}_fetch_KiB = {per['fetch'][k]:.1f}")
+            t.append(f"{k}_write_KiB = {per['write'][k]:.1f}")
+    if k1_traffic is not None:
+        t.append(f"k1_traffic_bytes_per_launch = {k1_traffic:.0f}")
+    t += [f"traffic_bytes_per_launch = {k2_traffic:.0f}",
           f"gemm_source_sha256_16 = {gemm_source_hash(workload)}"]
     with open(traffic_file(workload), "w") as f:
         f.write("\n".join(t) + "\n")

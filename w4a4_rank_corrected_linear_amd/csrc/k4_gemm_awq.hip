@@ -14,9 +14,10 @@
 // 32 x 32).  The accumulators are held in the MFMA's own orientation: lane l % 32 is
 // the output column, so a block's group scale and bias are one value per lane.  A
 // stage is one 64-group.  LDS holds two activation tiles (256 x 64 bf16, 16-byte units
-// swizzled as u = row 8 + (c ^ (row & 7)), c = k / 8), three raw weight slices (BN x
-// 32 bytes of nibbles) and two expanded weight tiles (BN x 64 bf16, the same swizzle
-// by column).  At the top of stage t every wave waits for its own copies, one barrier
+// swizzled as u = row 8 + (c ^ ((row / 2) & 7)), c = k / 8, so that the sixteen lanes
+// a fragment read serves at once, two rows per 256 bytes of the 64 banks, hit distinct
+// banks), three raw weight slices (BN x 32 bytes of nibbles) and two expanded weight
+// tiles (BN x 64 bf16, the same swizzle by column).  At the top of stage t every wave waits for its own copies, one barrier
 // publishes them together with the weight tile expanded during stage t - 1, and the
 // copies of stage t + 1's activations and stage t + 2's nibbles start (LDS DMA, 16
 // bytes per lane), after the global loads of the next group's scales and the zero
@@ -59,7 +60,7 @@ k4_gemm_awq(const uint16_t* __restrict__ X, const uint8_t* __restrict__ Q,
   const uint32_t lds0 = lds_addr(lds);
 
   // Copies.  Activations: wave w moves 16-byte units (4w + t) 64 + lane, t < 4, i.e.
-  // rows 32w + 8t + lane / 8, chunk (lane % 8) ^ (row % 8); the source is a fixed
+  // rows 32w + 8t + lane / 8, chunk (lane % 8) ^ ((row / 2) % 8); the source is a fixed
   // per-lane offset from a per-stage base.  Weight nibbles: wave j < QB / 1 KiB moves
   // units 64 j + lane (column u / 2, half u % 2).
   const uint8_t* xbase = reinterpret_cast<const uint8_t*>(X) + (size_t)row0 * K * 2;
@@ -67,7 +68,7 @@ k4_gemm_awq(const uint16_t* __restrict__ X, const uint8_t* __restrict__ Q,
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int r = 32 * wave + 8 * t + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     voffA[t] = (uint32_t)(min(row0 + r, M - 1) - row0) * (uint32_t)K * 2u + 16u * c;
   }
   const uint8_t* qbase = Q + (size_t)col0 * (K / 2);
@@ -165,16 +166,16 @@ k4_gemm_awq(const uint16_t* __restrict__ X, const uint8_t* __restrict__ Q,
       const float fo = (float)((od >> (8 * b)) & 0xFFu) - 16.0f;
       o[b] = (__float_as_uint(fe) >> 16) | (__float_as_uint(fo) & 0xFFFF0000u);
     }
-    *reinterpret_cast<uint4*>(lds + OFF_W + buf * WB + 16 * (c * 8 + (h ^ (c & 7)))) =
+    *reinterpret_cast<uint4*>(lds + OFF_W + buf * WB + 16 * (c * 8 + (h ^ ((c >> 1) & 7)))) =
         make_uint4(o[0], o[1], o[2], o[3]);
   };
 
   // Fragment addresses: lane l reads row (or column) 32 blk + l % 32, 16-byte unit
-  // (2 c + l / 32) ^ (l % 8) of k-chunk c; the per-lane part is the same for both
+  // (2 c + l / 32) ^ ((l % 32) / 2 % 8) of k-chunk c; the per-lane part is the same for both
   // operands.
   uint32_t foff[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) foff[c] = (uint32_t)(lr * 128 + 16 * ((2 * c + lh) ^ (lane & 7)));
+  for (int c = 0; c < 4; ++c) foff[c] = (uint32_t)(lr * 128 + 16 * ((2 * c + lh) ^ ((lr >> 1) & 7)));
   typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
   auto frag = [&](uint32_t base, int c) { return *(lds_v8bf*)(uintptr_t)(base + foff[c]); };
 
