@@ -168,3 +168,28 @@ def test_qkv_norm_rope_nvfp4(tiny_qkv_nvfp4, M):
     r = OL.w4a4_linear("nvfp4", li.x[:M], layer)["r"]
     check_y(y, AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[:M]))
     assert np.array_equal(y[:, 512:], host_bits(dev(x))[:, 512:])
+
+
+def test_qkv_norm_rope_nvfp4_dit_block_full_size():
+    """The NVFP4 GEMM's fused QKV epilogue at the block's shape (M = 4608, 3072 -> 9216,
+    1296 tiles of one head over several rounds) with the 1024x1024 rotary table:
+    sampled rows of text and image tokens against the oracle, and the V columns equal
+    to the plain NVFP4 linear bit for bit."""
+    pb = I.prepared_nvfp4_bytes(3, 3072, 9216, 32)
+    layer = P.SvdqLayer(precision="nvfp4", K=pb.K, N=pb.N, rank=pb.rank, qweight=pb.qweight,
+                        wscales=pb.wscales, w_global=pb.w_global, act_global=pb.act_global,
+                        smooth=pb.smooth, lora_down=pb.lora_down, lora_up=pb.lora_up, bias=pb.bias)
+    dev = svdq.SvdqLinear.from_interchange(
+        dev_u8(pb.qweight), dev_u8(pb.wscales), dev_bf16(pb.smooth), dev_bf16(pb.lora_down),
+        dev_bf16(pb.lora_up), dev_bf16(pb.bias), precision="nvfp4", w_global=pb.w_global,
+        act_global=pb.act_global)
+    M = 4608
+    x = I.chain_step_activations(M, 0)
+    rope = I.rope_table(M)
+    nq, nk = I.qk_norm_weights()
+    xd = dev_bf16(x)
+    y = host_bits(dev.qkv_norm_rope(xd, dev_bf16(nq), dev_bf16(nk), EPS, dev_f32(rope)))
+    rows = np.array([0, 1, 511, 512, 1000, 2222, 4000, 4607])
+    r = OL.w4a4_linear_rows("nvfp4", x, layer, rows)["r"]
+    check_y(y[rows], AT.qkv_norm_rope_f64(r, nq, nk, EPS, rope[rows]))
+    assert np.array_equal(y[:, 6144:], host_bits(dev(xd))[:, 6144:])
