@@ -36,11 +36,14 @@ __device__ __forceinline__ uint32_t int4_quant32(const float (&xh)[32], float (&
   const uint32_t s_bits = f32_to_bf16_rne(amax / 7.0f);
   const float s = bf16_to_f32(s_bits);
   const bool tiny = (s > 0.f) && (s < 0x1p-125f);
-  // q = round-half-even(xhat / s), decided exactly.  r = v_rcp_f32(s) is within one ulp
-  // of 1/s; y1 = xhat r is then within a few ulp of the quotient, the remainder
-  // e = xhat - y1 s is exact (fma), and y = y1 + e r differs from the quotient by a
-  // few ulp times 2^-23 relative: it rounds exactly onto k + 1/2 at a tie, while a
-  // non-tie quotient of two bf16 numbers lies at least 2^-9 from any half-integer.
+  // q = round-half-even(xhat / s), decided exactly without a division.  r = v_rcp_f32(s)
+  // is within one ulp of 1/s, so xhat r is within 7.02 * 2^-23 < 2^-20 of the quotient
+  // Q.  y = fl(xhat r + 192) - 192 puts it on the grid of 2^-16 (the fma rounds once,
+  // in the binade [128, 256); the subtraction is exact): at a tie Q = k + 1/2, itself
+  // on the grid, y is exactly k + 1/2 (the error is below half a step), and a non-tie
+  // quotient of two bf16 numbers with |Q| >= 1/4 lies more than 2^-12 from every
+  // half-integer (Q = a / (b 2^d) with integers |a|, b < 256 and d <= 2), far beyond
+  // the 2^-17 + 2^-20 that y can move, so y rounds to the integer Q rounds to.
   // With s = 0 every value is 0 and r = 0 gives y = 0.  A normal bf16 scale is within
   // 2^-9 relative of amax / 7, so |y| <= 7.014 and rounding to the nearest integer
   // already lands in [-7, 7]: the common path needs no clamp.  Scales below 2^-125
@@ -51,17 +54,11 @@ __device__ __forceinline__ uint32_t int4_quant32(const float (&xh)[32], float (&
   const float rcp = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
   if (!__any(tiny)) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float y1 = xh[i] * rcp;
-      const float e = __builtin_fmaf(-y1, s, xh[i]);
-      cq[i] = __builtin_fmaf(e, rcp, y1);
-    }
+    for (int i = 0; i < 32; ++i) cq[i] = __builtin_fmaf(xh[i], rcp, 192.0f) - 192.0f;
   } else {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float y1 = xh[i] * rcp;
-      const float e = __builtin_fmaf(-y1, s, xh[i]);
-      const float y = tiny ? __fdiv_rn(xh[i], s) : __builtin_fmaf(e, rcp, y1);
+      const float y = tiny ? __fdiv_rn(xh[i], s) : __builtin_fmaf(xh[i], rcp, 192.0f) - 192.0f;
       cq[i] = __builtin_amdgcn_fmed3f(y, -8.0f, 7.0f);
     }
   }
