@@ -21,12 +21,17 @@ Prints one JSON line:
                changed since they were taken
   cpu_baseline the CPU oracle on the same inputs (full call, repeated for about
                10-30 s), on the host's cores
+  clock_settle before the W warmup steps, the same step runs untimed for --settle-ms
+               (200 ms by default): from an idle GPU the clocks take about 20-25 ms
+               of sustained load to ramp up, and the first calls run up to 25 %
+               slower; the first and last batches' times are reported
 """
 
 from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import statistics
@@ -41,6 +46,7 @@ PEAK_FP6_TFLOPS = 10100.0   # MI355X dense FP6/FP4 MFMA
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
 COLD_SETS = 5                # rotating operand sets of the cold-cache pass (> 256 MB in all)
+SETTLE_MS = 200.0            # untimed sustained load before the warmup steps (clock ramp)
 
 WORKLOADS = {
     # name: (method, config id, M, K, N, rank)
@@ -162,6 +168,36 @@ def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 8):
                       f"{t:.3f} s (float64 numpy/BLAS)"}
 
 
+def clock_settle(step, ms: float, per_batch: int) -> dict | None:
+    """Runs `step` untimed in batches of `per_batch` (synchronized) until `ms` of wall
+    time have passed, so that the timed steps start at the clocks sustained load runs
+    at; returns the settle time, the step count and the first and last batches' times
+    per step, or None when ms <= 0."""
+    import torch
+    if ms <= 0:
+        return None
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    n, batches = 0, []
+    while True:
+        t0 = time.perf_counter()
+        for _ in range(per_batch):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n += per_batch
+        batches.append((t1 - t0) * 1e3 / per_batch)
+        if (t1 - t_start) * 1e3 >= ms:
+            break
+    out = {"ms": round((t1 - t_start) * 1e3, 1), "steps": n,
+           "ms_per_step_first_batch": round(batches[0], 6),
+           "ms_per_step_last_batch": round(batches[-1], 6)}
+    print(f"[bench] clock settle: {n} untimed steps in {out['ms']} ms, "
+          f"{out['ms_per_step_first_batch']} ms per step in the first batch, "
+          f"{out['ms_per_step_last_batch']} in the last", file=sys.stderr, flush=True)
+    return out
+
+
 def run_chain(args) -> int:
     """One DiT block's four W4A4 linears and the GELU per denoise step (config 5): the
     steps cycle through 8 fresh seeded inputs resident in HBM; K timed steps, then an
@@ -196,6 +232,8 @@ def run_chain(args) -> int:
     xs = [bf16(I.chain_step_activations(M, s)) for s in range(8)]
     print(f"[bench] workload chain: DiT block (QKV, out, MLP-up, GELU, MLP-down), M={M}, 8 fresh "
           f"step inputs; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    settle_i = itertools.count()
+    settle = clock_settle(lambda: chain(xs[next(settle_i) % 8], rope), args.settle_ms, 2)
     for i in range(args.warmup):
         chain(xs[i % 8], rope)
     torch.cuda.synchronize()
@@ -296,6 +334,7 @@ def run_chain(args) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settle,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -363,6 +402,7 @@ def run_prep(args) -> int:
     steps, warmup = min(args.steps, 20), min(args.warmup, 3)
     print(f"[bench] workload prep: K=N={K}, rank {rank}, oversample {over}, {iters} power "
           f"iterations; warmup {warmup}, steps {steps}", file=sys.stderr, flush=True)
+    settle = clock_settle(call, args.settle_ms, 1)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -382,6 +422,7 @@ def run_prep(args) -> int:
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "clock_settle": settle,
         "ms_per_step": round(ms, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -679,6 +720,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed sustained load before the warmup steps (0: none)")
     ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS) + ["chain", "prep"])
     ap.add_argument("--batch", type=int, default=1, choices=[1, 4],
                     help="chain workload: images per step (M = 4608 per image)")
@@ -765,6 +808,7 @@ def main() -> int:
     print(f"[bench] workload {args.workload} ({method}) M={M} K={K} N={N} rank={rank}; warmup "
           f"{args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
 
+    settle = clock_settle(call, args.settle_ms, 20)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -844,6 +888,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settle,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
