@@ -160,8 +160,8 @@ __device__ __forceinline__ void k1_batch(const K1Args& a) {
     __syncthreads();
     for (int t = threadIdx.x; t < 16 * rank; t += 256) {
       const int rr = t / rank, cc = t % rank;
-      a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)] =
-          ((ured[0][rr][cc] + ured[1][rr][cc]) + ured[2][rr][cc]) + ured[3][rr][cc];
+      store_wt(&a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)],
+               ((ured[0][rr][cc] + ured[1][rr][cc]) + ured[2][rr][cc]) + ured[3][rr][cc]);
     }
   }
 }

@@ -93,10 +93,10 @@ struct QuantInt4Fused {
     // h*32 + row%32 holds dwords 0-3 at slot*16 and dwords 4-5 at 1024 + slot*8.
     uint8_t* chunk = a.out + ((size_t)(row >> 5) * (a.K >> 6) + g) * 1536;
     const int slot = h * 32 + (row & 31);
-    *reinterpret_cast<uint4*>(chunk + slot * 16) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-    *reinterpret_cast<uint2*>(chunk + 1024 + slot * 8) = make_uint2(f6[4], f6[5]);
+    store_wt(chunk + slot * 16, make_uint4(f6[0], f6[1], f6[2], f6[3]));
+    store_wt(chunk + 1024 + slot * 8, make_uint2(f6[4], f6[5]));
     if (h == 0)
-      static_cast<uint2*>(a.scales)[(size_t)g * a.M_pad + row] = make_uint2(s_bits << (16 * (g & 1)), 0u);
+      store_wt(static_cast<uint2*>(a.scales) + (size_t)g * a.M_pad + row, make_uint2(s_bits << (16 * (g & 1)), 0u));
   }
 };
 

@@ -49,12 +49,11 @@ struct QuantNvfp4Fused {
     uint8_t* chunk = a.out + ((size_t)(row >> 5) * (a.K >> 6) + g64) * 1024;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<uint2*>(chunk + (h * 32 + (row & 31)) * 16 + j0 * 4) = make_uint2(d[0][h], d[1][h]);
+      store_wt(chunk + (h * 32 + (row & 31)) * 16 + j0 * 4, make_uint2(d[0][h], d[1][h]));
     // the two block scales as fp16 (exact: E4M3 values are fp16 numbers)
     const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)e4m3_value(sc[0]));
     const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)e4m3_value(sc[1]));
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.scales) + ((size_t)g64 * a.M_pad + row) * 4 + j0) =
-        h0 | (h1 << 16);
+    store_wt(static_cast<uint16_t*>(a.scales) + ((size_t)g64 * a.M_pad + row) * 4 + j0, h0 | (h1 << 16));
   }
 };
 

@@ -180,7 +180,7 @@ __device__ __forceinline__ void k1_rows32(const K1Args& a) {
           v.z += p[w].z;
           v.w += p[w].w;
         }
-      *reinterpret_cast<float4*>(&a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)]) = v;
+      store_wt(&a.uact[u_frag_index(blockIdx.y, row0 + rr, cc, a.M_pad, rank)], v4f{v.x, v.y, v.z, v.w});
     }
   }
 }
