@@ -95,6 +95,17 @@ __device__ __forceinline__ void store_wt(float* p, float v) {
   asm volatile("global_store_dword %0, %1, off sc1" :: "v"(p), "v"(v) : "memory");
 }
 
+// LDS DMA copy: lane i's 16 bytes at g go to LDS at lds + 16 i (lds wave-uniform).
+// Written as asm so that the compiler does not see it: for the builtin it waits for
+// every copy in flight before any LDS access of the wave (it cannot tell the copy's
+// destination from the accessed tile), which serializes a ring of tiles.  Every read
+// of a copied tile must therefore follow an explicit s_waitcnt vmcnt that covers the
+// copy; the instruction has no register result.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
 // float -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -8,8 +8,8 @@
 // rounded).
 //
 // Two kernels share the quantizer below:
-//  * k1_int4_fused / k1_int4_fused16 (the layer's own path) use the row-pair skeleton
-//    of k1_rows32.h or the 16-row batch skeleton of k1_batch.h and write the GEMM
+//  * k1_int4_fused / k1_int4_stream (the layer's own path) use the row-pair skeleton
+//    of k1_rows32.h or the row-stream skeleton of k1_stream.h and write the GEMM
 //    operand layout, scales [K/64][M_pad] (8-byte records by
 //    group parity, see common.h) and partial U per k-split in the fragment layout;
 //  * k1_int4_interchange (svdq_quantize_act) streams whole rows with register
@@ -19,8 +19,9 @@
 // same 32 values are one MFMA lane slot of the GEMM's A operand, so the fused layout
 // is produced in registers by v_cvt_scalef32_2xpk16_fp6_f32.
 #include "common.h"
-#include "k1_batch.h"
+#include "k1_common.h"
 #include "k1_rows32.h"
+#include "k1_stream.h"
 #include "kernels.h"
 
 namespace svdq {
@@ -66,6 +67,7 @@ __device__ __forceinline__ uint32_t int4_quant32(const float (&xh)[32], float (&
 }
 
 struct QuantInt4Fused {
+  static constexpr int kStores = 3;  // vector memory stores per call (wait counts)
   __device__ static void block(const K1Args& a, const float (&xh)[32], int row, int k0, int q) {
     float cq[32];
     const uint32_t s_bits = int4_quant32(xh, cq);
@@ -100,12 +102,11 @@ struct QuantInt4Fused {
   }
 };
 
-// Two skeletons of the same computation (identical codes and scales; U summed over the
-// waves in a different order): 32 rows and twelve waves per workgroup, one workgroup
-// per CU, when all workgroups fit in one round on the CUs; else 16 rows and four waves,
-// two workgroups per CU, whose smaller workgroups leave a finer last round.
+// Two skeletons of the same computation (identical codes, scales and U): 32 rows per
+// workgroup when all workgroups fit in one round on the CUs; else resident workgroups,
+// one per CU, that stream 16-row units and keep their k-split's operands loaded.
 __global__ void __launch_bounds__(768, 1) k1_int4_fused(K1Args a) { k1_rows32<QuantInt4Fused>(a); }
-__global__ void __launch_bounds__(256, 2) k1_int4_fused16(K1Args a) { k1_batch<QuantInt4Fused>(a); }
+__global__ void __launch_bounds__(768, 1) k1_int4_stream(K1Args a) { k1_stream<QuantInt4Fused>(a); }
 
 // Interchange kernel: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide
 // k-blocks kb = w, w+8, ... and prefetches the next block's X, smoothing and
@@ -255,8 +256,9 @@ hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uin
       hipExtLaunchKernelGGL(k1_int4_fused, dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0, st,
                             ev0, ev1, 0, a);
     } else {
-      hipExtLaunchKernelGGL(k1_int4_fused16, dim3(M_pad / 16, splits), dim3(256), 0, st, ev0, ev1, 0,
-                            a);
+      const int P = k1_stream_workgroups(M_pad, splits);
+      hipExtLaunchKernelGGL(k1_int4_stream, dim3(P, splits), dim3(64 * kK1StreamWaves), 0, st, ev0,
+                            ev1, 0, a);
     }
   } else {
     dim3 grid((M + 15) / 16);

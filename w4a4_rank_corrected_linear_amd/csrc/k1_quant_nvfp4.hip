@@ -12,22 +12,25 @@
 // k0 .. k0 + 31 of a 128-wide k-block (k0 = 128 kb + 32 q, q = l/16), i.e. two whole
 // NVFP4 blocks, so every amax is an in-lane max.
 //
-// Two kernels share the quantizer below: k1_nvfp4_fused and k1_nvfp4_fused32 (the
-// layer's own path, the batch and row-pair skeletons of k1_batch.h and k1_rows32.h)
+// Two kernels share the quantizer below: k1_nvfp4_fused32 and k1_nvfp4_stream (the
+// layer's own path, the row-pair and row-stream skeletons of k1_rows32.h and
+// k1_stream.h)
 // write the GEMM operand 4-bit: the E2M1 codes in the FP4 lane-slot layout of common.h
 // and each block's E4M3 scale as its exact fp16 value, plus partial U per k-split; the
 // per-tensor scale g stays out of the operand and is applied to the GEMM's fp32
 // result.  k1_nvfp4_interchange (svdq_quantize_act) writes codes [M][K/2] (element 2j
 // in bits 3:0), E4M3 scale bytes [M][K/16] and U [M][r].
 #include "common.h"
-#include "k1_batch.h"
+#include "k1_common.h"
 #include "k1_rows32.h"
+#include "k1_stream.h"
 #include "nvfp4_device.h"
 #include "kernels.h"
 
 namespace svdq {
 
 struct QuantNvfp4Fused {
+  static constexpr int kStores = 3;  // vector memory stores per call (wait counts)
   __device__ static void block(const K1Args& a, const float (&xh)[32], int row, int k0, int q) {
     (void)q;
     uint32_t codes[32], sc[2];
@@ -58,8 +61,8 @@ struct QuantNvfp4Fused {
 };
 
 // The two skeletons of the int4 quantizer, chosen the same way (k1_quant_int4.hip).
-__global__ void __launch_bounds__(256, 2) k1_nvfp4_fused(K1Args a) { k1_batch<QuantNvfp4Fused>(a); }
 __global__ void __launch_bounds__(768, 1) k1_nvfp4_fused32(K1Args a) { k1_rows32<QuantNvfp4Fused>(a); }
+__global__ void __launch_bounds__(768, 1) k1_nvfp4_stream(K1Args a) { k1_stream<QuantNvfp4Fused>(a); }
 
 struct K1Load {
   uint4 x[4];
@@ -200,8 +203,9 @@ hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const ui
       hipExtLaunchKernelGGL(k1_nvfp4_fused32, dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0,
                             st, ev0, ev1, 0, a);
     } else {
-      hipExtLaunchKernelGGL(k1_nvfp4_fused, dim3(M_pad / 16, splits), dim3(256), 0, st, ev0, ev1, 0,
-                            a);
+      const int P = k1_stream_workgroups(M_pad, splits);
+      hipExtLaunchKernelGGL(k1_nvfp4_stream, dim3(P, splits), dim3(64 * kK1StreamWaves), 0, st, ev0,
+                            ev1, 0, a);
     }
   } else {
     dim3 grid((M + 15) / 16);

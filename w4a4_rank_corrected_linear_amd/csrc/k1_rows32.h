@@ -11,7 +11,10 @@
 //
 // Each wave issues its smoothing slice and lora_down operands (registers), then its
 // two X tiles (16 rows x 128 values, 4 KiB each) into LDS with global_load_lds, and
-// quantizes the first half while the second is still in flight.  X tiles are stored
+// quantizes the two halves in turn (the compiler holds the first half's reads until
+// both copies have landed: it orders LDS reads after every copy in flight; both land
+// at nearly the same time, so the asm copies of k1_stream.h gain nothing here).  X
+// tiles are stored
 // as 16-byte units u = row * 16 + (c ^ (row & 7)) (c = k / 8 within the block), which
 // puts the eight rows of one read in distinct bank groups.  The smoothing slice is
 // widened to fp32 in LDS once per wave.  In the workgroup that holds the last rows,
@@ -24,7 +27,7 @@
 // order and written as the split's partial U (fp32, the fragment layout of common.h);
 // the GEMM adds the splits in a fixed order, so U is deterministic.
 #pragma once
-#include "k1_batch.h"
+#include "k1_common.h"
 
 namespace svdq {
 
