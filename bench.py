@@ -552,7 +552,8 @@ def summarize_profiles(out_dir: str, workload: str = "attn_proj") -> None:
     desc = {"int4": "int4 g64", "nvfp4": "nvfp4 g16", "awq": "awq_w4a16 int4 g64"}[method]
     cmds = {k: v.format(w=workload) for k, v in PROFILE_CMDS.items()}
     lines = [f"# rocprofv3 kernel statistics: bench.py, workload {workload} "
-             f"(M={M} K={K} N={N} rank {rank}, {desc}), 50 warmup + 500 timed + 500 event-timed calls",
+             f"(M={M} K={K} N={N} rank {rank}, {desc}), 200 ms untimed clock settle, 50 warmup + "
+             f"500 timed + 500 event-timed calls",
              f"# command: {cmds['stats']}",
              "# kernel                      calls     avg_us     min_us     max_us   share_%"]
     for r in csv.DictReader(open(one("prof_stats/**/*kernel_stats.csv"))):
