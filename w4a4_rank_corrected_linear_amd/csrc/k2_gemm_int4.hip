@@ -68,7 +68,7 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
              const uint2* __restrict__ sB, const uint16_t* __restrict__ L2t,
              const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
              int M, int N, int K, int M_pad, int rank, QkEpi qk, int full_tiles, int ks,
-             float* __restrict__ part) {
+             float* __restrict__ part, int y_wt) {
   constexpr int WMW = BM / 64;             // waves along the rows (4 or 2)
   constexpr int WNW = 8 / WMW;             // waves along the columns (2 or 4)
   constexpr int WC = BN / WNW;             // columns per wave
@@ -676,7 +676,11 @@ k2_gemm_int4(const uint8_t* __restrict__ A, const uint2* __restrict__ sA,
     const int row = c / CPR, ch = c % CPR;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + row * (WC + 8) + ch * 8);
     const int grow = row0 + wm * 64 + row;
-    if (grow < M) *reinterpret_cast<uint4*>(Y + (size_t)grow * N + col0 + wn * WC + ch * 8) = v;
+    if (grow < M) {
+      uint16_t* yp = Y + (size_t)grow * N + col0 + wn * WC + ch * 8;
+      if (y_wt) store_wt(yp, v);
+      else *reinterpret_cast<uint4*>(yp) = v;
+    }
   }
 }
 
@@ -877,8 +881,14 @@ hipError_t launch_k2_int4(const K2Plan& plan, const uint8_t* A, const uint2* sA,
   auto k = qkv ? k2_gemm_int4<128, 384, kEpiQkNormRope>
            : wide ? (epi == kEpiGelu ? k2_gemm_int4<256, 192, kEpiGelu> : k2_gemm_int4<256, 192, kEpiPlain>)
                   : (epi == kEpiGelu ? k2_gemm_int4<256, 128, kEpiGelu> : k2_gemm_int4<256, 128, kEpiPlain>);
+  // Y written through the L2 at device scope when every tile runs in the one round: then
+  // all tiles store at the end together and nothing is left for the release at the
+  // kernel's end to write back (C2, same box: 51.6-52.1 -> 51.0-51.5 us per call).  With
+  // more rounds the write-through stores of finished tiles load the fabric under the
+  // other tiles' main loops (QKV +1.5, MLP-up +2.2 us), so they keep plain stores.
+  const int y_wt = !split && g <= (unsigned)device_cu_count();
   hipExtLaunchKernelGGL(k, dim3(g), dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB, L2t,
-                        bias, Y, M, N, K, M_pad, rank, qk, plan.full, plan.ks, part);
+                        bias, Y, M, N, K, M_pad, rank, qk, plan.full, plan.ks, part, y_wt);
   if (split) {
     const unsigned gt = (unsigned)((plan.tiles - plan.full) * (plan.bm / 32) * (plan.bn == 384 ? 3 : 1));
     auto kt = qkv ? k2_tail_int4<128, 384, kEpiQkNormRope>
