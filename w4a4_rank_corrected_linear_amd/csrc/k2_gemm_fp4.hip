@@ -62,7 +62,7 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
             const float* __restrict__ U, int nsplit, const uint8_t* __restrict__ B,
             const uint16_t* __restrict__ sB, const uint16_t* __restrict__ L2t,
             const uint16_t* __restrict__ bias, float g, uint16_t* __restrict__ Y, int M, int N,
-            int K, int M_pad, int rank, QkEpi qk) {
+            int K, int M_pad, int rank, QkEpi qk, int y_wt) {
   constexpr int BM = 256, BN = 64 * WN, CB = BN / 32;
   constexpr int AC = 8 * 1024, BC = CB * 1024;  // code bytes per stage
   constexpr int AS = BM * 8, BS = BN * 8;       // scale bytes per stage
@@ -364,7 +364,11 @@ k2_gemm_fp4(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sA,
         const int rin = qd >> 2, ch = qd & 3;
         const uint4 v = *reinterpret_cast<const uint4*>(tile + rin * 40 + ch * 8);
         const int row = rowb + rin;
-        if (row < M) *reinterpret_cast<uint4*>(Y + (size_t)row * N + colb + ch * 8) = v;
+        if (row < M) {
+          uint16_t* yp = Y + (size_t)row * N + colb + ch * 8;
+          if (y_wt) store_wt(yp, v);
+          else *reinterpret_cast<uint4*>(yp) = v;
+        }
       }
     }
   }
@@ -384,8 +388,10 @@ hipError_t launch_k2_fp4(const uint8_t* A, const uint16_t* sA, const float* U, i
   auto k = epi == kEpiQkNormRope ? k2_gemm_fp4<2, kEpiQkNormRope>
            : wide ? (epi == kEpiGelu ? k2_gemm_fp4<3, kEpiGelu> : k2_gemm_fp4<3, kEpiPlain>)
                   : (epi == kEpiGelu ? k2_gemm_fp4<2, kEpiGelu> : k2_gemm_fp4<2, kEpiPlain>);
+  // Y through the L2 at device scope when the grid is one round (as in the int4 GEMM)
+  const int y_wt = grid.x <= (unsigned)device_cu_count();
   hipExtLaunchKernelGGL(k, grid, dim3(512), 0, st, ev0, ev1, 0, A, sA, U, nsplit, B, sB, L2t, bias,
-                        g, Y, M, N, K, M_pad, rank, qk);
+                        g, Y, M, N, K, M_pad, rank, qk, y_wt);
   return hipGetLastError();
 }
 

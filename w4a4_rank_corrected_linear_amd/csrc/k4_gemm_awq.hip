@@ -36,7 +36,8 @@ template <int WN, int W>
 __global__ void __launch_bounds__(512, 1)
 k4_gemm_awq(const uint16_t* __restrict__ X, const uint8_t* __restrict__ Q,
             const uint16_t* __restrict__ Sc, const uint8_t* __restrict__ Z,
-            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K) {
+            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K,
+            int y_wt) {
   constexpr int BM = 256, BN = 64 * WN;
   constexpr int AB = BM * 128;         // bytes of an activation tile (256 x 64 bf16)
   constexpr int QB = BN * 32;          // bytes of a raw weight slice (BN x 64 nibbles)
@@ -291,7 +292,11 @@ k4_gemm_awq(const uint16_t* __restrict__ X, const uint8_t* __restrict__ Q,
     const int r = idx / UPR, ch = idx % UPR;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + r * TS + ch * 8);
     const int row = row0 + wm * 64 + r;
-    if (row < M) *reinterpret_cast<uint4*>(Y + (size_t)row * N + col0 + wn * (BN / 2) + ch * 8) = v;
+    if (row < M) {
+      uint16_t* yp = Y + (size_t)row * N + col0 + wn * (BN / 2) + ch * 8;
+      if (y_wt) store_wt(yp, v);
+      else *reinterpret_cast<uint4*>(yp) = v;
+    }
   }
 }
 
@@ -302,14 +307,18 @@ hipError_t launch_k4_awq(const uint16_t* X, const uint8_t* Q, const uint16_t* Sc
   const int tiles_m = (M + 255) / 256;
   const bool w8 = (K / 64) % 8 == 0;  // scale and zero-point loads of 8 groups
   const dim3 blk(512);
+  // Y through the L2 at device scope when the grid is one round (as in the int4 GEMM)
+  const int cus = device_cu_count();
   if (N % 192 == 0) {
     const dim3 grid((N / 192) * tiles_m);
-    if (w8) hipExtLaunchKernelGGL(k4_gemm_awq<3, 8>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
-    else hipExtLaunchKernelGGL(k4_gemm_awq<3, 2>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
+    const int wt = grid.x <= (unsigned)cus;
+    if (w8) hipExtLaunchKernelGGL(k4_gemm_awq<3, 8>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K, wt);
+    else hipExtLaunchKernelGGL(k4_gemm_awq<3, 2>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K, wt);
   } else {
     const dim3 grid((N / 128) * tiles_m);
-    if (w8) hipExtLaunchKernelGGL(k4_gemm_awq<2, 8>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
-    else hipExtLaunchKernelGGL(k4_gemm_awq<2, 2>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K);
+    const int wt = grid.x <= (unsigned)cus;
+    if (w8) hipExtLaunchKernelGGL(k4_gemm_awq<2, 8>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K, wt);
+    else hipExtLaunchKernelGGL(k4_gemm_awq<2, 2>, grid, blk, 0, st, ev0, ev1, 0, X, Q, Sc, Z, bias, Y, M, N, K, wt);
   }
   return hipGetLastError();
 }
