@@ -33,26 +33,15 @@ struct QuantNvfp4Fused {
   static constexpr int kStores = 3;  // vector memory stores per call (wait counts)
   __device__ static void block(const K1Args& a, const float (&xh)[32], int row, int k0, int q) {
     (void)q;
-    uint32_t codes[32], sc[2];
-    float deq[32];
-    nvfp4_quant32(xh, a.g, codes, deq, sc);
+    uint32_t dw[4], sc[2];
+    nvfp4_quant32_packed(xh, a.g, dw, sc);
     // the lane's 32 values are blocks j0 and j0 + 1 of the 64-group k0 / 64; in each,
-    // half h (eight codes, one dword) goes to lane slot 32 h + row % 32 of the chunk
-    uint32_t d[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w |= codes[16 * b + 8 * h + i] << (4 * i);
-        d[b][h] = w;
-      }
+    // half h (eight codes, one dword dw[2 b + h]) goes to lane slot 32 h + row % 32
     const int g64 = k0 >> 6, j0 = (k0 >> 4) & 3;
     uint8_t* chunk = a.out + ((size_t)(row >> 5) * (a.K >> 6) + g64) * 1024;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      store_wt(chunk + (h * 32 + (row & 31)) * 16 + j0 * 4, make_uint2(d[0][h], d[1][h]));
+      store_wt(chunk + (h * 32 + (row & 31)) * 16 + j0 * 4, make_uint2(dw[h], dw[2 + h]));
     // the two block scales as fp16 (exact: E4M3 values are fp16 numbers)
     const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)e4m3_value(sc[0]));
     const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)e4m3_value(sc[1]));
@@ -137,20 +126,11 @@ k1_nvfp4_interchange(const uint16_t* __restrict__ x, int M, int K,
       }
     }
 
-    uint32_t codes[32], sc[2];
-    float deq[32];
-    nvfp4_quant32(xh, g, codes, deq, sc);
+    uint32_t w[4], sc[2];
+    nvfp4_quant32_packed(xh, g, w, sc);
 
     {
       if (valid) {
-        uint32_t w[4];
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          uint32_t acc = 0;
-#pragma unroll
-          for (int i = 7; i >= 0; --i) acc = (acc << 4) | codes[8 * d4 + i];
-          w[d4] = acc;
-        }
         *reinterpret_cast<uint4*>(out + ((size_t)row * K + k0) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
         *reinterpret_cast<uint16_t*>(scales + (size_t)row * (K / 16) + k0 / 16) =
             (uint16_t)(sc[0] | (sc[1] << 8));

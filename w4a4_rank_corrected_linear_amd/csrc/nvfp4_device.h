@@ -41,10 +41,11 @@ __device__ __forceinline__ uint32_t e2m1_twice(uint32_t mag) {
 // inside the normal range: a block with d < 2^-100 or amax r > 2^100 (never produced by
 // sane scales) makes the wave take the IEEE division instead, tested once per wave.
 // The dequantized value e2m1 * s is (2 e2m1) * (s / 2), exact in fp32 and in bf16.
-__device__ __forceinline__ void nvfp4_quant32(const float (&xh)[32], float g, uint32_t (&codes)[32],
-                                              float (&deq)[32], uint32_t (&sc)[2]) {
+// Block scale codes sc, scales s, divisors d = fl32(s g) and reciprocals r of the lane's
+// two blocks; true when a block leaves the range of the fma division (see above).
+__device__ __forceinline__ bool nvfp4_block_scales(const float (&xh)[32], float g, float (&s)[2],
+                                                   float (&d)[2], float (&r)[2], uint32_t (&sc)[2]) {
   const float denom = 6.0f * g;  // fl32(6 g)
-  float s[2], d[2], r[2];
   bool odd = false;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -58,6 +59,52 @@ __device__ __forceinline__ void nvfp4_quant32(const float (&xh)[32], float g, ui
     r[b] = s[b] > 0.f ? 1.0f / d[b] : 0.f;
     odd |= s[b] > 0.f && !(d[b] >= 0x1p-100f && amax * r[b] <= 0x1p100f);
   }
+  return odd;
+}
+
+// The lane's codes packed as the operand dwords: dw[2 b + h] holds the eight codes of
+// block b, k = 16 b + 8 h + [0, 8), element e in bits 4e..4e+3 (the quantizer's GEMM
+// operand and interchange layouts both store these dwords as they are).  The quotients
+// are those of nvfp4_quant32, refined as y - e' r with e' = y d - xhat, which keeps the
+// sign of a zero quotient (-0 stays -0: the sign is the quotient's, i.e. xhat's), so
+// the converter's own signed codes are the codes; it writes two of them into byte i of
+// the dword (its destination-byte operand).  A block with s = 0 has zero codes.
+__device__ __forceinline__ void nvfp4_quant32_packed(const float (&xh)[32], float g,
+                                                     uint32_t (&dw)[4], uint32_t (&sc)[2]) {
+  float s[2], d[2], r[2];
+  const bool odd = nvfp4_block_scales(xh, g, s, d, r, sc);
+  float quot[32];
+  if (__any(odd)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      quot[i] = __builtin_amdgcn_fmed3f(s[i >> 4] > 0.f ? xh[i] / d[i >> 4] : 0.f, -8.0f, 8.0f);
+  } else {
+    // |quotient| <= 6 / (1 - 2^-4): the converter saturates it at 6 without a clamp
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float y = xh[i] * r[i >> 4];
+      const float en = __builtin_fmaf(y, d[i >> 4], -xh[i]);  // exact: y d - xhat
+      quot[i] = __builtin_fmaf(-en, r[i >> 4], y);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e0 = 16 * b + 8 * h;
+      uint32_t w = 0;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, quot[e0 + 0], quot[e0 + 1], 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, quot[e0 + 2], quot[e0 + 3], 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, quot[e0 + 4], quot[e0 + 5], 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, quot[e0 + 6], quot[e0 + 7], 1.0f, 3);
+      dw[2 * b + h] = s[b] > 0.f ? w : 0u;
+    }
+}
+
+__device__ __forceinline__ void nvfp4_quant32(const float (&xh)[32], float g, uint32_t (&codes)[32],
+                                              float (&deq)[32], uint32_t (&sc)[2]) {
+  float s[2], d[2], r[2];
+  const bool odd = nvfp4_block_scales(xh, g, s, d, r, sc);
   float quot[32];
   if (__any(odd)) {
 #pragma unroll
