@@ -109,10 +109,11 @@ def test_nvfp4_layer_quantizer_bitexact(M, K):
 # The row-stream skeleton with padding rows (M = 4500: M_pad = 4608, so the 16-row unit
 # 281 holds 4 real rows and units 282..287 none) and every rank it supports: its wait
 # counts depend on the rank (which waves store a partial-U float4) and it has no barrier
-# at rank 0.
-@pytest.mark.parametrize("rank", [0, 16, 32])
-def test_int4_stream_quantizer_ragged_rows(rank):
-    M, K = 4500, 3072
+# at rank 0.  K = 3200 ends in a k-split of one 128-wide block, where eleven of the
+# twelve waves own no block and only take part in the barriers.
+@pytest.mark.parametrize("rank,K", [(0, 3072), (16, 3072), (32, 3072), (32, 3200)])
+def test_int4_stream_quantizer_ragged_rows(rank, K):
+    M = 4500
     x, layer = _inputs(9, M, K, 384, "int4", rank=rank)
     M_pad = -(-M // 256) * 256
     assert (M_pad // 32) * (K // 1536) > 256     # the row-stream skeleton
