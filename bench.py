@@ -227,7 +227,7 @@ def run_chain(args) -> int:
         qk_norm = (nq, nk, I.QK_NORM_EPS)
         rope = torch.from_numpy(I.rope_table(M)).to(dev)
     chain = svdq.DitBlockChain(lay["qkv"], lay["out"], lay["up"], lay["down"],
-                               fuse_gelu=args.fuse_gelu, qk_norm=qk_norm,
+                               fuse_gelu="down" if args.gelu_down else args.fuse_gelu, qk_norm=qk_norm,
                                fuse_qk=not args.qk_separate)
     xs = [bf16(I.chain_step_activations(M, s)) for s in range(8)]
     print(f"[bench] workload chain: DiT block (QKV, out, MLP-up, GELU, MLP-down), M={M}, 8 fresh "
@@ -279,7 +279,7 @@ def run_chain(args) -> int:
     # per-layer times: events around each call on the current stream (they include the
     # dispatch of the call's kernels)
     names = ["qkv"] + (["qk_norm_rope"] if args.qkv_norm_rope and args.qk_separate else []) + (
-        ["out", "up", "down"] if args.fuse_gelu else ["out", "up", "gelu", "down"])
+        ["out", "up", "down"] if (args.fuse_gelu or args.gelu_down) else ["out", "up", "gelu", "down"])
     n_inst = min(args.steps, 200)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in names] for _ in range(n_inst)]
@@ -300,10 +300,15 @@ def run_chain(args) -> int:
              lambda x: lay["out"](x, out=bufs["out"], workspace=ws)]
     if args.fuse_gelu:
         calls.append(lambda x: lay["up"](bufs["out"], out=bufs["act"], workspace=ws, gelu=True))
+    elif args.gelu_down:
+        calls.append(lambda x: lay["up"](bufs["out"], out=bufs["up"], workspace=ws))
     else:
         calls += [lambda x: lay["up"](bufs["out"], out=bufs["up"], workspace=ws),
                   lambda x: svdq.gelu(bufs["up"], out=bufs["act"])]
-    calls.append(lambda x: lay["down"](bufs["act"], out=bufs["down"], workspace=ws))
+    if args.gelu_down:
+        calls.append(lambda x: lay["down"](bufs["up"], out=bufs["down"], workspace=ws, gelu_in=True))
+    else:
+        calls.append(lambda x: lay["down"](bufs["act"], out=bufs["down"], workspace=ws))
     for i in range(n_inst):
         for j, c in enumerate(calls):
             ev[i][j][0].record()
@@ -326,6 +331,7 @@ def run_chain(args) -> int:
     out = {
         "metric": f"DiT block chain of svdq_w4a4 int4 linears (QKV, out, MLP-up, GELU, MLP-down) "
                   f"effective TOPS at M={M}" + (", GELU fused into MLP-up" if args.fuse_gelu else "")
+                  + (", GELU fused into MLP-down's quantizer" if args.gelu_down else "")
                   + ((", Q/K norm + rotary as a separate pass" if args.qk_separate else
                       ", Q/K norm + rotary fused into QKV") if args.qkv_norm_rope else "")
                   + (", 8 steps per HIP graph" if args.graph else ""),
@@ -344,6 +350,7 @@ def run_chain(args) -> int:
         "config": {"workload": f"chain: DiT block, batch {args.batch} (M={M}), 8 fresh step inputs "
                                "cycled, int4 g64 rank 32" + (", GELU in the MLP-up epilogue"
                                                              if args.fuse_gelu else "")
+                               + (", GELU in MLP-down's quantizer" if args.gelu_down else "")
                                + (", 8 steps per HIP graph replay" if args.graph else "")
                                + (", Q/K RMSNorm + rotary in the QKV epilogue"
                                   if args.qkv_norm_rope else ""),
@@ -728,6 +735,9 @@ def main() -> int:
                     help="chain workload: images per step (M = 4608 per image)")
     ap.add_argument("--fuse-gelu", action="store_true",
                     help="chain workload: GELU in the MLP-up GEMM's epilogue")
+    ap.add_argument("--gelu-down", action="store_true",
+                    help="chain workload: GELU in MLP-down's quantizer, applied to MLP-up's bf16 "
+                         "output as it is loaded (svdq_w4a4_linear_gelu_in)")
     ap.add_argument("--graph", action="store_true",
                     help="chain: record the 8 steps into one HIP graph and time its replays")
     ap.add_argument("--qkv-norm-rope", action="store_true",
@@ -750,6 +760,9 @@ def main() -> int:
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    if args.fuse_gelu and args.gelu_down:
+        print("--fuse-gelu and --gelu-down place the one GELU in two layers: pick one", file=sys.stderr)
         return 2
 
     import numpy as np

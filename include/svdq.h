@@ -195,6 +195,19 @@ svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight
                                   const uint16_t* x, int64_t M, float act_global, uint16_t* y,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same layer taking the GELU of its input: the second linear of the DiT MLP, whose
+ * input is the GELU of the first linear's bf16 output (Diffusers docs "Nunchaku Lite",
+ * "Fused kernels": the MLP's GELU fused with its projections).  The quantizer applies
+ *   h = bf16_rne( gelu(x) )   (gelu as in svdq_gelu_bf16, bit for bit)
+ * to each bf16 input value as it loads it and runs the layer on h, so
+ *   Y = svdq_w4a4_linear(h)  exactly (codes, scales, low-rank sums and Y identical to
+ * svdq_gelu_bf16 followed by svdq_w4a4_linear), without writing or reading h.
+ * x [M][K] bf16 is the pre-GELU activation; the other arguments, layouts, ownership and
+ * errors as for svdq_w4a4_linear. */
+svdq_status svdq_w4a4_linear_gelu_in(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                     const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* svdq_w4a4_linear for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, layouts, result and errors as svdq_w4a4_linear, without the workspace

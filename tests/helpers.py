@@ -54,8 +54,12 @@ def check_u(u: np.ndarray, ref: dict, lora_down_bits: np.ndarray, chain: int | N
     """The low-rank down projection: fp32 device result u [M, r] against the oracle's
     float64 U, within the rounding bound of an fp32 accumulation whose chain of
     roundings is at most `chain` deep: |u - U| <= chain 2^-24 sum_k |xhat_k L1[k, j]|.
-    The kernel splits K over 8 waves, each summing at most K/8 products in one chain,
-    then adds the 8 partial sums: chain = K/8 + 16 covers fully sequential rounding."""
+    The default chain = K/8 + 16 is well above the depth of the kernels' sums: the
+    fused quantizers sum each 128-wide k-block on the MFMA (four accumulating calls of
+    32 products), add the k-blocks of a k-split in a fixed order and hand the GEMM one
+    partial per k-split of 1536, which it adds in order; in the interchange quantizer
+    each of 8 waves accumulates its k-blocks w, w + 8, ... on the MFMA (at most K/8
+    products in one chain) and the 8 partials are then added."""
     if chain is None:
         chain = ref["xhat"].shape[1] // 8 + 16
     xh = np.abs(F.bf16_to_f64(ref["xhat"]))

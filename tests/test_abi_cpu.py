@@ -216,6 +216,10 @@ def test_gelu_entry_points_validate_like_the_linear():
     assert lib.svdq_w4a4_linear_gelu(*args(x=FAKE_MISALIGNED)) == L.ERR_ALIGN
     assert lib.svdq_w4a4_linear_gelu(*args(M=0)) == L.OK
     assert "svdq_w4a4_linear_gelu" in (lib.svdq_w4a4_linear_gelu(*args(x=None)) and L.last_error())
+    assert lib.svdq_w4a4_linear_gelu_in(*args(x=None)) == L.ERR_NULL
+    assert lib.svdq_w4a4_linear_gelu_in(*args(x=FAKE_MISALIGNED)) == L.ERR_ALIGN
+    assert lib.svdq_w4a4_linear_gelu_in(*args(M=0)) == L.OK
+    assert "svdq_w4a4_linear_gelu_in" in (lib.svdq_w4a4_linear_gelu_in(*args(x=None)) and L.last_error())
     assert lib.svdq_gelu_bf16(None, FAKE, 8, None) == L.ERR_NULL
     assert lib.svdq_gelu_bf16(FAKE_MISALIGNED, FAKE, 8, None) == L.ERR_ALIGN
     assert lib.svdq_gelu_bf16(FAKE, FAKE, -1, None) == L.ERR_SHAPE

@@ -39,3 +39,9 @@ def test_clock_settle_off():
     assert bench.clock_settle(lambda: calls.append(1), 0.0, 4) is None
     assert bench.clock_settle(lambda: calls.append(1), -5.0, 4) is None
     assert calls == []
+
+
+def test_gelu_in_two_layers_is_refused():
+    r = _run("--workload", "chain", "--fuse-gelu", "--gelu-down")
+    assert r.returncode == 2
+    assert "pick one" in r.stderr

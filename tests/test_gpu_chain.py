@@ -104,7 +104,27 @@ def test_block_chain_with_gelu_fused_into_mlp_up(block):
     check_y(out["down"][rows], ref_down)
 
 
-@pytest.mark.parametrize("fuse", [False, True])
+def test_block_chain_with_gelu_in_mlp_down_quantizer(block):
+    """MLP-down taking the GELU of MLP-up's bf16 output in its quantizer: no hidden
+    activation is written; MLP-down against the oracle on bf16(gelu(up)) formed by the
+    GELU kernel (the same values the quantizer forms), the other layers as before."""
+    layers, _, dev = block
+    chain = svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"], fuse_gelu="down")
+    M = 4608
+    x = I.chain_step_activations(M, 6)
+    r = chain(dev_bf16(x))
+    torch.cuda.synchronize()
+    out = {k: host_bits(v) for k, v in r.items()}
+    assert "act" not in out and set(out) == set(chain.results())
+    rows = np.unique(np.concatenate([np.arange(5, M, M // 12), [0, M - 1]]))
+    check_y(out["up"][rows], OL.w4a4_linear_rows("int4", out["out"], layers["up"], rows)["r"])
+    h = host_bits(svdq.gelu(dev_bf16(out["up"])))
+    check_y(out["down"][rows], OL.w4a4_linear_rows("int4", h, layers["down"], rows)["r"])
+    with pytest.raises(ValueError):
+        svdq.DitBlockChain(dev["qkv"], dev["out"], dev["up"], dev["down"], fuse_gelu="both")
+
+
+@pytest.mark.parametrize("fuse", [False, True, "down"])
 def test_block_chain_graph_replays_match_eager(block, fuse):
     """Three denoise steps recorded into one HIP graph (svdq_capture_begin/end): every
     replay, with eager calls and synchronizations between replays, leaves exactly the
@@ -139,7 +159,8 @@ def test_block_chain_graph_replays_match_eager(block, fuse):
     graph.destroy()
     # the replayed last step against the oracle on sampled rows
     rows = np.array([0, 1234, M - 1])
-    ref_down = OL.w4a4_linear_rows("int4", ref["act"], layers["down"], rows)["r"]
+    act = ref["act"] if "act" in ref else host_bits(svdq.gelu(dev_bf16(ref["up"])))
+    ref_down = OL.w4a4_linear_rows("int4", act, layers["down"], rows)["r"]
     check_y(ref["down"][rows], ref_down)
 
 

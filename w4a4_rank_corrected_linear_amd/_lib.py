@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.svdq_w4a4_linear_gelu.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32, vp, vp,
                                    ctypes.c_size_t, vp]
     L.svdq_w4a4_linear_gelu.restype = st
+    L.svdq_w4a4_linear_gelu_in.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32, vp,
+                                           vp, ctypes.c_size_t, vp]
+    L.svdq_w4a4_linear_gelu_in.restype = st
     L.svdq_w4a4_linear_noalloc.argtypes = [cfgp, ctypes.POINTER(SvdqW4A4Weight), vp, i64, f32, vp, vp]
     L.svdq_w4a4_linear_noalloc.restype = st
     L.svdq_noalloc_max_workspace_bytes.argtypes = []

@@ -158,9 +158,12 @@ class SvdqLinear:
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, act_global: float | None = None,
-                gelu: bool = False):
+                gelu: bool = False, gelu_in: bool = False):
         """y = layer(x); with gelu=True the exact GELU of each result is taken before the
-        bf16 rounding (svdq_w4a4_linear_gelu)."""
+        bf16 rounding (svdq_w4a4_linear_gelu); with gelu_in=True the layer runs on
+        bf16(gelu(x)), formed by the quantizer as it loads x (svdq_w4a4_linear_gelu_in)."""
+        if gelu and gelu_in:
+            raise ValueError("gelu and gelu_in together: no entry point takes both")
         _want(x, torch.bfloat16, "x")
         M, K = x.shape
         if K != self.K:
@@ -170,7 +173,8 @@ class SvdqLinear:
             return y
         ws = self.workspace(M, x.device) if workspace is None else workspace
         g = self.act_global if act_global is None else float(act_global)
-        fn = "svdq_w4a4_linear_gelu" if gelu else "svdq_w4a4_linear"
+        fn = ("svdq_w4a4_linear_gelu" if gelu else
+              "svdq_w4a4_linear_gelu_in" if gelu_in else "svdq_w4a4_linear")
         st = getattr(L.lib(), fn)(ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), M, g,
                                   _p(y), _p(ws), ws.numel(), _stream())
         L.check(st, fn)

@@ -7,8 +7,10 @@ between (Diffusers docs "Nunchaku Lite", "Fused kernels": the block's projection
 its GELU MLP).  Attention itself, the norms and the residual adds are not part of the
 layer: the QKV output is produced for the attention that would consume it, and the
 output projection reads the block's input activations in place of the attention
-output.  The GELU runs either as its own kernel or fused into the MLP-up GEMM's
-epilogue (on the fp32 result, before the bf16 rounding).  Several denoise steps can be
+output.  The GELU runs as its own kernel, fused into the MLP-up GEMM's epilogue (on
+the fp32 result, before the bf16 rounding), or fused into MLP-down's quantizer (on the
+bf16 MLP-up output as the quantizer loads it, the same values the separate kernel
+writes).  Several denoise steps can be
 recorded into one HIP graph and replayed with one launch (the launch overhead that the
 tutorial's torch.compile section recovers).  Every step runs in the library's kernels;
 this module only orders the calls.
@@ -26,8 +28,9 @@ class DitBlockChain:
     3072->12288 and 12288->3072 (any K/N that chain the same way)."""
 
     def __init__(self, qkv: SvdqLinear, out: SvdqLinear, up: SvdqLinear, down: SvdqLinear,
-                 fuse_gelu: bool = False, qk_norm=None, fuse_qk: bool = True):
-        """qk_norm: None, or (norm_q, norm_k, eps) to apply the per-head Q/K RMSNorm and
+                 fuse_gelu: bool | str = False, qk_norm=None, fuse_qk: bool = True):
+        """fuse_gelu: False (the GELU as its own kernel), True or "up" (in MLP-up's
+        epilogue) or "down" (in MLP-down's quantizer).  qk_norm: None, or (norm_q, norm_k, eps) to apply the per-head Q/K RMSNorm and
         rotary embedding to the QKV output, fused into the projection's epilogue
         (fuse_qk) or as a separate pass over its bf16 output; forward then takes the
         rotary table (float32 [M, 64, 2])."""
@@ -36,6 +39,9 @@ class DitBlockChain:
                              f"qkv {qkv.K}->{qkv.N}, out {out.K}->{out.N}, up {up.K}->{up.N}, "
                              f"down {down.K}->{down.N}")
         self.qkv, self.out, self.up, self.down = qkv, out, up, down
+        if fuse_gelu not in (False, True, "up", "down"):
+            raise ValueError(f"fuse_gelu = {fuse_gelu!r}: False, True, 'up' or 'down'")
+        self.gelu_mode = "up" if fuse_gelu is True else (fuse_gelu or "separate")
         self.fuse_gelu = fuse_gelu
         self.qk_norm = qk_norm
         self.fuse_qk = fuse_qk
@@ -50,7 +56,7 @@ class DitBlockChain:
 
     def forward(self, x: torch.Tensor, rope: torch.Tensor | None = None) -> dict:
         """x [M, K] bf16 -> {"qkv", "out", "up", "act", "down"} ("up" absent when the GELU
-        is fused into MLP-up's epilogue); the buffers are reused by the next call of the
+        is fused into MLP-up's epilogue, "act" when it is fused into MLP-down); the buffers are reused by the next call of the
         same M (copy what must outlive it).  rope: the rotary table, needed when the
         chain fuses the Q/K norm and rotary embedding into the QKV projection."""
         M, dev = x.shape[0], x.device
@@ -70,11 +76,16 @@ class DitBlockChain:
         else:
             r["qkv"] = self.qkv(x, out=self._tensor("qkv", (M, self.qkv.N), dev), workspace=ws)
         r["out"] = self.out(x, out=self._tensor("out", (M, self.out.N), dev), workspace=ws)
-        if self.fuse_gelu:
+        if self.gelu_mode == "up":
             r["act"] = self.up(r["out"], out=self._tensor("act", (M, self.up.N), dev), workspace=ws,
                                gelu=True)
         else:
             r["up"] = self.up(r["out"], out=self._tensor("up", (M, self.up.N), dev), workspace=ws)
+        if self.gelu_mode == "down":
+            r["down"] = self.down(r["up"], out=self._tensor("down", (M, self.down.N), dev),
+                                  workspace=ws, gelu_in=True)
+            return r
+        if self.gelu_mode == "separate":
             r["act"] = gelu(r["up"], out=self._tensor("act", (M, self.up.N), dev))
         r["down"] = self.down(r["act"], out=self._tensor("down", (M, self.down.N), dev), workspace=ws)
         return r
@@ -83,7 +94,8 @@ class DitBlockChain:
 
     def results(self) -> dict:
         """The result buffers of the last call or replay, by name (see forward)."""
-        names = ("qkv", "out", "act", "down") if self.fuse_gelu else ("qkv", "out", "up", "act", "down")
+        names = {"up": ("qkv", "out", "act", "down"), "down": ("qkv", "out", "up", "down"),
+                 "separate": ("qkv", "out", "up", "act", "down")}[self.gelu_mode]
         return {n: self._buf[n] for n in names if n in self._buf}
 
     def capture(self, xs, rope: torch.Tensor | None = None) -> "Graph":

@@ -105,8 +105,14 @@ struct QuantInt4Fused {
 // Two skeletons of the same computation (identical codes, scales and U): 32 rows per
 // workgroup when all workgroups fit in one round on the CUs; else resident workgroups,
 // one per CU, that stream 16-row units and keep their k-split's operands loaded.
-__global__ void __launch_bounds__(768, 1) k1_int4_fused(K1Args a) { k1_rows32<QuantInt4Fused>(a); }
-__global__ void __launch_bounds__(768, 1) k1_int4_stream(K1Args a) { k1_stream<QuantInt4Fused>(a); }
+template <bool GELU_IN>
+__global__ void __launch_bounds__(768, 1) k1_int4_fused(K1Args a) {
+  k1_rows32<QuantInt4Fused, GELU_IN>(a);
+}
+template <bool GELU_IN>
+__global__ void __launch_bounds__(768, 1) k1_int4_stream(K1Args a) {
+  k1_stream<QuantInt4Fused, GELU_IN>(a);
+}
 
 // Interchange kernel: a 512-thread workgroup owns 16 rows; wave w takes the 128-wide
 // k-blocks kb = w, w+8, ... and prefetches the next block's X, smoothing and
@@ -245,7 +251,7 @@ k1_int4_interchange(const uint16_t* __restrict__ x, int M, int K,
 //                and group, scale records [K/64][M_pad], partial U per k-split in
 //                the fragment layout of common.h, fp32);
 //                rows >= M are zero.
-hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
+hipError_t launch_k1_int4(bool fused, bool gelu_in, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, void* scales,
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
@@ -253,14 +259,15 @@ hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uin
     K1Args a{x, M, K, smooth, ldown, rank, codes, scales, uact, M_pad, 1.0f};
     const int splits = k1_splits(K);
     if ((int64_t)(M_pad / 32) * splits <= device_cu_count()) {
-      hipExtLaunchKernelGGL(k1_int4_fused, dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0, st,
-                            ev0, ev1, 0, a);
+      hipExtLaunchKernelGGL(gelu_in ? k1_int4_fused<true> : k1_int4_fused<false>,
+                            dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0, st, ev0, ev1, 0, a);
     } else {
       const int P = k1_stream_workgroups(M_pad, splits);
-      hipExtLaunchKernelGGL(k1_int4_stream, dim3(P, splits), dim3(64 * kK1StreamWaves), 0, st, ev0,
-                            ev1, 0, a);
+      hipExtLaunchKernelGGL(gelu_in ? k1_int4_stream<true> : k1_int4_stream<false>, dim3(P, splits),
+                            dim3(64 * kK1StreamWaves), 0, st, ev0, ev1, 0, a);
     }
   } else {
+    if (gelu_in) return hipErrorInvalidValue;  // the GELU input is a fused-layout option only
     dim3 grid((M + 15) / 16);
     hipExtLaunchKernelGGL(k1_int4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,
                           smooth, ldown, rank, codes, static_cast<uint16_t*>(scales), uact);

@@ -50,8 +50,14 @@ struct QuantNvfp4Fused {
 };
 
 // The two skeletons of the int4 quantizer, chosen the same way (k1_quant_int4.hip).
-__global__ void __launch_bounds__(768, 1) k1_nvfp4_fused32(K1Args a) { k1_rows32<QuantNvfp4Fused>(a); }
-__global__ void __launch_bounds__(768, 1) k1_nvfp4_stream(K1Args a) { k1_stream<QuantNvfp4Fused>(a); }
+template <bool GELU_IN>
+__global__ void __launch_bounds__(768, 1) k1_nvfp4_fused32(K1Args a) {
+  k1_rows32<QuantNvfp4Fused, GELU_IN>(a);
+}
+template <bool GELU_IN>
+__global__ void __launch_bounds__(768, 1) k1_nvfp4_stream(K1Args a) {
+  k1_stream<QuantNvfp4Fused, GELU_IN>(a);
+}
 
 struct K1Load {
   uint4 x[4];
@@ -173,21 +179,22 @@ k1_nvfp4_interchange(const uint16_t* __restrict__ x, int M, int K,
 // fused = true : E2M1 codes in the FP4 lane-slot layout and fp16 block scales
 //                [K/64][M_pad][4] (common.h; rows >= M are zero), partial U per k-split
 //                in the fragment layout of common.h.
-hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
+hipError_t launch_k1_nvfp4(bool fused, bool gelu_in, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (fused) {
     K1Args a{x, M, K, smooth, ldown, rank, out, scales, uact, M_pad, g};
     const int splits = k1_splits(K);
     if ((int64_t)(M_pad / 32) * splits <= device_cu_count()) {
-      hipExtLaunchKernelGGL(k1_nvfp4_fused32, dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0,
-                            st, ev0, ev1, 0, a);
+      hipExtLaunchKernelGGL(gelu_in ? k1_nvfp4_fused32<true> : k1_nvfp4_fused32<false>,
+                            dim3(M_pad / 32, splits), dim3(64 * kK1RowsWaves), 0, st, ev0, ev1, 0, a);
     } else {
       const int P = k1_stream_workgroups(M_pad, splits);
-      hipExtLaunchKernelGGL(k1_nvfp4_stream, dim3(P, splits), dim3(64 * kK1StreamWaves), 0, st, ev0,
-                            ev1, 0, a);
+      hipExtLaunchKernelGGL(gelu_in ? k1_nvfp4_stream<true> : k1_nvfp4_stream<false>, dim3(P, splits),
+                            dim3(64 * kK1StreamWaves), 0, st, ev0, ev1, 0, a);
     }
   } else {
+    if (gelu_in) return hipErrorInvalidValue;  // the GELU input is a fused-layout option only
     dim3 grid((M + 15) / 16);
     hipExtLaunchKernelGGL(k1_nvfp4_interchange, grid, dim3(512), 0, st, ev0, ev1, 0, x, M, K,
                           smooth, ldown, rank, g, out, scales, uact);

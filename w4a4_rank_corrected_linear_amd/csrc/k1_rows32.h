@@ -39,7 +39,7 @@ __device__ __forceinline__ void k1r_wait_vm0() { asm volatile("s_waitcnt vmcnt(0
 
 constexpr int kK1RowsWaves = 12;  // waves per workgroup = 128-wide k-blocks per split
 
-template <class QUANT>
+template <class QUANT, bool GELU_IN>
 __device__ __forceinline__ void k1_rows32(const K1Args& a) {
   constexpr int NW = kK1RowsWaves;
   constexpr int RB = 16 * 128;  // bf16 values of one X tile (16 rows)
@@ -132,8 +132,8 @@ __device__ __forceinline__ void k1_rows32(const K1Args& a) {
         const float mf[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float p0 = __uint_as_float(xw[p] << 16) * mf[2 * p];
-          const float p1 = __uint_as_float(xw[p] & 0xFFFF0000u) * mf[2 * p + 1];
+          const float p0 = k1_input<GELU_IN>(xw[p] << 16) * mf[2 * p];
+          const float p1 = k1_input<GELU_IN>(xw[p] & 0xFFFF0000u) * mf[2 * p + 1];
           const v2bf pk = {(__bf16)p0, (__bf16)p1};  // v_cvt_pk_bf16_f32: round to nearest even
           const uint32_t w = __builtin_bit_cast(uint32_t, pk);
           xb[4 * c + p] = w;

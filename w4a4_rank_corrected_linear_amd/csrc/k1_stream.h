@@ -61,7 +61,7 @@ inline int k1_stream_workgroups(int M_pad, int splits) {
   return per < 1 ? 1 : (per < units ? per : units);
 }
 
-template <class QUANT>
+template <class QUANT, bool GELU_IN>
 __device__ __forceinline__ void k1_stream(const K1Args& a) {
   constexpr int NW = kK1StreamWaves;
   constexpr int RB = 16 * 128;  // bf16 values of one X tile (16 rows)
@@ -149,8 +149,8 @@ __device__ __forceinline__ void k1_stream(const K1Args& a) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           // smoothing: xhat = bf16(x * m), one rounding of an exact product
-          const float p0 = __uint_as_float(xw[p] << 16) * mf[2 * p];
-          const float p1 = __uint_as_float(xw[p] & 0xFFFF0000u) * mf[2 * p + 1];
+          const float p0 = k1_input<GELU_IN>(xw[p] << 16) * mf[2 * p];
+          const float p1 = k1_input<GELU_IN>(xw[p] & 0xFFFF0000u) * mf[2 * p + 1];
           const v2bf pk = {(__bf16)p0, (__bf16)p1};  // v_cvt_pk_bf16_f32: round to nearest even
           const uint32_t w = __builtin_bit_cast(uint32_t, pk);
           xb[4 * c + p] = w;

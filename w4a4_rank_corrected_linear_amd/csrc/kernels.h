@@ -17,7 +17,7 @@ namespace svdq {
 constexpr int kK1SplitK = 1536;
 inline int k1_splits(int K) { return (K + kK1SplitK - 1) / kK1SplitK; }
 
-hipError_t launch_k1_int4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
+hipError_t launch_k1_int4(bool fused, bool gelu_in, const uint16_t* x, int M, int K, const uint16_t* smooth,
                           const uint16_t* ldown, int rank, uint8_t* codes, void* scales,
                           float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
@@ -66,7 +66,7 @@ hipError_t launch_k2_int4(const K2Plan& plan, const uint8_t* A, const uint2* sA,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
                           hipEvent_t ev2 = nullptr, hipEvent_t ev3 = nullptr);
 
-hipError_t launch_k1_nvfp4(bool fused, const uint16_t* x, int M, int K, const uint16_t* smooth,
+hipError_t launch_k1_nvfp4(bool fused, bool gelu_in, const uint16_t* x, int M, int K, const uint16_t* smooth,
                            const uint16_t* ldown, int rank, float g, uint8_t* out, uint8_t* scales,
                            float* uact, int M_pad, hipStream_t st, hipEvent_t ev0 = nullptr,
                            hipEvent_t ev1 = nullptr);

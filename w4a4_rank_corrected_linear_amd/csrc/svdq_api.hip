@@ -366,13 +366,13 @@ svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t
   if (M == 0) return ok();
   SVDQ_TRY(check_current_device());
   if (nv)
-    SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(false, x, (int)M, (int)K, smooth,
+    SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(false, false, x, (int)M, (int)K, smooth,
                                               cfg->rank ? lora_down : nullptr, cfg->rank,
                                               act_global, codes, static_cast<uint8_t*>(scales),
                                               cfg->rank ? lora_act : nullptr, (int)M, stream),
                        "quantize kernel launch"));
   else
-    SVDQ_TRY(hip_check(svdq::launch_k1_int4(false, x, (int)M, (int)K, smooth,
+    SVDQ_TRY(hip_check(svdq::launch_k1_int4(false, false, x, (int)M, (int)K, smooth,
                                              cfg->rank ? lora_down : nullptr, cfg->rank, codes,
                                              static_cast<uint16_t*>(scales),
                                              cfg->rank ? lora_act : nullptr, (int)M, stream),
@@ -382,7 +382,9 @@ svdq_status svdq_quantize_act(const svdq_config* cfg, const uint16_t* x, int64_t
 
 namespace {
 
-// The layer call behind svdq_w4a4_linear (gelu = false) and svdq_w4a4_linear_gelu.
+// The layer call behind svdq_w4a4_linear and its variants: epi selects the GEMM's
+// epilogue (plain, GELU on the output, the fused QKV norm and rotation); gelu_in makes
+// the quantizer take bf16(gelu(x)) as the layer's input.
 // The layer's workspace: the caller's buffer, or (scratch = true) the library's own
 // scratch array of kScratchBytes, whose address is looked up after every host check.
 struct Workspace {
@@ -393,7 +395,8 @@ struct Workspace {
 
 svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_weight* w,
                         const uint16_t* x, int64_t M, float act_global, uint16_t* y,
-                        Workspace wsa, int epi, const svdq::QkEpi& qk, hipStream_t stream) {
+                        Workspace wsa, int epi, const svdq::QkEpi& qk, hipStream_t stream,
+                        bool gelu_in = false) {
   void* workspace = wsa.ptr;
   const size_t workspace_bytes = wsa.bytes;
   if (!cfg || !w || !x || !y || (!workspace && !wsa.scratch) || !w->qweight || !w->wscales ||
@@ -450,7 +453,7 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
   timer_begin_call();
   const EvPair e1 = timer_kernel();
   if (nv) {
-    SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(true, x, (int)M, (int)w->K, w->smooth,
+    SVDQ_TRY(hip_check(svdq::launch_k1_nvfp4(true, gelu_in, x, (int)M, (int)w->K, w->smooth,
                                               cfg->rank ? w->lora_down : nullptr, cfg->rank,
                                               act_global, a_codes, ws + L.scales,
                                               cfg->rank ? a_lora : nullptr, (int)L.M_pad, stream,
@@ -467,7 +470,7 @@ svdq_status linear_impl(const char* fn, const svdq_config* cfg, const svdq_w4a4_
                        "gemm kernel launch"));
     return ok();
   }
-  SVDQ_TRY(hip_check(svdq::launch_k1_int4(true, x, (int)M, (int)w->K, w->smooth,
+  SVDQ_TRY(hip_check(svdq::launch_k1_int4(true, gelu_in, x, (int)M, (int)w->K, w->smooth,
                                            cfg->rank ? w->lora_down : nullptr, cfg->rank, a_codes,
                                            a_scales, cfg->rank ? a_lora : nullptr, (int)L.M_pad,
                                            stream, e1.start, e1.end),
@@ -504,6 +507,14 @@ svdq_status svdq_w4a4_linear_gelu(const svdq_config* cfg, const svdq_w4a4_weight
   return linear_impl("svdq_w4a4_linear_gelu", cfg, w, x, M, act_global, y,
                      Workspace{workspace, workspace_bytes, false}, svdq::kEpiGelu, svdq::QkEpi{},
                      stream);
+}
+
+svdq_status svdq_w4a4_linear_gelu_in(const svdq_config* cfg, const svdq_w4a4_weight* w,
+                                     const uint16_t* x, int64_t M, float act_global, uint16_t* y,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return linear_impl("svdq_w4a4_linear_gelu_in", cfg, w, x, M, act_global, y,
+                     Workspace{workspace, workspace_bytes, false}, svdq::kEpiPlain, svdq::QkEpi{},
+                     stream, true);
 }
 
 size_t svdq_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
