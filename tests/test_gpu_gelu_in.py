@@ -93,3 +93,27 @@ def test_gelu_in_rejects_gelu_on_the_output_too(layers):
     x = dev_bf16(_pre_gelu(4, layer.K, 3))
     with pytest.raises(ValueError):
         layer(x, gelu=True, gelu_in=True)
+
+
+@pytest.mark.parametrize("rank,M", [(0, 200), (0, 4608), (16, 200), (16, 4608)])
+def test_gelu_in_low_ranks_and_no_bias(rank, M):
+    """Ranks 0 (no low-rank branch, no bias) and 16 (one rank slice) on both quantizer
+    skeletons: the same byte identity with the separate GELU pass."""
+    K, N = 3072, 384
+    pb = I.prepared_int4_bytes(12, K, N, rank=rank)
+    bias = None if rank == 0 else pb.bias
+    layer = svdq.SvdqLinear.from_interchange(
+        dev_u8(pb.qweight), dev_bf16(pb.wscales), dev_bf16(pb.smooth),
+        dev_bf16(pb.lora_down) if rank else None, dev_bf16(pb.lora_up) if rank else None,
+        dev_bf16(bias) if bias is not None else None)
+    print(f"[gelu_in] int4 rank={rank} M={M} K={K} N={N}", flush=True)
+    x = dev_bf16(_pre_gelu(M, K, 7300 + rank + M))
+    need = layer.workspace_bytes(M)
+    ws = [torch.full((need + GUARD,), 0xA5, dtype=torch.uint8, device=x.device) for _ in range(2)]
+    y_sep = layer(svdq.gelu(x), workspace=ws[0][:need])
+    y_fused = layer(x, workspace=ws[1][:need], gelu_in=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y_fused), host_bits(y_sep))
+    w0, w1 = ws[0].cpu().numpy(), ws[1].cpu().numpy()
+    assert np.array_equal(w1, w0)
+    assert np.all(w1[need:] == 0xA5)
