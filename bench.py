@@ -46,6 +46,7 @@ PEAK_FP6_TFLOPS = 10100.0   # MI355X dense FP6/FP4 MFMA
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
 COLD_SETS = 5                # rotating operand sets of the cold-cache pass (> 256 MB in all)
+WEIGHTS_COLD_BYTES = 320e6   # layer weights rotated by the weights-cold pass (> 256 MB)
 SETTLE_MS = 200.0            # untimed sustained load before the warmup steps (clock ramp)
 
 WORKLOADS = {
@@ -709,9 +710,54 @@ def cold_cache_pass(args, inp, layer_args, M: int, N: int, K: int, dev) -> dict:
     ms = wall * 1e3 / steps
     print(f"[bench] cold-cache pass: {steps} calls over {COLD_SETS} sets of {per_set / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
+    # the same rotation once more with per-kernel events (quantizer, GEMM)
+    svdq.timing_start(steps)
+    for i in range(steps):
+        lay, x, y, ws = sets[i % COLD_SETS]
+        lay(x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    _, kms = svdq.timing_stop(4)
+    x0, y0, ws0 = sets[0][1], sets[0][2], sets[0][3]
     del sets
-    return {"ms_per_step": round(ms, 6), "TOPS": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 3),
-            "sets": COLD_SETS, "bytes_per_set": per_set, "steps": steps}
+    out = {"ms_per_step": round(ms, 6), "TOPS": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 3),
+           "sets": COLD_SETS, "bytes_per_set": per_set, "steps": steps,
+           "kernels_ms": {"quantize": round(kms[0], 6), "gemm": round(kms[1], 6)} if len(kms) >= 2 else None}
+
+    # Weights cold, activations warm (a layer inside a model: its input was just
+    # written, its weights were last read a whole forward pass ago): one X, Y and
+    # workspace, the call rotating over enough copies of the layer that their weights
+    # exceed the Infinity Cache.
+    layers = []
+    w_bytes = 0
+    while w_bytes < WEIGHTS_COLD_BYTES:
+        la, kw = layer_args()
+        lay = svdq.SvdqLinear.from_interchange(*la, **kw)
+        layers.append(lay)
+        w_bytes += sum(t.numel() * t.element_size() for t in
+                       (lay.qweight, lay.wscales, lay.smooth, lay.lora_down, lay.lora_up, lay.bias)
+                       if t is not None)
+    for i in range(len(layers)):
+        layers[i](x0, out=y0, workspace=ws0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layers[i % len(layers)](x0, out=y0, workspace=ws0)
+    torch.cuda.synchronize()
+    wms = (time.perf_counter() - t0) * 1e3 / steps
+    svdq.timing_start(steps)
+    for i in range(steps):
+        layers[i % len(layers)](x0, out=y0, workspace=ws0)
+    torch.cuda.synchronize()
+    _, wkms = svdq.timing_stop(4)
+    print(f"[bench] weights-cold pass: {steps} calls over {len(layers)} layers "
+          f"({w_bytes / 1e6:.0f} MB of weights), one X", file=sys.stderr, flush=True)
+    n_layers = len(layers)
+    del layers
+    out["weights_cold"] = {
+        "ms_per_step": round(wms, 6), "TOPS": round(2.0 * M * N * K / (wms * 1e-3) / 1e12, 3),
+        "layers": n_layers, "weight_bytes_rotated": w_bytes, "steps": steps,
+        "kernels_ms": {"quantize": round(wkms[0], 6), "gemm": round(wkms[1], 6)} if len(wkms) >= 2 else None}
+    return out
 
 
 def main() -> int:
